@@ -1,0 +1,91 @@
+"""Pins of the oracle's reference products: pure-Python brute force, closed
+forms for constant operands, one-hot activations, and the error metric."""
+
+import numpy as np
+
+from oracle import fp8, gemm, intquant as IQ, mx
+
+
+def test_reference_product_matches_brute_force():
+    rng = np.random.default_rng(31)
+    a = rng.standard_normal((5, 96))
+    w = rng.standard_normal((7, 96))
+    assert np.allclose(gemm.reference_product(a, w), gemm.brute_force_product(a, w),
+                       rtol=1e-13, atol=1e-13)
+    # orientation: Y[m, n] = sum_k A[m, k] W[n, k]
+    assert abs(gemm.reference_product(a, w)[2, 3] - sum(a[2] * w[3])) < 1e-12
+
+
+def test_w4a16_reference_on_tiny_case_brute_force():
+    rng = np.random.default_rng(32)
+    w = (rng.standard_normal((6, 256)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    for asym in (False, True):
+        if asym:
+            q, s, z = IQ.quantize_asym(w, 128)
+        else:
+            (q, s), z = IQ.quantize_sym(w, 128), None
+        packed = IQ.pack_int4(q)
+        y = gemm.w4a16_reference(x, packed, s, z, 128)
+        # brute force from the codes, written per group with the cross term
+        yb = np.zeros((3, 6))
+        for mi in range(3):
+            for n in range(6):
+                acc = 0.0
+                for g in range(2):
+                    sl = slice(128 * g, 128 * (g + 1))
+                    sg = float(s[n, g])
+                    zg = 0.0 if z is None else float(z[n, g])
+                    xq = sum(float(a) * float(b) for a, b in zip(x[mi, sl], q[n, sl]))
+                    acc += sg * (xq - zg * float(np.sum(x[mi, sl].astype(np.float64))))
+                yb[mi, n] = acc
+        assert np.allclose(y, yb, rtol=1e-12, atol=1e-12)
+
+
+def test_constant_operands_closed_form():
+    # all x = a, all w = b (an on-grid value) -> Y = K * a * b exactly
+    k = 512
+    x = np.full((2, k), 0.75, dtype=np.float32)
+    w = np.full((3, k), 0.5, dtype=np.float32)
+    q, s = IQ.quantize_sym(w, 128)
+    y = gemm.w4a16_reference(x, IQ.pack_int4(q), s, None, 128)
+    # scale fp16(0.5/7); q = 7 -> w_hat = 7 * fp16(0.5/7)
+    w_hat = 7 * float(s[0, 0])
+    assert np.allclose(y, k * 0.75 * w_hat, rtol=0, atol=1e-12)
+    # MX: x = 1.5 and w = -3 are on-grid after scaling -> exact
+    pa, ea = mx.quantize(np.full((2, 64), 1.5, np.float32))
+    pb, eb = mx.quantize(np.full((3, 64), -3.0, np.float32))
+    assert (gemm.mx_reference(pa, ea, pb, eb) == 64 * 1.5 * -3.0).all()
+
+
+def test_one_hot_rows_select_dequantized_columns():
+    rng = np.random.default_rng(33)
+    w = (rng.standard_normal((9, 256)) * 0.02).astype(np.float32)
+    q, s, z = IQ.quantize_asym(w, 128)
+    x = np.eye(256, dtype=np.float32)[[0, 5, 130, 255]]
+    y = gemm.w4a16_reference(x, IQ.pack_int4(q), s, z, 128)
+    w_hat = IQ.dequantize(q, s, z, 128)
+    assert (y == w_hat[:, [0, 5, 130, 255]].T).all()
+
+
+def test_fp8_and_int8_references_use_both_scales():
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
+    xq, sx = fp8.quantize_rows(x)
+    wq, sw = fp8.quantize_rows(w)
+    y = gemm.fp8_reference(xq, sx, wq, sw)
+    assert gemm.rel_fro(y, x.astype(np.float64) @ w.T.astype(np.float64)) < 0.05
+    qx, sxi, zx = IQ.quantize_asym(x, 64, "int8_asym")
+    qw, swi = IQ.quantize_sym(w, 64, "int8_sym")
+    y8 = gemm.int8_reference(qx, sxi, zx, qw, swi, None)
+    yb = gemm.brute_force_product(IQ.dequantize(qx, sxi, zx, 64), IQ.dequantize(qw, swi, None, 64))
+    assert np.allclose(y8, yb, rtol=1e-12, atol=1e-12)
+    assert gemm.rel_fro(y8, x.astype(np.float64) @ w.T.astype(np.float64)) < 0.02
+
+
+def test_rel_fro_metric():
+    y = np.array([[3.0, 4.0]])
+    assert gemm.rel_fro(y, y) == 0.0
+    assert abs(gemm.rel_fro(y * 1.001, y) - 0.001) < 1e-12
+    assert abs(gemm.rel_fro(np.array([[3.0, 0.0]]), y) - 0.8) < 1e-12
