@@ -1,0 +1,208 @@
+/*
+ * qgemm.h -- C ABI of the quantized linear layer library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Y = X * W^T.  W is stored [N][K] row-major (row n = output channel), X is
+ * [M][K] and Y is [M][N], both row-major.  Quantization groups and MX blocks
+ * run along K.
+ *
+ * Sources of the operations (page titles, with the section used):
+ *   [Q&A]  《量化与加速》: format table (E4M3 +-448, E5M2 +-57344, INT8, INT4
+ *          [-8,7]), float formula, "INT8 量化原理" affine equations
+ *          x_q = clip(round(x/s) + z), x_hat = s (x_q - z).
+ *   [SRV]  《推理优化与量化算子深度技术调研》 section 1.2 (INT8 symmetric scale
+ *          max|x|/127 with clip +-127, asymmetric scale (max-min)/255 with
+ *          zero point round(-min/s) and clip [0,255]; dequantization fused
+ *          into the GEMM), 1.3 (group-wise INT4, group 128, W4A16 decode is
+ *          HBM bound), 1.4 (FP8 E4M3 with an fp32 scale tensor).
+ *   [L6]   《第 6 课：量化源码走读》 section 2 (eight INT4 codes per int32;
+ *          W4A16 dequantizes inside the GEMM; W8A8/FP8 quantizes activations
+ *          dynamically; figure 6-2 Out = acc * scale_x * scale_w; micro-block
+ *          scaling), section 3 (the asymmetric cross term must be kept; the
+ *          MX block must divide K), practice exercise (a zero block uses
+ *          scale 1; invalid geometry is an error).
+ *   [MX]   《大模型量化推理引擎全景大复盘》 section 2 eq. 3 (32 four-bit
+ *          elements share one E8M0 exponent), section 3 code (shared scale
+ *          2^ceil(log2(max|x|/6))).
+ *   [CH1]  《第 1 章：推理加速全景》 section 4.1 (uniform quantization math).
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; each call only enqueues work on
+ *     `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *   - Arguments are validated before any HIP call; on an error nothing is
+ *     enqueued and a status other than QG_OK is returned.  QG_ERR_HIP reports
+ *     a failed kernel launch (hipGetLastError after the launch).
+ *   - Every data pointer must be 16-byte aligned (QG_ERR_ALIGN otherwise);
+ *     128-bit loads and stores are used throughout.
+ *   - round() is round-half-to-even; x/s is one IEEE fp32 division by the
+ *     scale as stored; a scale that is zero (an all-zero group) is stored as 1.
+ *   - Calls are stateless and re-entrant; calls on different streams may run
+ *     concurrently (they share no state).
+ *
+ * Storage formats (bit-exact, and what the kernels read):
+ *   INT4_SYM   codes int32 [rows][K/8]: element k = 8j+i in bits 4i..4i+3 of
+ *              word j (LSB first), two's-complement nibble; q in [-8,7];
+ *              scales fp16 [rows][K/group] = fp16(max|x|/7) (saturating).
+ *   INT4_ASYM  same packing, unsigned nibble q in [0,15]; scales fp16 =
+ *              fp16((max-min)/15); zeros fp16 [rows][K/group], integer
+ *              values round(-min/s), not clamped.
+ *   INT8_SYM   codes int8 [rows][K], q in [-127,127]; scales fp32 =
+ *              max|x|/127 [rows][K/group].
+ *   INT8_ASYM  codes uint8 [rows][K], q in [0,255]; scales fp32 = (max-min)/255;
+ *              zeros fp32 [rows][K/group].
+ *   FP8_E4M3   codes uint8 [rows][K], OCP E4M3FN bits, nearest value with ties
+ *              to even, saturating at +-448 (never NaN), sign kept;
+ *              scales fp32 [rows][K/group] = max|x|/448.
+ *   MXFP4      codes uint8 [rows][K/2], E2M1 sign-magnitude nibbles, element
+ *              2j in the low nibble of byte j; E8M0 uint8 [rows][K/32] = e+127
+ *              with e the smallest integer such that max|x| <= 6*2^e over the
+ *              32-element block (0 for an all-zero block), clamped to
+ *              [-127,127].
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_GEOMETRY = 1,     /* sizes: non-positive, group does not divide K, ... */
+    QG_ERR_ALIGN = 2,        /* a pointer is not 16-byte aligned */
+    QG_ERR_FORMAT = 3,       /* unknown format or unsupported format pair */
+    QG_ERR_NULL = 4,         /* a required pointer is NULL */
+    QG_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+    QG_ERR_UNSUPPORTED = 6   /* valid but not implemented (e.g. GEMV group != 128) */
+} qg_status;
+
+typedef enum {
+    QG_BF16 = 0,
+    QG_F32 = 1
+} qg_dtype;
+
+typedef enum {
+    QG_INT4_SYM = 0,
+    QG_INT4_ASYM = 1,
+    QG_INT8_SYM = 2,
+    QG_INT8_ASYM = 3,
+    QG_FP8_E4M3 = 4,
+    QG_BF16_ACT = 5,   /* unquantized bf16 activations (the A side of W4A16) */
+    QG_MXFP4 = 6
+} qg_format;
+
+/*
+ * qg_quantize_pack -- quantize `rows` x `K` values along K in groups of
+ * `group` (group == K: one scale per row, i.e. per output channel for
+ * weights or per token for activations).  [Q&A] "INT8 量化原理"; [SRV] 1.2,
+ * 1.3, 1.4; [L6] section 2 (dynamic per-token activation quantization,
+ * eight INT4 codes per int32) and the practice exercise (zero block -> 1).
+ *   fmt        QG_INT4_SYM | QG_INT4_ASYM | QG_INT8_SYM | QG_INT8_ASYM |
+ *              QG_FP8_E4M3.
+ *   src        [rows][K] of src_dtype (QG_BF16 or QG_F32), row-major.
+ *   group      > 0, divides K; for INT4 a multiple of 8.
+ *   codes, scales, zeros   outputs in the storage format above; zeros is
+ *              required for *_ASYM and must be NULL otherwise.
+ * Errors: QG_ERR_GEOMETRY (rows < 1, K < 1, bad group), QG_ERR_FORMAT,
+ * QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_quantize_pack(qg_format fmt, const void* src, qg_dtype src_dtype,
+                           int64_t rows, int64_t K, int64_t group,
+                           void* codes, void* scales, void* zeros, void* stream);
+
+/*
+ * qg_dequant -- x_hat = s * (q - z) per group ([Q&A] "INT8 量化原理"; [SRV]
+ * 1.2), or 2^(e8m0-127) * e2m1(q) per 32-block for QG_MXFP4 ([MX]).
+ *   fmt        any quantized format (QG_MXFP4: scales = E8M0 bytes, group
+ *              must be 32, zeros NULL).
+ *   dst        [rows][K] of dst_dtype.  QG_F32 is the value s*(q-z) rounded
+ *              once to fp32; QG_BF16 is that fp32 value rounded to bf16 (RNE).
+ * Errors as for qg_quantize_pack.
+ */
+qg_status qg_dequant(qg_format fmt, const void* codes, const void* scales, const void* zeros,
+                     int64_t rows, int64_t K, int64_t group,
+                     void* dst, qg_dtype dst_dtype, void* stream);
+
+/*
+ * qg_qgemv -- W4A16 decode product Y = X * dequant(W)^T for 1 <= M <= 16
+ * ([SRV] 1.3: the small-batch W4A16 GEMV is HBM bound; [L6] section 2:
+ * dequantization happens inside the kernel; section 3: the zero-point cross
+ * term).  Computes
+ *   y[m][n] = bf16( sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]) )
+ * with fp32 accumulation and one round-to-nearest-even conversion to bf16.
+ *   wfmt       QG_INT4_SYM (wzeros NULL) or QG_INT4_ASYM.
+ *   x          bf16 [M][K];  wcodes int32 [N][K/8];  wscales/wzeros fp16
+ *              [N][K/group];  y bf16 [M][N].
+ *   group      must be 128 (QG_ERR_UNSUPPORTED otherwise); K % 128 == 0.
+ * Errors: QG_ERR_GEOMETRY (M outside 1..16, N < 1, K not a multiple of
+ * group), QG_ERR_UNSUPPORTED, QG_ERR_FORMAT, QG_ERR_NULL, QG_ERR_ALIGN,
+ * QG_ERR_HIP.
+ */
+qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
+                   const void* wcodes, const void* wscales, const void* wzeros,
+                   int64_t N, int64_t K, int64_t group, void* y, void* stream);
+
+/*
+ * qg_qgemm -- quantized GEMM Y = dequant(A) * dequant(W)^T, fp32
+ * accumulation, bf16 output (round to nearest even).  Format pairs:
+ *   W INT4_SYM|INT4_ASYM, A BF16_ACT : W4A16 prefill ([SRV] 1.3; [L6] sec. 2);
+ *       a = bf16 [M][K], a_scales/a_zeros NULL, group must be 128.
+ *   W FP8_E4M3, A FP8_E4M3 : FP8 W8A8 ([L6] figure 6-2: the product of the
+ *       codes is rescaled by s_x[m] * s_w[n]); per-row scales only
+ *       (group == K): a_scales fp32 [M], wscales fp32 [N].
+ *   W INT8_SYM|INT8_ASYM, A INT8_SYM|INT8_ASYM : INT8 W8A8 ([SRV] 1.2;
+ *       [L6] section 3 cross terms); per-row scales/zeros (group == K).
+ *   y          bf16 [M][N].
+ * Errors: QG_ERR_GEOMETRY (M, N, K < 1; K % 128 for W4A16; K % 16 for the
+ * 8-bit formats; group), QG_ERR_FORMAT, QG_ERR_UNSUPPORTED, QG_ERR_NULL,
+ * QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_qgemm(qg_format wfmt, qg_format afmt,
+                   const void* a, const void* a_scales, const void* a_zeros, int64_t M,
+                   const void* wcodes, const void* wscales, const void* wzeros,
+                   int64_t N, int64_t K, int64_t group, void* y, void* stream);
+
+/*
+ * qg_mx_quant -- OCP MXFP4 quantization of [rows][K] along K ([MX]; [L6]
+ * section 2 micro-block scaling).  K must be a multiple of 32 ([L6]
+ * section 3), else QG_ERR_GEOMETRY.
+ *   src        [rows][K] of src_dtype (QG_BF16 or QG_F32).
+ *   codes      uint8 [rows][K/2];  e8m0  uint8 [rows][K/32].
+ */
+qg_status qg_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
+                      void* codes, void* e8m0, void* stream);
+
+/*
+ * qg_mx_gemm -- block-scaled MXFP4 product
+ *   y[m][n] = bf16( sum_b 2^(ea[m][b] + eb[n][b] - 254) *
+ *                   sum_{k in b} e2m1(a[m][k]) * e2m1(b[n][k]) )
+ * on the gfx950 scaled matrix cores, fp32 accumulation ([MX]; [L6] sec. 2).
+ *   a_codes uint8 [M][K/2], a_e8m0 uint8 [M][K/32]; b_codes uint8 [N][K/2],
+ *   b_e8m0 uint8 [N][K/32] (the layout qg_mx_quant writes); y bf16 [M][N].
+ * Errors: QG_ERR_GEOMETRY (M, N < 1; K < 32 or K % 32 != 0), QG_ERR_NULL,
+ * QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
+                     const void* b_codes, const void* b_e8m0, int64_t N, int64_t K,
+                     void* y, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* qg_status_str(qg_status status);
+
+/* Detail of the last error returned on the calling thread (static or
+ * thread-local storage; empty string if none). */
+const char* qg_last_error(void);
+
+/* QG_ABI_VERSION of the built library. */
+int qg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

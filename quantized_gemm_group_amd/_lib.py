@@ -1,0 +1,76 @@
+"""ctypes loader of libqgemm.so and the C ABI prototypes (include/qgemm.h).
+
+The library is loaded from this package directory only; there is no other
+implementation to fall back to, so a missing or stale build raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemm.so")
+
+# qg_format
+INT4_SYM, INT4_ASYM, INT8_SYM, INT8_ASYM, FP8_E4M3, BF16_ACT, MXFP4 = range(7)
+# qg_dtype
+BF16, F32 = 0, 1
+# qg_status
+OK, ERR_GEOMETRY, ERR_ALIGN, ERR_FORMAT, ERR_NULL, ERR_HIP, ERR_UNSUPPORTED = range(7)
+
+EXPORTS = [
+    "qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant", "qg_mx_gemm",
+    "qg_status_str", "qg_last_error", "qg_abi_version",
+]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libqgemm.so (once) and declare its prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m quantized_gemm_group_amd.build` "
+            "(the HIP library is the only implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.qg_quantize_pack.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp]
+    lib.qg_dequant.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i32, vp]
+    lib.qg_qgemv.argtypes = [i32, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
+    lib.qg_qgemm.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
+    lib.qg_mx_quant.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    lib.qg_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp]
+    for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
+                 "qg_mx_gemm"]:
+        getattr(lib, name).restype = i32
+    lib.qg_status_str.argtypes = [i32]
+    lib.qg_status_str.restype = ctypes.c_char_p
+    lib.qg_last_error.argtypes = []
+    lib.qg_last_error.restype = ctypes.c_char_p
+    lib.qg_abi_version.argtypes = []
+    lib.qg_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(detail)
+
+
+def check(status: int) -> None:
+    """Raise on a non-OK status: ValueError for invalid geometry (the
+    convention of the lesson's exercise), QGError otherwise."""
+    if status == OK:
+        return
+    lib = load()
+    name = lib.qg_status_str(status).decode()
+    detail = lib.qg_last_error().decode()
+    if status == ERR_GEOMETRY:
+        raise ValueError(f"invalid quantization geometry: {detail}")
+    raise QGError(status, f"{name}: {detail}")

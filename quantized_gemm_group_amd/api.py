@@ -1,0 +1,160 @@
+"""Python binding of the C ABI: same six operations, torch tensors in and out.
+
+Marshalling only: every function checks tensor placement and dtypes,
+allocates its outputs with torch on the input's device, and makes ONE call
+into libqgemm.so on the current HIP stream.  No arithmetic of the method
+happens here.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+FORMATS = {
+    "int4_sym": _lib.INT4_SYM,
+    "int4_asym": _lib.INT4_ASYM,
+    "int8_sym": _lib.INT8_SYM,
+    "int8_asym": _lib.INT8_ASYM,
+    "fp8_e4m3": _lib.FP8_E4M3,
+    "bf16": _lib.BF16_ACT,
+    "mxfp4": _lib.MXFP4,
+}
+_ASYM = {"int4_asym", "int8_asym"}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dev(t: torch.Tensor) -> torch.device:
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.device
+
+
+def _src_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise ValueError("source must be bf16 or fp32")
+
+
+def _code_shapes(fmt: str, rows: int, k: int, group: int):
+    """(codes shape, codes dtype, scale dtype) of the storage format."""
+    if fmt.startswith("int4"):
+        return (rows, k // 8), torch.int32, torch.float16
+    if fmt == "int8_sym":
+        return (rows, k), torch.int8, torch.float32
+    if fmt in ("int8_asym", "fp8_e4m3"):
+        return (rows, k), torch.uint8, torch.float32
+    raise ValueError(f"unknown format {fmt}")
+
+
+def default_group(fmt: str, k: int) -> int:
+    return 128 if fmt.startswith("int4") else k
+
+
+def quantize_pack(x: torch.Tensor, fmt: str, group: int | None = None):
+    """Quantize x [rows][K] (bf16 or fp32) along K.  Returns
+    (codes, scales, zeros or None) in the storage format of include/qgemm.h."""
+    lib = _lib.load()
+    dev = _dev(x)
+    rows, k = x.shape
+    group = default_group(fmt, k) if group is None else group
+    if group <= 0 or k % group:
+        raise ValueError("invalid quantization geometry: group must divide K")
+    cshape, cdt, sdt = _code_shapes(fmt, rows, k, group)
+    codes = torch.empty(cshape, dtype=cdt, device=dev)
+    scales = torch.empty((rows, k // group), dtype=sdt, device=dev)
+    zeros = torch.empty_like(scales) if fmt in _ASYM else None
+    _lib.check(lib.qg_quantize_pack(FORMATS[fmt], _ptr(x), _src_dtype(x), rows, k, group,
+                                    _ptr(codes), _ptr(scales), _ptr(zeros), _stream(dev)))
+    return codes, scales, zeros
+
+
+def dequant(codes: torch.Tensor, scales: torch.Tensor, zeros, fmt: str, k: int,
+            group: int | None = None, out_dtype=torch.float32) -> torch.Tensor:
+    """x_hat = s * (q - z) (or 2^e * e2m1 for "mxfp4") as [rows][K]."""
+    lib = _lib.load()
+    dev = _dev(codes)
+    rows = codes.shape[0]
+    group = (32 if fmt == "mxfp4" else default_group(fmt, k)) if group is None else group
+    out = torch.empty((rows, k), dtype=out_dtype, device=dev)
+    dt = _lib.BF16 if out_dtype == torch.bfloat16 else _lib.F32
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bf16 or fp32")
+    _lib.check(lib.qg_dequant(FORMATS[fmt], _ptr(codes), _ptr(scales), _ptr(zeros), rows, k,
+                              group, _ptr(out), dt, _stream(dev)))
+    return out
+
+
+def qgemv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, zeros, fmt: str,
+          group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A16 decode product y = x * dequant(W)^T for 1 <= M <= 16; x bf16 [M][K]."""
+    lib = _lib.load()
+    dev = _dev(x)
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    m, k = x.shape
+    n = codes.shape[0]
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_qgemv(FORMATS[fmt], _ptr(x), m, _ptr(codes), _ptr(scales), _ptr(zeros),
+                            n, k, group, _ptr(y), _stream(dev)))
+    return y
+
+
+def qgemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_zeros, wfmt: str,
+          afmt: str, a_scales=None, a_zeros=None, k: int | None = None,
+          group: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantized GEMM y = dequant(a) * dequant(W)^T with bf16 output.
+    Pairs: (int4_*, "bf16"), ("fp8_e4m3", "fp8_e4m3"), (int8_*, int8_*)."""
+    lib = _lib.load()
+    dev = _dev(a)
+    m = a.shape[0]
+    k = a.shape[1] if k is None else k
+    n = w_codes.shape[0]
+    group = default_group(wfmt, k) if group is None else group
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_qgemm(FORMATS[wfmt], FORMATS[afmt], _ptr(a), _ptr(a_scales), _ptr(a_zeros),
+                            m, _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros), n, k, group,
+                            _ptr(y), _stream(dev)))
+    return y
+
+
+def mx_quant(x: torch.Tensor):
+    """OCP MXFP4 quantization of x [rows][K] along K.  Returns (codes uint8
+    [rows][K/2], e8m0 uint8 [rows][K/32])."""
+    lib = _lib.load()
+    dev = _dev(x)
+    rows, k = x.shape
+    if k % 32 or k == 0:
+        raise ValueError("invalid quantization geometry: K must be a multiple of 32")
+    codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+    e8m0 = torch.empty((rows, k // 32), dtype=torch.uint8, device=dev)
+    _lib.check(lib.qg_mx_quant(_ptr(x), _src_dtype(x), rows, k, _ptr(codes), _ptr(e8m0),
+                               _stream(dev)))
+    return codes, e8m0
+
+
+def mx_gemm(a_codes: torch.Tensor, a_e8m0: torch.Tensor, b_codes: torch.Tensor,
+            b_e8m0: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Block-scaled MXFP4 product y = A * B^T (both [rows][K] in MX form), bf16."""
+    lib = _lib.load()
+    dev = _dev(a_codes)
+    m, kh = a_codes.shape
+    n = b_codes.shape[0]
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_mx_gemm(_ptr(a_codes), _ptr(a_e8m0), m, _ptr(b_codes), _ptr(b_e8m0), n,
+                              2 * kh, _ptr(y), _stream(dev)))
+    return y

@@ -1,0 +1,192 @@
+// C ABI of the quantized linear layer library (declared in include/qgemm.h).
+//
+// Every entry point validates its arguments completely before the first HIP
+// call, so an invalid call enqueues nothing and touches no device state.  The
+// library allocates nothing and never synchronizes.
+
+#include <cstdio>
+#include <cstring>
+
+#include "qg_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+qg_status fail(qg_status st, const char* what) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s", what);
+  return st;
+}
+
+qg_status ok() {
+  g_last_error[0] = '\0';
+  return QG_OK;
+}
+
+qg_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  std::snprintf(g_last_error, sizeof(g_last_error), "HIP launch error: %s", hipGetErrorString(e));
+  return QG_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_quant_fmt(qg_format f) {
+  return f == QG_INT4_SYM || f == QG_INT4_ASYM || f == QG_INT8_SYM || f == QG_INT8_ASYM ||
+         f == QG_FP8_E4M3;
+}
+
+bool is_asym(qg_format f) { return f == QG_INT4_ASYM || f == QG_INT8_ASYM; }
+
+bool is_int4(qg_format f) { return f == QG_INT4_SYM || f == QG_INT4_ASYM; }
+
+bool is_int8(qg_format f) { return f == QG_INT8_SYM || f == QG_INT8_ASYM; }
+
+// Shared checks of a quantized [rows][K] operand with groups along K.
+qg_status check_quant_operand(qg_format fmt, int64_t rows, int64_t K, int64_t group,
+                              const void* codes, const void* scales, const void* zeros) {
+  if (rows < 1 || K < 1) return fail(QG_ERR_GEOMETRY, "rows and K must be positive");
+  if (group <= 0 || K % group != 0) return fail(QG_ERR_GEOMETRY, "group must divide K");
+  if (group % 8 != 0) return fail(QG_ERR_GEOMETRY, "group must be a multiple of 8");
+  if (!codes || !scales) return fail(QG_ERR_NULL, "codes and scales are required");
+  if (is_asym(fmt) && !zeros) return fail(QG_ERR_NULL, "asymmetric formats need zeros");
+  if (!is_asym(fmt) && zeros) return fail(QG_ERR_NULL, "zeros must be NULL for this format");
+  if (!aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)))
+    return fail(QG_ERR_ALIGN, "pointers must be 16-byte aligned");
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qg_abi_version(void) { return QG_ABI_VERSION; }
+
+const char* qg_last_error(void) { return g_last_error; }
+
+const char* qg_status_str(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_GEOMETRY: return "invalid quantization geometry";
+    case QG_ERR_ALIGN: return "misaligned pointer";
+    case QG_ERR_FORMAT: return "unsupported format";
+    case QG_ERR_NULL: return "null pointer";
+    case QG_ERR_HIP: return "HIP error";
+    case QG_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+qg_status qg_quantize_pack(qg_format fmt, const void* src, qg_dtype src_dtype, int64_t rows,
+                           int64_t K, int64_t group, void* codes, void* scales, void* zeros,
+                           void* stream) {
+  if (!is_quant_fmt(fmt)) return fail(QG_ERR_FORMAT, "quantize_pack: unknown format");
+  if (src_dtype != QG_BF16 && src_dtype != QG_F32)
+    return fail(QG_ERR_FORMAT, "quantize_pack: source dtype must be bf16 or f32");
+  qg_status st = check_quant_operand(fmt, rows, K, group, codes, scales, zeros);
+  if (st != QG_OK) return st;
+  if (!src) return fail(QG_ERR_NULL, "quantize_pack: src is NULL");
+  if (!aligned16(src)) return fail(QG_ERR_ALIGN, "quantize_pack: src must be 16-byte aligned");
+  return from_hip(qg::launch_quantize(fmt, src, src_dtype, rows, K, group, codes, scales, zeros,
+                                      (hipStream_t)stream));
+}
+
+qg_status qg_dequant(qg_format fmt, const void* codes, const void* scales, const void* zeros,
+                     int64_t rows, int64_t K, int64_t group, void* dst, qg_dtype dst_dtype,
+                     void* stream) {
+  if (!is_quant_fmt(fmt) && fmt != QG_MXFP4) return fail(QG_ERR_FORMAT, "dequant: unknown format");
+  if (dst_dtype != QG_BF16 && dst_dtype != QG_F32)
+    return fail(QG_ERR_FORMAT, "dequant: destination dtype must be bf16 or f32");
+  if (fmt == QG_MXFP4 && group != 32)
+    return fail(QG_ERR_GEOMETRY, "dequant: MXFP4 blocks are 32 elements");
+  qg_status st = check_quant_operand(fmt, rows, K, group, codes, scales, zeros);
+  if (st != QG_OK) return st;
+  if (!dst) return fail(QG_ERR_NULL, "dequant: dst is NULL");
+  if (!aligned16(dst)) return fail(QG_ERR_ALIGN, "dequant: dst must be 16-byte aligned");
+  return from_hip(qg::launch_dequant(fmt, codes, scales, zeros, rows, K, group, dst, dst_dtype,
+                                     (hipStream_t)stream));
+}
+
+qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M, const void* wcodes,
+                   const void* wscales, const void* wzeros, int64_t N, int64_t K, int64_t group,
+                   void* y, void* stream) {
+  if (!is_int4(wfmt)) return fail(QG_ERR_FORMAT, "qgemv: weights must be INT4_SYM or INT4_ASYM");
+  if (M < 1 || M > 16) return fail(QG_ERR_GEOMETRY, "qgemv: M must be in 1..16");
+  if (N < 1 || N > (int64_t)1 << 30) return fail(QG_ERR_GEOMETRY, "qgemv: N out of range");
+  qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
+  if (st != QG_OK) return st;
+  if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemv: only group 128 is implemented");
+  if (K > 65536) return fail(QG_ERR_UNSUPPORTED, "qgemv: K above 65536 is not implemented");
+  if (!x || !y) return fail(QG_ERR_NULL, "qgemv: x and y are required");
+  if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemv: x, y must be 16-byte aligned");
+  return from_hip(qg::launch_qgemv(wfmt == QG_INT4_ASYM, x, M, wcodes, wscales, wzeros, N, K, y,
+                                   (hipStream_t)stream));
+}
+
+qg_status qg_qgemm(qg_format wfmt, qg_format afmt, const void* a, const void* a_scales,
+                   const void* a_zeros, int64_t M, const void* wcodes, const void* wscales,
+                   const void* wzeros, int64_t N, int64_t K, int64_t group, void* y,
+                   void* stream) {
+  if (M < 1 || N < 1 || K < 1) return fail(QG_ERR_GEOMETRY, "qgemm: M, N, K must be positive");
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+    return fail(QG_ERR_GEOMETRY, "qgemm: size out of range");
+  if (!a || !y) return fail(QG_ERR_NULL, "qgemm: a and y are required");
+  if (!aligned16(a) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemm: a, y must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (is_int4(wfmt) && afmt == QG_BF16_ACT) {
+    qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
+    if (st != QG_OK) return st;
+    if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemm W4A16: only group 128 is implemented");
+    if (a_scales || a_zeros) return fail(QG_ERR_NULL, "qgemm W4A16: a_scales/a_zeros must be NULL");
+    return from_hip(qg::launch_gemm_w4a16(wfmt == QG_INT4_ASYM, a, M, wcodes, wscales, wzeros, N,
+                                          K, y, s));
+  }
+  if (wfmt == QG_FP8_E4M3 && afmt == QG_FP8_E4M3) {
+    if (group != K) return fail(QG_ERR_UNSUPPORTED, "qgemm FP8: per-row scales only (group == K)");
+    if (K % 16 != 0) return fail(QG_ERR_GEOMETRY, "qgemm FP8: K must be a multiple of 16");
+    qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
+    if (st != QG_OK) return st;
+    st = check_quant_operand(afmt, M, K, group, a, a_scales, a_zeros);
+    if (st != QG_OK) return st;
+    return from_hip(qg::launch_gemm_fp8(a, a_scales, M, wcodes, wscales, N, K, y, s));
+  }
+  if (is_int8(wfmt) && is_int8(afmt)) {
+    if (group != K) return fail(QG_ERR_UNSUPPORTED, "qgemm INT8: per-row scales only (group == K)");
+    if (K % 16 != 0) return fail(QG_ERR_GEOMETRY, "qgemm INT8: K must be a multiple of 16");
+    qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
+    if (st != QG_OK) return st;
+    st = check_quant_operand(afmt, M, K, group, a, a_scales, a_zeros);
+    if (st != QG_OK) return st;
+    return from_hip(qg::launch_gemm_int8(afmt == QG_INT8_ASYM, wfmt == QG_INT8_ASYM, a, a_scales,
+                                         a_zeros, M, wcodes, wscales, wzeros, N, K, y, s));
+  }
+  return fail(QG_ERR_FORMAT, "qgemm: unsupported format pair");
+}
+
+qg_status qg_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K, void* codes,
+                      void* e8m0, void* stream) {
+  if (src_dtype != QG_BF16 && src_dtype != QG_F32)
+    return fail(QG_ERR_FORMAT, "mx_quant: source dtype must be bf16 or f32");
+  if (rows < 1 || K < 32 || K % 32 != 0)
+    return fail(QG_ERR_GEOMETRY, "mx_quant: rows >= 1 and K a positive multiple of 32");
+  if (!src || !codes || !e8m0) return fail(QG_ERR_NULL, "mx_quant: NULL pointer");
+  if (!aligned16(src) || !aligned16(codes) || !aligned16(e8m0))
+    return fail(QG_ERR_ALIGN, "mx_quant: pointers must be 16-byte aligned");
+  return from_hip(qg::launch_mx_quant(src, src_dtype, rows, K, codes, e8m0, (hipStream_t)stream));
+}
+
+qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M, const void* b_codes,
+                     const void* b_e8m0, int64_t N, int64_t K, void* y, void* stream) {
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
+    return fail(QG_ERR_GEOMETRY, "mx_gemm: M, N >= 1 and K a positive multiple of 32");
+  if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+    return fail(QG_ERR_GEOMETRY, "mx_gemm: size out of range");
+  if (!a_codes || !a_e8m0 || !b_codes || !b_e8m0 || !y) return fail(QG_ERR_NULL, "mx_gemm: NULL pointer");
+  if (!aligned16(a_codes) || !aligned16(a_e8m0) || !aligned16(b_codes) || !aligned16(b_e8m0) ||
+      !aligned16(y))
+    return fail(QG_ERR_ALIGN, "mx_gemm: pointers must be 16-byte aligned");
+  return from_hip(qg::launch_mx_gemm(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Device-side numeric helpers shared by the quantization and GEMM kernels.
+//
+// Everything here is exact by construction: round-to-nearest-even
+// conversions written with integer arithmetic on the IEEE encodings, the
+// saturating FP8 E4M3 encoder and the E2M1 encoder built from the format
+// definitions (《量化与加速》 float formula and format table; E2M1 maximum 6 from
+// the MX scale rule of 《大模型量化推理引擎全景大复盘》 section 3), and the MX
+// shared exponent decided with integer logic instead of a floating-point log.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// ---------------------------------------------------------------- bf16 / fp16
+
+// fp32 -> bf16 bits, round to nearest even (IEEE: overflow goes to inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> fp16 round to nearest even, results that would overflow to
+// infinity clamped to +-65504 (scale storage).  Returns the stored value
+// widened back to fp32.
+__device__ __forceinline__ float f32_to_f16_sat(float f, uint16_t* bits) {
+  _Float16 h = (_Float16)f;                       // v_cvt_f16_f32, RNE
+  float back = (float)h;
+  if (__builtin_isinf(back) && !__builtin_isinf(f)) {
+    h = (_Float16)(f > 0.f ? 65504.f : -65504.f);
+    back = (float)h;
+  }
+  *bits = __builtin_bit_cast(uint16_t, h);
+  return back;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// ------------------------------------------------------------------ FP8 E4M3
+
+// Saturating OCP E4M3FN encoder: nearest value, ties to the even code, |v| >=
+// 448 -> +-448 (0x7E), sign kept (so tiny negatives give 0x80).
+__device__ __forceinline__ uint32_t e4m3_encode_sat(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __builtin_fabsf(v);
+  if (!(a < 448.f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                            // below 2^-6: steps of 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.f);   // exact scaling, RNE
+  }
+  uint32_t ua = __float_as_uint(a);
+  ua += 0x7ffffu + ((ua >> 20) & 1u);             // round the 20 dropped bits
+  uint32_t e = (ua >> 23) - 127u + 7u;            // biased E4M3 exponent (1..15)
+  uint32_t code = (e << 3) | ((ua >> 20) & 7u);
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e ? __builtin_ldexpf((float)(8u + m), (int)e - 10)
+                : __builtin_ldexpf((float)m, -9);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ------------------------------------------------------------------ FP4 E2M1
+
+// E2M1 magnitudes by code: 0, .5, 1, 1.5, 2, 3, 4, 6.  Nearest value with ties
+// to the even code (midpoints .25 .75 1.25 1.75 2.5 3.5 5), saturating at 6;
+// the sign of v is kept (bit 3).
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  float a = __builtin_fabsf(v);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+  const uint32_t m = c & 7u;
+  // 0 .5 1 1.5 2 3 4 6 = (m < 2) ? m/2 : (2 + (m&1)) * 2^((m>>1)-1)
+  float mag = (m < 2u) ? 0.5f * (float)m
+                       : __builtin_ldexpf((float)(2u + (m & 1u)), (int)(m >> 1) - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+// MX shared exponent: smallest integer e with m <= 6 * 2^e, for m = f * 2^E
+// (f in [1,2)) that is E - 2 + [f > 1.5]; clamped to [-127, 127]; 0 for m == 0.
+__device__ __forceinline__ int mx_shared_exponent(float m) {
+  if (m == 0.f) return 0;
+  int ex;
+  float fr = __builtin_frexpf(m, &ex);            // m = fr * 2^ex, fr in [0.5, 1)
+  int e = (ex - 1) - 2 + (fr > 0.75f ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// ------------------------------------------------------------ wave utilities
+
+// xor-shuffle within a wave (ds_bpermute based).
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float wave_max_seg(float v, int seg) {
+  for (int o = 1; o < seg; o <<= 1) v = __builtin_fmaxf(v, shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_min_seg(float v, int seg) {
+  for (int o = 1; o < seg; o <<= 1) v = __builtin_fminf(v, shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace qg

@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (qg_api.hip) and the kernel
+// translation units.  Arguments reaching these functions are already
+// validated; each function only enqueues kernels on `stream` and returns the
+// hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qgemm.h"
+
+namespace qg {
+
+hipError_t launch_quantize(qg_format fmt, const void* src, qg_dtype src_dtype, int64_t rows,
+                           int64_t K, int64_t group, void* codes, void* scales, void* zeros,
+                           hipStream_t stream);
+
+hipError_t launch_dequant(qg_format fmt, const void* codes, const void* scales,
+                          const void* zeros, int64_t rows, int64_t K, int64_t group, void* dst,
+                          qg_dtype dst_dtype, hipStream_t stream);
+
+hipError_t launch_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
+                           void* codes, void* e8m0, hipStream_t stream);
+
+hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
+                        const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
+                        hipStream_t stream);
+
+hipError_t launch_gemm_w4a16(bool asym, const void* x, int64_t M, const void* wcodes,
+                             const void* wscales, const void* wzeros, int64_t N, int64_t K,
+                             void* y, hipStream_t stream);
+
+hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const void* w,
+                           const void* w_scales, int64_t N, int64_t K, void* y,
+                           hipStream_t stream);
+
+hipError_t launch_gemm_int8(bool a_asym, bool w_asym, const void* a, const void* a_scales,
+                            const void* a_zeros, int64_t M, const void* w, const void* w_scales,
+                            const void* w_zeros, int64_t N, int64_t K, void* y,
+                            hipStream_t stream);
+
+hipError_t launch_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
+                          const void* b_codes, const void* b_e8m0, int64_t N, int64_t K, void* y,
+                          hipStream_t stream);
+
+}  // namespace qg

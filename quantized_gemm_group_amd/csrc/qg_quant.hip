@@ -1,0 +1,416 @@
+// Quantization, dequantization and MXFP4 quantization kernels.
+//
+// Group-wise quantization follows the affine equations of 《量化与加速》
+// ("INT8 量化原理": x_q = clip(round(x/s) + z), x_hat = s (x_q - z)) with the
+// symmetric and asymmetric scale rules of 《推理优化与量化算子深度技术调研》
+// section 1.2 (max|x|/q_max; (max-min)/(2^b-1) with z = round(-min/s)), the
+// zero-block rule of the practice exercise in 《第 6 课：量化源码走读》 (scale 1)
+// and its packing of eight INT4 codes per int32 (section 2).  Per-row FP8
+// (scale max|x|/448, E4M3 range from the format table of 《量化与加速》) is the
+// dynamic per-token activation quantization of that lesson's section 2.
+// MXFP4 follows 《大模型量化推理引擎全景大复盘》 section 2 eq. 3 and section 3
+// (32 elements share 2^ceil(log2(max/6))).
+//
+// Work unit: a "vec" of 8 consecutive elements along K (one int32 of INT4
+// codes, 8 bytes of INT8/FP8 codes, 4 bytes of MXFP4 codes).  A group is
+// T = group/8 consecutive vecs; groups tile the row-major [rows][K] array in
+// order, so the group of vec v is v / T.
+//  - T a power of two <= 64: one lane per vec, the group's T lanes reduce
+//    with xor-shuffles (no LDS, one pass over HBM).
+//  - otherwise (large groups, per-row scales): one 256-thread workgroup per
+//    group, a block reduction, then a second pass that re-reads the group
+//    from cache and writes the codes.
+// Every kernel is HBM bound (4 B read + <= 1 B written per fp32 weight).
+
+#include "qg_device.hpp"
+#include "qg_internal.hpp"
+
+namespace qg {
+namespace {
+
+enum QKind { K_INT4_SYM = 0, K_INT4_ASYM = 1, K_INT8_SYM = 2, K_INT8_ASYM = 3, K_FP8 = 4 };
+
+constexpr int kThreads = 256;
+
+template <bool BF16>
+__device__ __forceinline__ void load_vec(const void* src, int64_t vec, float (&v)[8]) {
+  if constexpr (BF16) {
+    const u32x4 w = reinterpret_cast<const u32x4*>(src)[vec];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(src) + 2 * vec;
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
+
+struct Stats {
+  float amax, lo, hi;
+};
+
+__device__ __forceinline__ Stats stats_of(const float (&v)[8]) {
+  Stats s{0.f, __builtin_inff(), -__builtin_inff()};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s.amax = __builtin_fmaxf(s.amax, __builtin_fabsf(v[i]));
+    s.lo = __builtin_fminf(s.lo, v[i]);
+    s.hi = __builtin_fmaxf(s.hi, v[i]);
+  }
+  return s;
+}
+
+struct Params {
+  float s;          // stored scale, as fp32
+  float z;          // stored zero point, as fp32 (0 for symmetric kinds)
+  uint32_t s_bits;  // fp16 bits (INT4) -- unused for fp32 storage
+  uint32_t z_bits;
+};
+
+// Scale (and zero point) of one group, rounded to the storage dtype first;
+// a stored scale of 0 becomes 1.
+template <int K>
+__device__ __forceinline__ Params make_params(const Stats& st) {
+  Params p{1.f, 0.f, 0x3C00u, 0u};
+  if constexpr (K == K_INT4_SYM) {
+    uint16_t b;
+    float s = f32_to_f16_sat(st.amax / 7.0f, &b);
+    if (s == 0.f) { s = 1.f; b = 0x3C00; }
+    p.s = s; p.s_bits = b;
+  } else if constexpr (K == K_INT4_ASYM) {
+    uint16_t b, zb;
+    float s = f32_to_f16_sat((st.hi - st.lo) / 15.0f, &b);
+    if (s == 0.f) { s = 1.f; b = 0x3C00; }
+    float z = f32_to_f16_sat(__builtin_rintf(-st.lo / s), &zb);
+    p.s = s; p.s_bits = b; p.z = z; p.z_bits = zb;
+  } else if constexpr (K == K_INT8_SYM) {
+    float s = st.amax / 127.0f;
+    p.s = (s == 0.f) ? 1.f : s;
+  } else if constexpr (K == K_INT8_ASYM) {
+    float s = (st.hi - st.lo) / 255.0f;
+    s = (s == 0.f) ? 1.f : s;
+    p.s = s;
+    p.z = __builtin_rintf(-st.lo / s);
+  } else {  // K_FP8
+    float s = st.amax / 448.0f;
+    p.s = (s == 0.f) ? 1.f : s;
+  }
+  return p;
+}
+
+template <int K>
+__device__ __forceinline__ void store_params(const Params& p, void* scales, void* zeros,
+                                             int64_t g) {
+  if constexpr (K == K_INT4_SYM || K == K_INT4_ASYM) {
+    reinterpret_cast<uint16_t*>(scales)[g] = (uint16_t)p.s_bits;
+    if constexpr (K == K_INT4_ASYM) reinterpret_cast<uint16_t*>(zeros)[g] = (uint16_t)p.z_bits;
+  } else {
+    reinterpret_cast<float*>(scales)[g] = p.s;
+    if constexpr (K == K_INT8_ASYM) reinterpret_cast<float*>(zeros)[g] = p.z;
+  }
+}
+
+// Quantize 8 values with the group parameters and store their codes.
+template <int K>
+__device__ __forceinline__ void quantize_store(const float (&v)[8], const Params& p,
+                                               void* codes, int64_t vec) {
+  if constexpr (K == K_INT4_SYM || K == K_INT4_ASYM) {
+    constexpr float lo = (K == K_INT4_SYM) ? -8.f : 0.f;
+    constexpr float hi = (K == K_INT4_SYM) ? 7.f : 15.f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = __builtin_rintf(v[i] / p.s) + p.z;       // round, then add z
+      q = __builtin_fminf(__builtin_fmaxf(q, lo), hi);    // then clip
+      word |= ((uint32_t)(int)q & 0xFu) << (4 * i);
+    }
+    reinterpret_cast<uint32_t*>(codes)[vec] = word;
+  } else {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (K == K_FP8) {
+        b[i] = e4m3_encode_sat(v[i] / p.s);
+      } else {
+        constexpr float lo = (K == K_INT8_SYM) ? -127.f : 0.f;
+        constexpr float hi = (K == K_INT8_SYM) ? 127.f : 255.f;
+        float q = __builtin_rintf(v[i] / p.s) + p.z;
+        q = __builtin_fminf(__builtin_fmaxf(q, lo), hi);
+        b[i] = (uint32_t)(int)q & 0xFFu;
+      }
+    }
+    uint2 out;
+    out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    reinterpret_cast<uint2*>(codes)[vec] = out;
+  }
+}
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(kThreads) void quant_wave_kernel(const void* __restrict__ src,
+                                                              int64_t total_vecs, int t_log2,
+                                                              void* __restrict__ codes,
+                                                              void* __restrict__ scales,
+                                                              void* __restrict__ zeros) {
+  const int64_t vec = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool valid = vec < total_vecs;
+  float v[8];
+  if (valid) {
+    load_vec<BF16>(src, vec, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  Stats st = stats_of(v);
+  const int seg = 1 << t_log2;
+  // segments never straddle valid and invalid lanes (total_vecs % seg == 0)
+  for (int o = 1; o < seg; o <<= 1) {
+    st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
+    st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
+    st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+  }
+  if (!valid) return;
+  const Params p = make_params<K>(st);
+  quantize_store<K>(v, p, codes, vec);
+  if ((vec & (seg - 1)) == 0) store_params<K>(p, scales, zeros, vec >> t_log2);
+}
+
+template <int K, bool BF16>
+__global__ __launch_bounds__(kThreads) void quant_block_kernel(const void* __restrict__ src,
+                                                               int64_t t_vecs,
+                                                               void* __restrict__ codes,
+                                                               void* __restrict__ scales,
+                                                               void* __restrict__ zeros) {
+  __shared__ float red[3][kThreads / 64];
+  const int64_t g = blockIdx.x;
+  const int64_t v0 = g * t_vecs;
+  Stats st{0.f, __builtin_inff(), -__builtin_inff()};
+  for (int64_t i = threadIdx.x; i < t_vecs; i += kThreads) {
+    float v[8];
+    load_vec<BF16>(src, v0 + i, v);
+    const Stats s = stats_of(v);
+    st.amax = __builtin_fmaxf(st.amax, s.amax);
+    st.lo = __builtin_fminf(st.lo, s.lo);
+    st.hi = __builtin_fmaxf(st.hi, s.hi);
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
+    st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
+    st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = st.amax;
+    red[1][w] = st.lo;
+    red[2][w] = st.hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    st.amax = __builtin_fmaxf(st.amax, red[0][i]);
+    st.lo = __builtin_fminf(st.lo, red[1][i]);
+    st.hi = __builtin_fmaxf(st.hi, red[2][i]);
+  }
+  const Params p = make_params<K>(st);
+  for (int64_t i = threadIdx.x; i < t_vecs; i += kThreads) {
+    float v[8];
+    load_vec<BF16>(src, v0 + i, v);
+    quantize_store<K>(v, p, codes, v0 + i);
+  }
+  if (threadIdx.x == 0) store_params<K>(p, scales, zeros, g);
+}
+
+// --------------------------------------------------------------- dequant
+
+template <int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const void* __restrict__ codes,
+                                                           const void* __restrict__ scales,
+                                                           const void* __restrict__ zeros,
+                                                           int64_t total_vecs, int64_t t_vecs,
+                                                           void* __restrict__ dst) {
+  const int64_t vec = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (vec >= total_vecs) return;
+  const int64_t g = vec / t_vecs;
+  float out[8];
+  if constexpr (FMT == QG_INT4_SYM || FMT == QG_INT4_ASYM) {
+    const float s = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(scales)[g]);
+    const float z =
+        (FMT == QG_INT4_ASYM) ? f16_bits_to_f32(reinterpret_cast<const uint16_t*>(zeros)[g]) : 0.f;
+    const uint32_t word = reinterpret_cast<const uint32_t*>(codes)[vec];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int q = (int)((word >> (4 * i)) & 0xFu);
+      if (FMT == QG_INT4_SYM) q = (q ^ 8) - 8;        // two's-complement nibble
+      out[i] = s * ((float)q - z);
+    }
+  } else if constexpr (FMT == QG_MXFP4) {
+    const int e = (int)reinterpret_cast<const uint8_t*>(scales)[g] - 127;
+    const uint32_t word = reinterpret_cast<const uint32_t*>(codes)[vec];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = __builtin_ldexpf(e2m1_decode(word >> (4 * i)), e);
+  } else {
+    const float s = reinterpret_cast<const float*>(scales)[g];
+    const float z = (FMT == QG_INT8_ASYM) ? reinterpret_cast<const float*>(zeros)[g] : 0.f;
+    const uint2 w = reinterpret_cast<const uint2*>(codes)[vec];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = ((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xFFu;
+      if constexpr (FMT == QG_FP8_E4M3) {
+        out[i] = s * e4m3_decode(b);
+      } else if constexpr (FMT == QG_INT8_SYM) {
+        out[i] = s * ((float)(int)(int8_t)b - z);
+      } else {
+        out[i] = s * ((float)(int)b - z);
+      }
+    }
+  }
+  if constexpr (OUT_BF16) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(out[2 * i], out[2 * i + 1]);
+    reinterpret_cast<u32x4*>(dst)[vec] = o;
+  } else {
+    f32x4* p = reinterpret_cast<f32x4*>(dst) + 2 * vec;
+    p[0] = f32x4{out[0], out[1], out[2], out[3]};
+    p[1] = f32x4{out[4], out[5], out[6], out[7]};
+  }
+}
+
+// ---------------------------------------------------------------- MXFP4
+
+// One lane per 8 elements, 4 lanes per 32-element block.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const void* __restrict__ src,
+                                                            int64_t total_vecs,
+                                                            void* __restrict__ codes,
+                                                            void* __restrict__ e8m0) {
+  const int64_t vec = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool valid = vec < total_vecs;
+  float v[8];
+  if (valid) {
+    load_vec<BF16>(src, vec, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  m = __builtin_fmaxf(m, shfl_xor(m, 1));
+  m = __builtin_fmaxf(m, shfl_xor(m, 2));
+  if (!valid) return;
+  const int e = mx_shared_exponent(m);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= e2m1_encode(__builtin_ldexpf(v[i], -e)) << (4 * i);
+  reinterpret_cast<uint32_t*>(codes)[vec] = word;
+  if ((vec & 3) == 0) reinterpret_cast<uint8_t*>(e8m0)[vec >> 2] = (uint8_t)(e + 127);
+}
+
+inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+template <int K, bool BF16>
+void launch_quant_t(const void* src, int64_t rows, int64_t Kdim, int64_t group, void* codes,
+                    void* scales, void* zeros, hipStream_t stream) {
+  const int64_t t_vecs = group / 8;
+  const int64_t total = rows * Kdim / 8;
+  if (t_vecs <= 64 && (t_vecs & (t_vecs - 1)) == 0) {
+    int t_log2 = 0;
+    while ((1LL << t_log2) < t_vecs) ++t_log2;
+    hipLaunchKernelGGL((quant_wave_kernel<K, BF16>), dim3(blocks_for(total)), dim3(kThreads), 0,
+                       stream, src, total, t_log2, codes, scales, zeros);
+  } else {
+    const int64_t groups = rows * (Kdim / group);
+    hipLaunchKernelGGL((quant_block_kernel<K, BF16>), dim3((unsigned)groups), dim3(kThreads), 0,
+                       stream, src, t_vecs, codes, scales, zeros);
+  }
+}
+
+template <bool BF16>
+void launch_quant_fmt(qg_format fmt, const void* src, int64_t rows, int64_t Kdim, int64_t group,
+                      void* codes, void* scales, void* zeros, hipStream_t stream) {
+  switch (fmt) {
+    case QG_INT4_SYM:
+      return launch_quant_t<K_INT4_SYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+    case QG_INT4_ASYM:
+      return launch_quant_t<K_INT4_ASYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+    case QG_INT8_SYM:
+      return launch_quant_t<K_INT8_SYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+    case QG_INT8_ASYM:
+      return launch_quant_t<K_INT8_ASYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+    default:
+      return launch_quant_t<K_FP8, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+  }
+}
+
+template <int FMT>
+void launch_dequant_t(const void* codes, const void* scales, const void* zeros, int64_t total,
+                      int64_t t_vecs, void* dst, qg_dtype dt, hipStream_t stream) {
+  if (dt == QG_BF16)
+    hipLaunchKernelGGL((dequant_kernel<FMT, true>), dim3(blocks_for(total)), dim3(kThreads), 0,
+                       stream, codes, scales, zeros, total, t_vecs, dst);
+  else
+    hipLaunchKernelGGL((dequant_kernel<FMT, false>), dim3(blocks_for(total)), dim3(kThreads), 0,
+                       stream, codes, scales, zeros, total, t_vecs, dst);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(qg_format fmt, const void* src, qg_dtype src_dtype, int64_t rows,
+                           int64_t K, int64_t group, void* codes, void* scales, void* zeros,
+                           hipStream_t stream) {
+  if (src_dtype == QG_BF16)
+    launch_quant_fmt<true>(fmt, src, rows, K, group, codes, scales, zeros, stream);
+  else
+    launch_quant_fmt<false>(fmt, src, rows, K, group, codes, scales, zeros, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(qg_format fmt, const void* codes, const void* scales,
+                          const void* zeros, int64_t rows, int64_t K, int64_t group, void* dst,
+                          qg_dtype dst_dtype, hipStream_t stream) {
+  const int64_t total = rows * K / 8;
+  const int64_t t_vecs = group / 8;
+  switch (fmt) {
+    case QG_INT4_SYM:
+      launch_dequant_t<QG_INT4_SYM>(codes, scales, zeros, total, t_vecs, dst, dst_dtype, stream);
+      break;
+    case QG_INT4_ASYM:
+      launch_dequant_t<QG_INT4_ASYM>(codes, scales, zeros, total, t_vecs, dst, dst_dtype, stream);
+      break;
+    case QG_INT8_SYM:
+      launch_dequant_t<QG_INT8_SYM>(codes, scales, zeros, total, t_vecs, dst, dst_dtype, stream);
+      break;
+    case QG_INT8_ASYM:
+      launch_dequant_t<QG_INT8_ASYM>(codes, scales, zeros, total, t_vecs, dst, dst_dtype, stream);
+      break;
+    case QG_FP8_E4M3:
+      launch_dequant_t<QG_FP8_E4M3>(codes, scales, zeros, total, t_vecs, dst, dst_dtype, stream);
+      break;
+    default:
+      launch_dequant_t<QG_MXFP4>(codes, scales, zeros, total, t_vecs, dst, dst_dtype, stream);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
+                           void* codes, void* e8m0, hipStream_t stream) {
+  const int64_t total = rows * K / 8;
+  if (src_dtype == QG_BF16)
+    hipLaunchKernelGGL((mx_quant_kernel<true>), dim3(blocks_for(total)), dim3(kThreads), 0,
+                       stream, src, total, codes, e8m0);
+  else
+    hipLaunchKernelGGL((mx_quant_kernel<false>), dim3(blocks_for(total)), dim3(kThreads), 0,
+                       stream, src, total, codes, e8m0);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,111 @@
+"""The C ABI library: it loads without a GPU, exports every entry point the
+header declares, and rejects invalid arguments before any HIP call (so these
+tests never launch a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_gemm_group_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+vp = ctypes.c_void_p
+A16 = vp(0x1000)      # fake, aligned: never dereferenced (validation fails first)
+A16b = vp(0x2000)
+A16c = vp(0x3000)
+A16d = vp(0x4000)
+A16e = vp(0x5000)
+MIS = vp(0x1008)      # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declarations_are_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:qg_status|const char\*|int)\s+(qg_\w+)\s*\(", text, re.M))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qg_abi_version() == 1
+    assert lib.qg_status_str(_lib.ERR_GEOMETRY) == b"invalid quantization geometry"
+    assert lib.qg_status_str(_lib.OK) == b"ok"
+    assert lib.qg_status_str(99) == b"unknown status"
+
+
+def test_quantize_pack_validation(lib):
+    q = lib.qg_quantize_pack
+    assert q(_lib.INT4_SYM, A16, _lib.F32, 4, 256, 100, A16b, A16c, None, None) == _lib.ERR_GEOMETRY
+    assert q(_lib.INT4_SYM, A16, _lib.F32, 4, 256, 0, A16b, A16c, None, None) == _lib.ERR_GEOMETRY
+    assert q(_lib.INT4_SYM, A16, _lib.F32, 0, 256, 128, A16b, A16c, None, None) == _lib.ERR_GEOMETRY
+    assert q(_lib.INT4_SYM, A16, _lib.F32, 4, 12, 12, A16b, A16c, None, None) == _lib.ERR_GEOMETRY
+    assert q(_lib.INT4_ASYM, A16, _lib.F32, 4, 256, 128, A16b, A16c, None, None) == _lib.ERR_NULL
+    assert q(_lib.INT4_SYM, A16, _lib.F32, 4, 256, 128, A16b, A16c, A16d, None) == _lib.ERR_NULL
+    assert q(_lib.INT4_SYM, None, _lib.F32, 4, 256, 128, A16b, A16c, None, None) == _lib.ERR_NULL
+    assert q(_lib.INT4_SYM, MIS, _lib.F32, 4, 256, 128, A16b, A16c, None, None) == _lib.ERR_ALIGN
+    assert q(_lib.BF16_ACT, A16, _lib.F32, 4, 256, 128, A16b, A16c, None, None) == _lib.ERR_FORMAT
+    assert q(_lib.INT8_SYM, A16, 7, 4, 256, 256, A16b, A16c, None, None) == _lib.ERR_FORMAT
+
+
+def test_dequant_validation(lib):
+    d = lib.qg_dequant
+    assert d(_lib.MXFP4, A16, A16b, None, 4, 256, 64, A16c, _lib.F32, None) == _lib.ERR_GEOMETRY
+    assert d(_lib.INT4_SYM, A16, A16b, None, 4, 256, 128, None, _lib.F32, None) == _lib.ERR_NULL
+    assert d(_lib.INT4_SYM, A16, A16b, None, 4, 256, 128, MIS, _lib.F32, None) == _lib.ERR_ALIGN
+    assert d(_lib.INT4_SYM, A16, A16b, None, 4, 256, 128, A16c, 5, None) == _lib.ERR_FORMAT
+    assert d(_lib.BF16_ACT, A16, A16b, None, 4, 256, 128, A16c, _lib.F32, None) == _lib.ERR_FORMAT
+
+
+def test_qgemv_validation(lib):
+    g = lib.qg_qgemv
+    assert g(_lib.INT4_SYM, A16, 0, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert g(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 0, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 200, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 256, 64, A16e, None) == _lib.ERR_UNSUPPORTED
+    assert g(_lib.INT8_SYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_FORMAT
+    assert g(_lib.INT4_ASYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_NULL
+    assert g(_lib.INT4_SYM, MIS, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_ALIGN
+    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 256, 128, None, None) == _lib.ERR_NULL
+
+
+def test_qgemm_validation(lib):
+    g = lib.qg_qgemm
+    i4, bf, f8, i8 = _lib.INT4_SYM, _lib.BF16_ACT, _lib.FP8_E4M3, _lib.INT8_SYM
+    assert g(i4, f8, A16, None, None, 8, A16b, A16c, None, 8, 256, 128, A16e, None) == _lib.ERR_FORMAT
+    assert g(i4, bf, A16, None, None, 0, A16b, A16c, None, 8, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert g(i4, bf, A16, None, None, 8, A16b, A16c, None, 8, 256, 64, A16e, None) == _lib.ERR_UNSUPPORTED
+    assert g(f8, f8, A16, A16d, None, 8, A16b, A16c, None, 8, 256, 128, A16e, None) == _lib.ERR_UNSUPPORTED
+    assert g(f8, f8, A16, None, None, 8, A16b, A16c, None, 8, 256, 256, A16e, None) == _lib.ERR_NULL
+    assert g(i8, _lib.INT8_ASYM, A16, A16d, None, 8, A16b, A16c, None, 8, 256, 256, A16e,
+             None) == _lib.ERR_NULL
+    assert g(f8, f8, A16, A16d, None, 8, A16b, A16c, None, 8, 8, 8, A16e, None) == _lib.ERR_GEOMETRY
+
+
+def test_mx_validation(lib):
+    assert lib.qg_mx_quant(A16, _lib.BF16, 4, 48, A16b, A16c, None) == _lib.ERR_GEOMETRY
+    assert lib.qg_mx_quant(A16, _lib.BF16, 4, 0, A16b, A16c, None) == _lib.ERR_GEOMETRY
+    assert lib.qg_mx_quant(A16, _lib.BF16, 4, 64, None, A16c, None) == _lib.ERR_NULL
+    assert lib.qg_mx_quant(MIS, _lib.BF16, 4, 64, A16b, A16c, None) == _lib.ERR_ALIGN
+    assert lib.qg_mx_gemm(A16, A16b, 4, A16c, A16d, 4, 40, A16e, None) == _lib.ERR_GEOMETRY
+    assert lib.qg_mx_gemm(A16, A16b, 4, A16c, A16d, 0, 64, A16e, None) == _lib.ERR_GEOMETRY
+    assert lib.qg_mx_gemm(A16, None, 4, A16c, A16d, 4, 64, A16e, None) == _lib.ERR_NULL
+    assert lib.qg_mx_gemm(A16, A16b, 4, A16c, A16d, 4, 64, MIS, None) == _lib.ERR_ALIGN
+
+
+def test_python_raises_value_error_for_geometry(lib):
+    assert lib.qg_qgemv(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e,
+                        None) == _lib.ERR_GEOMETRY
+    with pytest.raises(ValueError, match="invalid quantization geometry"):
+        _lib.check(_lib.ERR_GEOMETRY)
+    with pytest.raises(_lib.QGError):
+        _lib.check(_lib.ERR_ALIGN)

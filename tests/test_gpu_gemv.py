@@ -1,0 +1,113 @@
+"""GPU parity of the W4A16 decode GEMV against the oracle's fp64 product of
+the dequantized operands: relative Frobenius error <= 2e-3, no NaN/Inf,
+bit-exact codes, and a one-hot layout pin (each output equals the bf16
+rounding of one dequantized weight)."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemm_group_amd as qg
+from oracle import formats as of, gemm as og, intquant as oi
+from synthetic import WORKLOADS, bf16_as_f32, rng_for, small_case, to_bf16, workload_case
+from tests.gpu_util import cosine, device, finite_checks, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def oracle_weights(w, asym):
+    if asym:
+        q, s, z = oi.quantize_asym(w, 128, "int4_asym")
+    else:
+        (q, s), z = oi.quantize_sym(w, 128, "int4_sym"), None
+    return oi.pack_int4(q), s, z
+
+
+def run_case(m, k, n, asym, seed, outliers=(0.01, 20.0)):
+    dev = device()
+    c = small_case(m, k, n, seed, w_outlier=outliers)
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"qgemv m={m} k={k} n={n} fmt={fmt} seed={seed}", flush=True)
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
+    packed, s, z = oracle_weights(c["w"], asym)
+    assert (host(codes) == packed).all()
+    y = host(qg.qgemv(to_dev(c["x"], dev), codes, scales, zeros, fmt))
+    ref = og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, 128)
+    finite_checks(y)
+    err = og.rel_fro(y, ref)
+    assert err <= TOL, f"rel_fro {err}"
+    assert cosine(y, ref) > 0.99
+    return err
+
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("m,k,n", [(1, 128, 64), (1, 1024, 200), (3, 1024, 200), (4, 4096, 1000),
+                                   (16, 2048, 333), (7, 14336, 96), (16, 640, 48)])
+def test_qgemv_small(m, k, n, asym):
+    run_case(m, k, n, asym, seed=m * 1000 + n)
+
+
+def test_qgemv_ragged_single_row():
+    run_case(1, 256, 1, True, seed=3)
+    run_case(2, 256, 17, False, seed=4)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_qgemv_one_hot_is_bit_exact(asym):
+    # x rows are unit vectors e_k: y[m][n] = bf16(w_hat[n][k_m]) exactly
+    dev = device()
+    k, n = 1024, 80
+    w = (rng_for(9).standard_normal((n, k), dtype=np.float32) * np.float32(0.02))
+    fmt = "int4_asym" if asym else "int4_sym"
+    codes, scales, zeros = qg.quantize_pack(to_dev(w, dev), fmt, 128)
+    packed, s, z = oracle_weights(w, asym)
+    ks = [0, 1, 7, 8, 127, 128, 300, 1023, 513, 64, 65, 1000, 5, 6, 900, 777]
+    x = np.zeros((16, k), np.float32)
+    x[np.arange(16), ks] = 1.0
+    y = host(qg.qgemv(to_dev(to_bf16(x), dev), codes, scales, zeros, fmt))
+    q = oi.unpack_int4(packed, signed=not asym)
+    w_hat = oi.dequantize(q, s, z, 128, out="f32")
+    expect = of.round_to_bf16(w_hat[:, ks].T)
+    assert (y.view(np.uint32) == expect.view(np.uint32)).all()
+
+
+def test_qgemv_gemv_4096_full():
+    dev = device()
+    c = workload_case("gemv_4096")
+    print("qgemv gemv_4096 M=1 K=N=4096 int4_sym", flush=True)
+    codes, scales, _ = qg.quantize_pack(to_dev(c["w"], dev), "int4_sym", 128)
+    packed, s, _ = oracle_weights(c["w"], False)
+    assert (host(codes) == packed).all()
+    assert (host(scales).view(np.uint16) == s.view(np.uint16)).all()
+    x = c["x"][:1]
+    y = host(qg.qgemv(to_dev(x, dev), codes, scales, None, "int4_sym"))
+    ref = og.w4a16_reference(bf16_as_f32(x), packed, s, None, 128)
+    finite_checks(y)
+    assert og.rel_fro(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("proj", range(4))
+def test_qgemv_llama3_8b_decode_sampled(proj):
+    # full-size shapes, all three batch sizes; codes and outputs checked on
+    # sampled output channels (the oracle quantizes those rows itself)
+    dev = device()
+    c = workload_case("llama3_8b_decode", proj)
+    n, k = c["n"], c["k"]
+    print(f"qgemv llama3_8b_decode {c['name']} K={k} N={n}", flush=True)
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), "int4_asym", 128)
+    rng = np.random.default_rng(proj)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
+                                     rng.choice(n, 160, replace=False)]))
+    packed, s, z = oracle_weights(c["w"][rows], True)
+    assert (host(codes)[rows] == packed).all()
+    assert (host(scales)[rows].view(np.uint16) == s.view(np.uint16)).all()
+    assert (host(zeros)[rows].view(np.uint16) == z.view(np.uint16)).all()
+    xs = bf16_as_f32(c["x"])
+    for m in WORKLOADS["llama3_8b_decode"].ms:
+        y = host(qg.qgemv(to_dev(c["x"][:m], dev), codes, scales, zeros, "int4_asym"))
+        finite_checks(y)
+        ref = og.w4a16_reference(xs[:m], packed, s, z, 128)
+        err = og.rel_fro(y[:, rows], ref)
+        assert err <= TOL, f"M={m} rel_fro {err}"
