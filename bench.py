@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized linear layer on one MI355X.
+
+Headline: W4A16 decode, Llama-3-8B projection shapes (K->N 4096->6144 QKV,
+4096->4096 O, 4096->28672 gate+up, 14336->4096 down), asymmetric INT4 in
+groups of 128, M = 1.  One step = the four GEMVs of one layer; steps rotate
+over distinct weight copies (more than the 256 MiB last-level cache) so every
+step streams its weights from HBM.  Steps are replayed from a HIP graph
+(captured through torch), so launch overhead on the host is not measured.
+
+value = algorithmic bytes of the timed steps / time (GB/s): packed codes +
+fp16 scales and zero points + bf16 activations + bf16 outputs.
+
+Also reported (``detail``): the same layer at M = 4 and 16, the 4096x4096
+GEMV, and the prefill-size GEMMs -- FP8 E4M3 W8A8 (M=N=K=8192, dynamic
+per-token activation quantization timed separately), MXFP4 W4A4 (M=4096,
+N=K=8192) and W4A16 prefill (M=2048, Qwen2.5-72B FFN shapes) -- in TFLOP/s
+against the matching dense matrix-core peak.
+
+``roofline`` describes the dominant kernel (the gate+up GEMV launch), timed
+with HIP events around a graph of back-to-back launches on its own stream.
+``cpu_baseline`` times the CPU oracle (numpy) on one layer at M = 1.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-detail", action="store_true", help="headline only")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ helpers
+
+def graph_of(fn, stream):
+    """Capture fn() (a sequence of library launches) into a CUDA/HIP graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()                                   # warm (library and allocator)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, stream, reps=1):
+    import torch
+    st = torch.cuda.Event(enable_timing=True)
+    en = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        st.record(stream)
+        for _ in range(reps):
+            g.replay()
+        en.record(stream)
+    en.synchronize()
+    return st.elapsed_time(en) * 1e-3
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src, key):
+    """HBM bytes per launch measured with rocprofv3 counters (committed under
+    profiles/), or None if missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        ent = data[key]
+        if ent.get("source_sha256_16") != source_hash(kernel_src):
+            return None
+        return float(ent["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+# ------------------------------------------------------------ decode layer
+
+def build_decode_layer(dev):
+    """Quantized weights of the four projections (asymmetric INT4 g128) and
+    bf16 activations (16 rows; M rows are the first M)."""
+    import torch
+    import quantized_gemm_group_amd as qg
+    from synthetic import WORKLOADS, workload_case
+    layer = []
+    for i, p in enumerate(WORKLOADS["llama3_8b_decode"].projections):
+        c = workload_case("llama3_8b_decode", i)
+        w = torch.from_numpy(c["w"]).to(dev)
+        codes, s, z = qg.quantize_pack(w, "int4_asym", 128)
+        del w
+        layer.append(dict(name=p.name, k=p.k, n=p.n, codes=codes, s=s, z=z,
+                          x=c["x"].to(dev), w_host=c["w"], x_host=c["x"]))
+    torch.cuda.synchronize()
+    return layer
+
+
+def layer_bytes(layer, m):
+    tot = 0
+    for p in layer:
+        tot += p["codes"].numel() * 4 + p["s"].numel() * 2 + p["z"].numel() * 2
+        tot += m * p["k"] * 2 + m * p["n"] * 2
+    return tot
+
+
+def proj_bytes(p, m):
+    return p["codes"].numel() * 4 + p["s"].numel() * 4 + m * p["k"] * 2 + m * p["n"] * 2
+
+
+def decode_copies(layer, count):
+    copies = [layer]
+    for _ in range(count - 1):
+        copies.append([dict(p, codes=p["codes"].clone(), s=p["s"].clone(), z=p["z"].clone())
+                       for p in layer])
+    return copies
+
+
+def run_layer(qg, lay, m, outs):
+    for p, y in zip(lay, outs):
+        qg.qgemv(p["x"][:m], p["codes"], p["s"], p["z"], "int4_asym", out=y)
+
+
+def bench_decode(qg, torch, copies, m, steps, warmup, stream):
+    outs = [torch.empty((m, p["n"]), dtype=torch.bfloat16, device=p["x"].device)
+            for p in copies[0]]
+
+    def seq(nsteps):
+        def f():
+            for s in range(nsteps):
+                run_layer(qg, copies[s % len(copies)], m, outs)
+        return f
+    gw = graph_of(seq(max(warmup, 1)), stream)
+    gt = graph_of(seq(steps), stream)
+    time_graph(gw, stream)
+    torch.cuda.synchronize()
+    t = time_graph(gt, stream)
+    torch.cuda.synchronize()
+    return t
+
+
+def bench_dominant(qg, torch, copies, stream, reps=40):
+    """Back-to-back launches of the gate+up GEMV (M=1) over rotating copies."""
+    idx = [i for i, p in enumerate(copies[0]) if p["name"] == "gate_up"][0]
+    p0 = copies[0][idx]
+    y = torch.empty((1, p0["n"]), dtype=torch.bfloat16, device=p0["x"].device)
+
+    def f():
+        for r in range(reps):
+            p = copies[r % len(copies)][idx]
+            qg.qgemv(p["x"][:1], p["codes"], p["s"], p["z"], "int4_asym", out=y)
+    g = graph_of(f, stream)
+    time_graph(g, stream)
+    t = time_graph(g, stream)
+    return t / reps, proj_bytes(p0, 1)
+
+
+# --------------------------------------------------------------- GEMMs
+
+def bench_gemms(qg, torch, dev, stream):
+    from synthetic import workload_case
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(reps):
+            fn()
+        en.record()
+        en.synchronize()
+        return st.elapsed_time(en) * 1e-3 / reps
+
+    # FP8 W8A8, M=N=K=8192
+    c = workload_case("fp8_8192")
+    x = c["x"].to(dev)
+    wq, sw, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "fp8_e4m3")
+    xq, sx, _ = qg.quantize_pack(x, "fp8_e4m3")
+    y = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    t = timed(lambda: qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx, out=y), 10)
+    tq = timed(lambda: qg.quantize_pack(x, "fp8_e4m3"), 10)
+    fl = 2 * 8192 ** 3
+    out["fp8_gemm_8192"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
+                                frac=fl / t / 1e12 / PEAK_TFLOPS["fp8"],
+                                act_quant_us=tq * 1e6,
+                                act_quant_gbs=(8192 * 8192 * 3 + 8192 * 4) / tq / 1e9,
+                                end_to_end_tflops=fl / (t + tq) / 1e12)
+    del x, wq, sw, xq, sx, y, c
+    # MXFP4, M=4096, N=K=8192
+    c = workload_case("mxfp4_4096x8192")
+    x = c["x"].to(dev)
+    bc, be = qg.mx_quant(torch.from_numpy(c["w"]).to(dev))
+    ac, ae = qg.mx_quant(x)
+    y = torch.empty((4096, 8192), dtype=torch.bfloat16, device=dev)
+    t = timed(lambda: qg.mx_gemm(ac, ae, bc, be, out=y), 10)
+    tq = timed(lambda: qg.mx_quant(x), 10)
+    fl = 2 * 4096 * 8192 * 8192
+    out["mxfp4_gemm_4096x8192"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
+                                       frac=fl / t / 1e12 / PEAK_TFLOPS["fp4"],
+                                       act_quant_us=tq * 1e6,
+                                       end_to_end_tflops=fl / (t + tq) / 1e12)
+    del x, bc, be, ac, ae, y, c
+    # W4A16 prefill, Qwen2.5-72B FFN shapes
+    for i, name in enumerate(["ffn_up", "ffn_down"]):
+        c = workload_case("qwen72b_prefill", i)
+        x = c["x"].to(dev)
+        codes, s, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_sym", 128)
+        y = torch.empty((2048, c["n"]), dtype=torch.bfloat16, device=dev)
+        t = timed(lambda: qg.qgemm(x, codes, s, None, "int4_sym", "bf16", out=y), 5)
+        fl = 2 * 2048 * c["k"] * c["n"]
+        out[f"w4a16_prefill_{name}"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
+                                            frac=fl / t / 1e12 / PEAK_TFLOPS["bf16"])
+        del x, codes, s, y, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_gemv_4096(qg, torch, dev, stream):
+    from synthetic import workload_case
+    c = workload_case("gemv_4096")
+    codes, s, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_sym", 128)
+    per = codes.numel() * 4 + s.numel() * 2
+    r = max(2, -(-2 * MALL_BYTES // per))
+    bufs = [(codes.clone(), s.clone()) for _ in range(r)]
+    x = c["x"][:1].to(dev)
+    y = torch.empty((1, 4096), dtype=torch.bfloat16, device=dev)
+
+    def f():
+        for i in range(r):
+            qg.qgemv(x, bufs[i][0], bufs[i][1], None, "int4_sym", out=y)
+    g = graph_of(f, stream)
+    time_graph(g, stream)
+    t = time_graph(g, stream) / r
+    b = per + 4096 * 2 * 2
+    return dict(us=t * 1e6, gbs=b / t / 1e9, frac=b / t / 1e9 / HBM_PEAK_GBS, copies=r)
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(layer):
+    """The oracle as it stands on one layer at M = 1 (quantize the weights,
+    then the fp64 product of the dequantized operands)."""
+    import numpy as np
+    from oracle import gemm as og, intquant as oi
+    from synthetic import bf16_as_f32
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    nbytes = 0
+    for p in layer:
+        q, s, z = oi.quantize_asym(p["w_host"], 128)
+        packed = oi.pack_int4(q)
+        og.w4a16_reference(bf16_as_f32(p["x_host"][:1]), packed, s, z, 128)
+        nbytes += packed.nbytes + s.nbytes + z.nbytes + p["k"] * 2 + p["n"] * 2
+    t = time.perf_counter() - t0
+    return dict(value=nbytes / t / 1e9, unit="GB/s", cores=int(blas_threads), kind="oracle",
+                sample="one Llama-3-8B layer (QKV, O, gate+up, down) at M=1: oracle INT4 "
+                       f"quantization + fp64 dequantized product, {t:.1f} s")
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_gemm_group_amd as qg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    qg.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+
+    log("building the decode layer ...")
+    layer = build_decode_layer(dev)
+    per_layer = layer_bytes(layer, 1)
+    ncopies = max(2, -(-2 * MALL_BYTES // per_layer))      # > 2x the last-level cache
+    copies = decode_copies(layer, ncopies)
+    log(f"layer {per_layer / 1e6:.1f} MB x {ncopies} copies")
+
+    t = bench_decode(qg, torch, copies, 1, args.steps, args.warmup, stream)
+    value = args.steps * per_layer / t / 1e9
+    ms_per_step = t / args.steps * 1e3
+
+    dom_t, dom_b = bench_dominant(qg, torch, copies, stream)
+    achieved = dom_b / dom_t / 1e9
+    traffic = traffic_from_profile(os.path.join(ROOT, "quantized_gemm_group_amd", "csrc",
+                                                "qg_gemv.hip"), "qgemv_gate_up_m1")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "qgemv_kernel<2,true> (gate+up 4096->28672, M=1)",
+                "us_per_launch": round(dom_t * 1e6, 3), "bytes_per_launch": dom_b}
+
+    detail = {}
+    if not args.no_detail:
+        for m in (4, 16):
+            tm = bench_decode(qg, torch, copies, m, max(20, args.steps // 4), 5, stream)
+            b = layer_bytes(layer, m) * max(20, args.steps // 4)
+            detail[f"decode_layer_m{m}"] = dict(gbs=b / tm / 1e9,
+                                                frac=b / tm / 1e9 / HBM_PEAK_GBS,
+                                                us_per_layer=tm / max(20, args.steps // 4) * 1e6)
+        detail["decode_layer_m1"] = dict(gbs=value, frac=value / HBM_PEAK_GBS,
+                                         us_per_layer=ms_per_step * 1e3)
+        del copies
+        torch.cuda.empty_cache()
+        detail["gemv_4096"] = bench_gemv_4096(qg, torch, dev, stream)
+        log("GEMMs ...")
+        detail.update(bench_gemms(qg, torch, dev, stream))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline(layer)
+
+    line = {
+        "metric": "W4A16 GEMV HBM GB/s (% peak) + MXFP4/FP8 GEMM TFLOPS (% MFMA peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights with 1% outlier input channels x20, N(0,1) bf16 activations)",
+        "config": {"workload": "llama3_8b_decode: one layer's QKV 4096->6144, O 4096->4096, "
+                               "gate+up 4096->28672, down 14336->4096 W4A16 GEMVs, M=1, "
+                               "asymmetric INT4 group 128",
+                   "bytes_per_step": per_layer, "weight_copies": ncopies},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

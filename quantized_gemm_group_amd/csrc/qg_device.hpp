@@ -97,9 +97,10 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
 
 __device__ __forceinline__ float e2m1_decode(uint32_t c) {
   const uint32_t m = c & 7u;
-  // 0 .5 1 1.5 2 3 4 6 = (m < 2) ? m/2 : (2 + (m&1)) * 2^((m>>1)-1)
+  // codes 0,1 are subnormal (0, 0.5); codes 2..7 are 2^(e-1) * (1 + f/2) with
+  // e = m >> 1, f = m & 1, i.e. (2 + f) * 2^(e-2): 1 1.5 2 3 4 6
   float mag = (m < 2u) ? 0.5f * (float)m
-                       : __builtin_ldexpf((float)(2u + (m & 1u)), (int)(m >> 1) - 1);
+                       : __builtin_ldexpf((float)(2u + (m & 1u)), (int)(m >> 1) - 2);
   return (c & 8u) ? -mag : mag;
 }
 

@@ -1,0 +1,201 @@
+"""GPU parity of the quantized GEMMs against the oracle's fp64 product of the
+dequantized operands (relative Frobenius error <= 2e-3, no NaN/Inf), with
+bit-exact operand codes: FP8 W8A8 with dynamic per-token activation scales,
+MXFP4 W4A4, INT8 W8A8 (symmetric/asymmetric pairs) and the W4A16 prefill
+GEMM.  Small cases span several tiles with ragged M/N/K tails; the full-size
+workloads are checked on sampled rows (the oracle quantizes those rows of the
+seeded inputs itself)."""
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_gemm_group_amd as qg
+from oracle import fp8 as of8, gemm as og, intquant as oi, mx as omx
+from synthetic import (bf16_as_f32, rng_for, small_case, to_bf16, workload_case,
+                       normal_activations, normal_weights, scale_input_channels,
+                       scale_random_entries)
+from tests.gpu_util import cosine, device, finite_checks, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def check(y, ref, what):
+    finite_checks(y)
+    err = og.rel_fro(y, ref)
+    assert err <= TOL, f"{what}: rel_fro {err}"
+    assert cosine(y, ref) > 0.99
+    return err
+
+
+# ----------------------------------------------------------------------- FP8
+
+def fp8_case(m, k, n, seed):
+    c = small_case(m, k, n, seed, x_outlier=(0.001, 100.0))
+    return c["w"], c["x"]
+
+
+@pytest.mark.parametrize("m,k,n", [(64, 256, 80), (130, 512, 200), (257, 1040, 129), (1, 128, 16),
+                                   (300, 2048, 384)])
+def test_fp8_gemm_small(m, k, n):
+    dev = device()
+    w, x = fp8_case(m, k, n, seed=m + n + k)
+    print(f"fp8 gemm m={m} k={k} n={n}", flush=True)
+    xq, sx, _ = qg.quantize_pack(to_dev(x, dev), "fp8_e4m3")
+    wq, sw, _ = qg.quantize_pack(to_dev(w, dev), "fp8_e4m3")
+    oxq, osx = of8.quantize_rows(bf16_as_f32(x))
+    owq, osw = of8.quantize_rows(w)
+    assert (host(xq) == oxq).all() and (host(wq) == owq).all()
+    y = host(qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx))
+    check(y, og.fp8_reference(oxq, osx, owq, osw), "fp8")
+
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+                                     rng.choice(n, count, replace=False)]))
+
+
+def test_fp8_gemm_8192_sampled():
+    dev = device()
+    c = workload_case("fp8_8192")
+    print("fp8 gemm M=N=K=8192", flush=True)
+    xq, sx, _ = qg.quantize_pack(to_dev(c["x"], dev), "fp8_e4m3")
+    wq, sw, _ = qg.quantize_pack(to_dev(c["w"], dev), "fp8_e4m3")
+    y = host(qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx))
+    rm, rn = _sample_rows(8192, 80, 1), _sample_rows(8192, 80, 2)
+    oxq, osx = of8.quantize_rows(bf16_as_f32(c["x"][rm]))
+    owq, osw = of8.quantize_rows(c["w"][rn])
+    assert (host(xq)[rm] == oxq).all() and (host(sx)[rm, 0] == osx).all()
+    assert (host(wq)[rn] == owq).all() and (host(sw)[rn, 0] == osw).all()
+    check(y[np.ix_(rm, rn)], og.fp8_reference(oxq, osx, owq, osw), "fp8 8192")
+
+
+# ---------------------------------------------------------------------- MXFP4
+
+@pytest.mark.parametrize("m,k,n", [(64, 256, 64), (130, 512, 200), (33, 1056, 129), (1, 32, 16),
+                                   (256, 4096, 260)])
+def test_mx_gemm_small(m, k, n):
+    dev = device()
+    c = small_case(m, k, n, seed=3 * m + n, w_outlier=(0.01, 50.0))
+    print(f"mx gemm m={m} k={k} n={n}", flush=True)
+    ac, ae = qg.mx_quant(to_dev(c["x"], dev))
+    bc, be = qg.mx_quant(to_dev(c["w"], dev))
+    oac, oae = omx.quantize(bf16_as_f32(c["x"]))
+    obc, obe = omx.quantize(c["w"])
+    assert (host(ac) == oac).all() and (host(ae) == oae).all()
+    assert (host(bc) == obc).all() and (host(be) == obe).all()
+    y = host(qg.mx_gemm(ac, ae, bc, be))
+    check(y, og.mx_reference(oac, oae, obc, obe), "mx")
+
+
+def test_mx_gemm_4096x8192_sampled():
+    dev = device()
+    c = workload_case("mxfp4_4096x8192")
+    print("mx gemm M=4096 N=K=8192", flush=True)
+    ac, ae = qg.mx_quant(to_dev(c["x"], dev))
+    bc, be = qg.mx_quant(to_dev(c["w"], dev))
+    y = host(qg.mx_gemm(ac, ae, bc, be))
+    rm, rn = _sample_rows(4096, 80, 3), _sample_rows(8192, 80, 4)
+    oac, oae = omx.quantize(bf16_as_f32(c["x"][rm]))
+    obc, obe = omx.quantize(c["w"][rn])
+    assert (host(ac)[rm] == oac).all() and (host(ae)[rm] == oae).all()
+    assert (host(bc)[rn] == obc).all() and (host(be)[rn] == obe).all()
+    check(y[np.ix_(rm, rn)], og.mx_reference(oac, oae, obc, obe), "mx 4096x8192")
+
+
+# ----------------------------------------------------------------------- INT8
+
+def _int8_oracle(v, fmt):
+    k = v.shape[1]
+    if fmt == "int8_sym":
+        q, s = oi.quantize_sym(v, k, "int8_sym")
+        return q.astype(np.int8), s, None
+    q, s, z = oi.quantize_asym(v, k, "int8_asym")
+    return q.astype(np.uint8), s, z
+
+
+@pytest.mark.parametrize("afmt", ["int8_sym", "int8_asym"])
+@pytest.mark.parametrize("wfmt", ["int8_sym", "int8_asym"])
+@pytest.mark.parametrize("m,k,n", [(64, 256, 80), (130, 1040, 200)])
+def test_int8_gemm(m, k, n, afmt, wfmt):
+    dev = device()
+    c = small_case(m, k, n, seed=m * 7 + n, x_outlier=(0.001, 100.0))
+    x = bf16_as_f32(c["x"])
+    if afmt == "int8_asym":
+        x = x + np.float32(0.75)              # a shifted activation distribution
+        x = bf16_as_f32(to_bf16(x))
+    print(f"int8 gemm m={m} k={k} n={n} a={afmt} w={wfmt}", flush=True)
+    aq, as_, az = qg.quantize_pack(to_dev(to_bf16(x), dev), afmt)
+    wq, ws, wz = qg.quantize_pack(to_dev(c["w"], dev), wfmt)
+    oaq, oas, oaz = _int8_oracle(x, afmt)
+    owq, ows, owz = _int8_oracle(c["w"], wfmt)
+    assert (host(aq) == oaq).all() and (host(wq) == owq).all()
+    y = host(qg.qgemm(aq, wq, ws, wz, wfmt, afmt, a_scales=as_, a_zeros=az))
+    ref = og.int8_reference(oaq.astype(np.int64), oas, oaz, owq.astype(np.int64), ows, owz)
+    check(y, ref, f"int8 {afmt}/{wfmt}")
+
+
+def test_int8_gemm_4096_sampled():
+    dev = device()
+    rng = rng_for(44)
+    w = normal_weights(rng, 4096, 4096)
+    x = normal_activations(rng, 4096, 4096)
+    scale_random_entries(rng, x, 0.001, 100.0)
+    xb = to_bf16(x)
+    print("int8 gemm M=N=K=4096 asym activations, sym weights", flush=True)
+    aq, as_, az = qg.quantize_pack(to_dev(xb, dev), "int8_asym")
+    wq, ws, _ = qg.quantize_pack(to_dev(w, dev), "int8_sym")
+    y = host(qg.qgemm(aq, wq, ws, None, "int8_sym", "int8_asym", a_scales=as_, a_zeros=az))
+    rm, rn = _sample_rows(4096, 64, 5), _sample_rows(4096, 64, 6)
+    oaq, oas, oaz = _int8_oracle(bf16_as_f32(xb[rm]), "int8_asym")
+    owq, ows, _ = _int8_oracle(w[rn], "int8_sym")
+    assert (host(aq)[rm] == oaq).all() and (host(wq)[rn] == owq).all()
+    ref = og.int8_reference(oaq.astype(np.int64), oas, oaz, owq.astype(np.int64), ows, None)
+    check(y[np.ix_(rm, rn)], ref, "int8 4096")
+
+
+# --------------------------------------------------------------- W4A16 prefill
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("m,k,n", [(64, 256, 80), (200, 1024, 136), (1, 128, 16), (300, 2048, 520)])
+def test_w4a16_gemm_small(m, k, n, asym):
+    dev = device()
+    c = small_case(m, k, n, seed=m + 11 * n, w_outlier=(0.01, 20.0))
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"w4a16 gemm m={m} k={k} n={n} {fmt}", flush=True)
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
+    if asym:
+        q, s, z = oi.quantize_asym(c["w"], 128)
+    else:
+        (q, s), z = oi.quantize_sym(c["w"], 128), None
+    packed = oi.pack_int4(q)
+    assert (host(codes) == packed).all()
+    y = host(qg.qgemm(to_dev(c["x"], dev), codes, scales, zeros, fmt, "bf16"))
+    check(y, og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, 128), f"w4a16 {fmt}")
+
+
+@pytest.mark.parametrize("proj", [0, 1])
+def test_w4a16_prefill_qwen72b_sampled(proj):
+    dev = device()
+    c = workload_case("qwen72b_prefill", proj)
+    print(f"w4a16 prefill {c['name']} M=2048 K={c['k']} N={c['n']}", flush=True)
+    codes, scales, _ = qg.quantize_pack(to_dev(c["w"], dev), "int4_sym", 128)
+    y = host(qg.qgemm(to_dev(c["x"], dev), codes, scales, None, "int4_sym", "bf16"))
+    rm, rn = _sample_rows(2048, 64, 7 + proj), _sample_rows(c["n"], 64, 9 + proj)
+    q, s = oi.quantize_sym(c["w"][rn], 128)
+    packed = oi.pack_int4(q)
+    assert (host(codes)[rn] == packed).all()
+    assert (host(scales)[rn].view(np.uint16) == s.view(np.uint16)).all()
+    ref = og.w4a16_reference(bf16_as_f32(c["x"][rm]), packed, s, None, 128)
+    check(y[np.ix_(rm, rn)], ref, "w4a16 prefill")
+
+
+def test_qgemm_format_pair_errors():
+    dev = device()
+    a = torch.zeros((4, 128), dtype=torch.uint8, device=dev)
+    with pytest.raises(qg.QGError):
+        qg.qgemm(a, a, torch.ones((4, 1), device=dev), None, "fp8_e4m3", "int8_sym",
+                 a_scales=torch.ones((4, 1), device=dev))
