@@ -321,7 +321,7 @@ def main():
                                                 "qg_gemv.hip"), "qgemv_gate_up_m1")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "qgemv_kernel<2,true> (gate+up 4096->28672, M=1)",
+                "traffic": traffic, "kernel": "qgemv_kernel<asym, x in LDS> (gate+up 4096->28672, M=1)",
                 "us_per_launch": round(dom_t * 1e6, 3), "bytes_per_launch": dom_b}
 
     detail = {}

@@ -7,24 +7,28 @@
 // the asymmetric zero-point cross term kept (same lesson, section 3).
 //
 // Design for gfx950 (64-wide waves, bf16 MFMA):
-//  * Each workgroup owns a tile of 16*RT output channels and splits K among
-//    its KS waves; a wave walks its groups of 128 with 128-bit loads: lane l
-//    reads 16 bytes (32 nibbles) of row l%16 at byte offset 16*(l/16) of the
-//    group, so one load instruction covers 16 rows x 64 contiguous bytes and
-//    the next group completes each 128-byte line.
-//  * Nibbles are unpacked in registers with one and/or per pair:
-//    (w >> 4j) & 0x000F000F | 0x43004300 is the bf16 pair (128+u_j, 128+u_{j+4}),
-//    exact integers, so the matrix cores multiply exact codes and the product
-//    needs no rounding of dequantized weights.  The activations are loaded
-//    with the same pairing (x_j, x_{j+4}) by a byte permute.
-//  * v_mfma_f32_16x16x32_bf16 accumulates, per group, A = codes (rows n) times
-//    B = x^T (columns m, zero beyond M), and a second MFMA with A = 1.0 gives
-//    the group sums of x.  The fp32 flush per group is
-//        y += s * (acc - c * sum_x),  c = 128 + z (asymmetric) or 136
-//    (symmetric codes are stored two's complement; xor 0x8 maps q to q + 8).
-//  * Group scales and offsets (s, c) of the tile are staged once in LDS as
-//    fp32 pairs; at the end the KS partial tiles are summed through LDS and
-//    rounded once to bf16 (RNE).
+//  * A wave owns 16 output channels and a slice of the K groups.  Lane l
+//    reads 16 bytes (32 nibbles) of row l%16 at byte offset 16*(l/16) of a
+//    group: one 128-bit load covers 16 rows x 64 contiguous bytes, the next
+//    group completes each 128-byte line.  Loads are raw buffer loads (rows
+//    past N read as zero).
+//  * Nibbles are unpacked in registers with one and/xor per pair:
+//    ((w >> 4j) & 0x000F000F) ^ C is the bf16 pair (128+u_j, 128+u_{j+4}),
+//    exact integers (u = q + 8 for two's-complement codes), so the matrix
+//    cores multiply exact codes and no dequantized weight is ever rounded.
+//  * v_mfma_f32_16x16x32_bf16: A = codes (16 channels), B = x^T (columns m,
+//    zero beyond M; pairs (x_j, x_{j+4}) to match the unpack), plus one MFMA
+//    with A = 1.0 for the group sums of x.  Per group, in fp32:
+//        y += s * (acc - c * sum_x),  c = 136 (symmetric) or 128 + z.
+//  * When M*K is small the activations are staged (pair-permuted) in LDS once
+//    per workgroup; the only vector-memory loads left in the loop are the
+//    weights, kept kRing groups deep in a register ring (vector loads
+//    complete in issue order, so a deep ring only works when nothing else
+//    shares the queue).  Larger M*K reads x from the cache and prefetches one
+//    group ahead.
+//  * Group scales and offsets (s, c) of the workgroup's rows are staged once
+//    in LDS; the K-slices of a row tile are summed through LDS and rounded
+//    once to bf16 (RNE).  No scratch memory.
 
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
@@ -33,18 +37,26 @@ namespace qg {
 namespace {
 
 constexpr int kGroup = 128;
+constexpr int kRing = 4;                    // weight groups in flight per wave
+constexpr int kXldsMaxBytes = 48 * 1024;    // x staged in LDS up to this size
+constexpr int kXu = 4;                      // x chunks per thread loaded ahead of the ring
+constexpr int kSu = 1;                      // 16-byte (s, z) loads per thread issued ahead
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Unpack one int32 of 8 nibbles into 4 bf16 pairs (128+u_j, 128+u_{j+4}).
-__device__ __forceinline__ u32x4 unpack_word(uint32_t w) {
+// ((w >> 4j) & 0x000F000F) ^ C per pair.  The mask and the constant arrive
+// as kernel arguments, so the compiler cannot fold them into literals (gfx950
+// VOP3 encodings take no literal operands) and selects one v_bitop3_b32 per
+// pair instead of shift, and, or with literals.
+template <bool ASYM>
+__device__ __forceinline__ u32x4 unpack_word(uint32_t w, uint32_t mask, uint32_t c) {
   u32x4 r;
-  r[0] = (w & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r[0] = (w & mask) ^ c;
+  r[1] = ((w >> 4) & mask) ^ c;
+  r[2] = ((w >> 8) & mask) ^ c;
+  r[3] = ((w >> 12) & mask) ^ c;
   return r;
 }
 
@@ -58,147 +70,296 @@ __device__ __forceinline__ u32x4 pair_activations(const u32x4& d) {
   return r;
 }
 
-// Loads of one group: RT x 16 bytes of codes and 4 x 16 bytes of activations.
-template <int RT>
-__device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t wres, __amdgpu_buffer_rsrc_t xres,
-                                           const uint32_t (&woff)[RT], uint32_t xoff, int g,
-                                           u32x4 (&a)[RT], u32x4 (&b)[4]) {
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-    a[rt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rt], g * 64, 0));
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff, g * 256 + i * 16, 0));
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// The math of one group for RT row tiles: MFMA over the 128 codes of each
-// row tile, the group sums of x by an MFMA with A = 1.0, then the fp32 flush
-// y += s * (acc - c * sum_x) with (s, c) read from LDS.
-template <int RT, bool ASYM>
-__device__ __forceinline__ void group_step(const u32x4 (&a)[RT], const u32x4 (&b)[4],
-                                           const float* lds, int g, int TR, int lg,
-                                           float (&yacc)[RT][4]) {
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  bf16x8 bx[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) bx[i] = as_bf16x8(pair_activations(b[i]));
+// One group of one 16-channel tile: 4 code MFMAs, then the flush
+// y += s * (acc - c * sum_x).  sum_x comes precomputed (x staged in LDS) or
+// from 4 more MFMAs against 1.0 (x read from the cache).
+template <bool ASYM, bool SUMX_GIVEN>
+__device__ __forceinline__ void group_math(const u32x4& a, const bf16x8 (&bx)[4], const float* sc,
+                                           float sx_given, uint32_t mask, uint32_t cmag,
+                                           float (&yacc)[4]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), bx[i], sacc, 0, 0, 0);
-  const float sx = sacc[0];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t word = a[rt][i];
-      if (!ASYM) word ^= 0x88888888u;
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(unpack_word(word)), bx[i], acc, 0,
-                                                    0, 0);
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (!SUMX_GIVEN) {
+      const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), bx[i], sacc, 0, 0, 0);
     }
-    const float4* sc = reinterpret_cast<const float4*>(lds + (g * TR + rt * 16 + lg * 4) * 2);
-    const float4 p01 = sc[0], p23 = sc[1];
-    const float sv[4] = {p01.x, p01.z, p23.x, p23.z};
-    const float cv[4] = {p01.y, p01.w, p23.y, p23.w};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(unpack_word<ASYM>(a[i], mask, cmag)),
+                                                  bx[i], acc, 0, 0, 0);
+  }
+  const float4 p01 = reinterpret_cast<const float4*>(sc)[0];
+  const float4 p23 = reinterpret_cast<const float4*>(sc)[1];
+  const float sx = SUMX_GIVEN ? sx_given : sacc[0];
+  yacc[0] = __builtin_fmaf(p01.x, __builtin_fmaf(-p01.y, sx, acc[0]), yacc[0]);
+  yacc[1] = __builtin_fmaf(p01.z, __builtin_fmaf(-p01.w, sx, acc[1]), yacc[1]);
+  yacc[2] = __builtin_fmaf(p23.x, __builtin_fmaf(-p23.y, sx, acc[2]), yacc[2]);
+  yacc[3] = __builtin_fmaf(p23.z, __builtin_fmaf(-p23.w, sx, acc[3]), yacc[3]);
+}
+
+// Stage the (s, c) pairs of rows [n0, n0 + TR) for all G groups into
+// scl[(g * TR + r) * 2 + {0, 1}]; four elements per thread in flight.
+template <bool ASYM>
+__device__ __forceinline__ void stage_scales(const uint16_t* __restrict__ s16,
+                                             const uint16_t* __restrict__ z16, int N, int G,
+                                             int n0, int TR, float* scl) {
+  const int total = TR * G;
+  for (int i0 = threadIdx.x; i0 < total; i0 += 4 * blockDim.x) {
+    uint16_t sv[4], zv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      yacc[rt][r] = __builtin_fmaf(sv[r], __builtin_fmaf(-cv[r], sx, acc[r]), yacc[rt][r]);
+    for (int u = 0; u < 4; ++u) {
+      const int idx = i0 + u * blockDim.x;
+      const int r = idx / G, g = idx - r * G;
+      const int n = n0 + r;
+      sv[u] = 0;
+      zv[u] = 0;
+      if (idx < total && n < N) {
+        sv[u] = s16[(int64_t)n * G + g];
+        if (ASYM) zv[u] = z16[(int64_t)n * G + g];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = i0 + u * blockDim.x;
+      if (idx >= total) continue;
+      const int r = idx / G, g = idx - r * G;
+      const bool ok = n0 + r < N;
+      scl[(g * TR + r) * 2] = ok ? f16_bits_to_f32(sv[u]) : 0.f;
+      scl[(g * TR + r) * 2 + 1] = ok ? (ASYM ? 128.f + f16_bits_to_f32(zv[u]) : 136.f) : 0.f;
+    }
   }
 }
 
-template <int RT, bool ASYM>
+// Workgroup = RW row tiles x KS K-slices, one wave each (wave = rw*KS + kw).
+//   LDS: [x: M*K bf16, pair-permuted (XLDS)] [sum_x: M*G floats (XLDS)]
+//        [sc: G * RW*16 float2]; then reused for the partial sums
+//        [RW][KS][4][64] floats.
+template <bool ASYM, bool XLDS, bool SVEC>
 __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict__ x, int M,
                                                      const uint32_t* __restrict__ w,
                                                      const uint16_t* __restrict__ s16,
                                                      const uint16_t* __restrict__ z16, int N,
-                                                     int K, uint16_t* __restrict__ y) {
+                                                     int K, int KS, int RW,
+                                                     uint16_t* __restrict__ y, uint32_t mask,
+                                                     uint32_t cmag) {
   extern __shared__ float4 lds4[];
-  float* lds = reinterpret_cast<float*>(lds4);
-  constexpr int TR = 16 * RT;                      // rows per workgroup
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds4);
   const int G = K / kGroup;
-  const int KS = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int li = lane & 15;
-  const int lg = lane >> 4;
-  const int n0 = blockIdx.x * TR;
+  const int li = lane & 15, lg = lane >> 4;
+  const int kw = wave % KS, rw = wave / KS;
+  const int tile0 = blockIdx.x * RW;                 // first row tile of the workgroup
+  const int TR = RW * 16;
 
-  // ---- stage (s, c) of every (group, row) of the tile: lds[(g*TR + r)*2 + {0,1}]
-  for (int idx = threadIdx.x; idx < TR * G; idx += blockDim.x) {
-    const int r = idx / G, g = idx - r * G;
-    const int n = n0 + r;
-    float s = 0.f, c = 0.f;
-    if (n < N) {
-      s = f16_bits_to_f32(s16[(int64_t)n * G + g]);
-      c = ASYM ? 128.f + f16_bits_to_f32(z16[(int64_t)n * G + g]) : 136.f;
-    }
-    lds[(g * TR + r) * 2] = s;
-    lds[(g * TR + r) * 2 + 1] = c;
-  }
-  __syncthreads();
+  const int gb = (int)((int64_t)kw * G / KS);
+  const int ge = (int)((int64_t)(kw + 1) * G / KS);
 
-  const int gb = (int)((int64_t)wave * G / KS);
-  const int ge = (int)((int64_t)(wave + 1) * G / KS);
-
-  // Raw buffer loads: bytes past the end of a buffer read as zero, which
-  // masks rows n >= N and activation rows m >= M without branches; being
-  // intrinsics (not plain loads) they also stay where they are issued, so the
-  // next group is in flight while the current one is computed.
+  const int64_t wbytes = (int64_t)N * K / 2;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)w, (short)0, (int)((int64_t)N * K / 2 > 0x7fffffff ? 0x7fffffff : (int64_t)N * K / 2),
-      0x00020000);
-  const __amdgpu_buffer_rsrc_t xres =
-      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
-  uint32_t woff[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int n = n0 + rt * 16 + li;
-    woff[rt] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + lg * 16 : 0x80000000u;
-  }
-  const uint32_t xoff = li < M ? (uint32_t)li * (uint32_t)(K * 2) + lg * 64 : 0x80000000u;
-  float yacc[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yacc[rt][r] = 0.f;
+      (void*)w, (short)0, (int)(wbytes > 0x7ffff000LL ? 0x7ffff000LL : wbytes), 0x00020000);
+  const int nrow = (tile0 + rw) * 16 + li;
+  const uint32_t woff = nrow < N ? (uint32_t)nrow * (uint32_t)(K / 2) + lg * 16 : 0x80000000u;
+  float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int xbytes = XLDS ? M * K * 2 : 0;
+  const int sxbytes = XLDS ? (M * G * 4 + 15) & ~15 : 0;
+  float* sxl = reinterpret_cast<float*>(lds + xbytes);
+  float* scl = reinterpret_cast<float*>(lds + xbytes + sxbytes);
+  const float* sc_base = scl + (rw * 16 + lg * 4) * 2;
 
-  // Two register sets used in ping-pong (no copies, so the prefetched loads
-  // are never waited for before they are needed).
-  u32x4 a0[RT], b0[4], a1[RT], b1[4];
-  if (gb < ge) load_group<RT>(wres, xres, woff, xoff, gb, a0, b0);
-  for (int g = gb; g < ge; g += 2) {
-    // unconditional prefetch (clamped: the last group re-reads itself, a
-    // cache hit); a branch here would make the compiler wait for it
-    load_group<RT>(wres, xres, woff, xoff, g + 1 < ge ? g + 1 : g, a1, b1);
+  if constexpr (XLDS) {
+    // ---- 1. staging loads first (x: kXu chunks, scales: kSu elements per
+    //      thread), then the weight ring: vector loads return in issue order,
+    //      so the staging data lands before the ring and the wait below does
+    //      not drain the ring.
+    const int chunks = M * K / 8;
+    const int total_sc = TR * G;
+    const int nt = blockDim.x;
+    u32x4 xv[kXu];
+    // unconditional loads from clamped (always valid) addresses: a
+    // predicated load makes the compiler wait for it on the spot; entries
+    // past the end are masked when written to LDS
+#pragma unroll
+    for (int u = 0; u < kXu; ++u) {
+      const int q = threadIdx.x + u * nt;
+      xv[u] = reinterpret_cast<const u32x4*>(x)[q < chunks ? q : chunks - 1];
+    }
+    // scales: 8 fp16 per 16-byte load when a row's groups come in whole
+    // 16-byte pieces (G % 8 == 0), else one element per load; the first
+    // kSu loads per thread are issued ahead of the ring
+    constexpr bool svec = SVEC;
+    const int total_sv = svec ? total_sc / 8 : total_sc;
+    u32x4 svv[kSu], zvv[kSu];
+#pragma unroll
+    for (int u = 0; u < kSu; ++u) {
+      int idx = threadIdx.x + u * nt;
+      idx = idx < total_sv ? idx : total_sv - 1;
+      if (svec) {
+        const int r = idx / (G / 8), gc = idx - r * (G / 8);
+        int n = tile0 * 16 + r;
+        n = n < N ? n : N - 1;
+        svv[u] = reinterpret_cast<const u32x4*>(s16 + (int64_t)n * G)[gc];
+        zvv[u] = ASYM ? reinterpret_cast<const u32x4*>(z16 + (int64_t)n * G)[gc] : svv[u];
+      } else {
+        const int r = idx / G, g = idx - r * G;
+        int n = tile0 * 16 + r;
+        n = n < N ? n : N - 1;
+        svv[u][0] = s16[(int64_t)n * G + g];
+        zvv[u][0] = ASYM ? z16[(int64_t)n * G + g] : (uint16_t)0;
+      }
+    }
+    u32x4 ring[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j)
+      ring[j] = bload(wres, gb + j < ge ? woff : 0x80000000u, (gb + j) * 64);
     __builtin_amdgcn_sched_barrier(0);
-    group_step<RT, ASYM>(a0, b0, lds, g, TR, lg, yacc);
-    if (g + 1 >= ge) break;
-    load_group<RT>(wres, xres, woff, xoff, g + 2 < ge ? g + 2 : g + 1, a0, b0);
+
+    // ---- 2. x into LDS pair-permuted, with the group sums of x (16
+    //      consecutive chunks of 8 form one group of 128; xor-shuffles sum them).
+    //      The preloaded first kXu rounds are handled straight-line so their
+    //      loads stay ahead of the ring.
+    auto put_x = [&](const u32x4& d, int q) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        part += bf16_bits_to_f32(d[e] & 0xffffu) + bf16_bits_to_f32(d[e] >> 16);
+      part += shfl_xor(part, 1);
+      part += shfl_xor(part, 2);
+      part += shfl_xor(part, 4);
+      part += shfl_xor(part, 8);
+      if (q < chunks) {
+        reinterpret_cast<u32x4*>(lds)[q] = pair_activations(d);
+        if ((q & 15) == 0) sxl[q >> 4] = part;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kXu; ++u) put_x(xv[u], threadIdx.x + u * nt);
+    for (int u = kXu; u * nt < chunks; ++u) {
+      const int q = threadIdx.x + u * nt;
+      put_x(reinterpret_cast<const u32x4*>(x)[q < chunks ? q : chunks - 1], q);
+    }
+    // ---- 3. (s, c) pairs
+    auto put_sc = [&](uint32_t sb, uint32_t zb, int r, int g) {
+      const bool ok = tile0 * 16 + r < N;
+      scl[(g * TR + r) * 2] = ok ? f16_bits_to_f32((uint16_t)sb) : 0.f;
+      scl[(g * TR + r) * 2 + 1] =
+          ok ? (ASYM ? 128.f + f16_bits_to_f32((uint16_t)zb) : 136.f) : 0.f;
+    };
+    auto put_sv = [&](const u32x4& sv, const u32x4& zv, int idx) {
+      if (idx >= total_sv) return;
+      if (svec) {
+        const int r = idx / (G / 8), g0 = (idx - r * (G / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          put_sc(sv[e >> 1] >> (16 * (e & 1)), zv[e >> 1] >> (16 * (e & 1)), r, g0 + e);
+      } else {
+        const int r = idx / G;
+        put_sc(sv[0], zv[0], r, idx - r * G);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kSu; ++u) put_sv(svv[u], zvv[u], threadIdx.x + u * nt);
+    for (int u = kSu; u * nt < total_sv; ++u) {
+      const int idx = threadIdx.x + u * nt;
+      const int ic = idx < total_sv ? idx : total_sv - 1;
+      u32x4 sv = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+      if (svec) {
+        const int r = ic / (G / 8), gc = ic - r * (G / 8);
+        int n = tile0 * 16 + r;
+        n = n < N ? n : N - 1;
+        sv = reinterpret_cast<const u32x4*>(s16 + (int64_t)n * G)[gc];
+        if (ASYM) zv = reinterpret_cast<const u32x4*>(z16 + (int64_t)n * G)[gc];
+      } else {
+        const int r = ic / G, g = ic - r * G;
+        int n = tile0 * 16 + r;
+        n = n < N ? n : N - 1;
+        sv[0] = s16[(int64_t)n * G + g];
+        if (ASYM) zv[0] = z16[(int64_t)n * G + g];
+      }
+      put_sv(sv, zv, idx);
+    }
+    __syncthreads();
+
+    // ---- 4. main loop: group g uses ring slot (g - gb) % kRing.  Columns
+    //      m >= M read row 0: their results are never stored.
+    const int mrow = li < M ? li : 0;
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(lds + (size_t)mrow * K * 2);
+    const float* sxrow = sxl + mrow * G;
+    for (int g0 = gb; g0 < ge; g0 += kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        const int g = g0 + j;
+        if (g < ge) {
+          bf16x8 bx[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bx[i] = as_bf16x8(xrow[g * 16 + lg * 4 + i]);
+          group_math<ASYM, true>(ring[j], bx, sc_base + g * TR * 2, sxrow[g], mask, cmag, yacc);
+        }
+        ring[j] = bload(wres, g + kRing < ge ? woff : 0x80000000u, (g + kRing) * 64);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    // x from the cache: weights and x of the next group prefetched together
+    const bool mvalid = li < M;
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, 0x00020000);
+    const uint32_t xoff = mvalid ? (uint32_t)li * (uint32_t)(K * 2) + lg * 64 : 0x80000000u;
+    u32x4 a0, a1, b0[4], b1[4];
+    auto load_group = [&](int g, u32x4& a, u32x4 (&b)[4]) {
+      const bool ok = g < ge;
+      a = bload(wres, ok ? woff : 0x80000000u, g * 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = bload(xres, ok ? xoff : 0x80000000u, g * 256 + i * 16);
+    };
+    stage_scales<ASYM>(s16, z16, N, G, tile0 * 16, TR, scl);
+    load_group(gb, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    group_step<RT, ASYM>(a1, b1, lds, g + 1, TR, lg, yacc);
+    __syncthreads();
+    for (int g = gb; g < ge; g += 2) {
+      load_group(g + 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        bf16x8 bx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bx[i] = as_bf16x8(pair_activations(b0[i]));
+        group_math<ASYM, false>(a0, bx, sc_base + g * TR * 2, 0.f, mask, cmag, yacc);
+      }
+      if (g + 1 >= ge) break;
+      load_group(g + 2, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        bf16x8 bx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bx[i] = as_bf16x8(pair_activations(b1[i]));
+        group_math<ASYM, false>(a1, bx, sc_base + (g + 1) * TR * 2, 0.f, mask, cmag, yacc);
+      }
+    }
   }
 
-  // ---- sum the KS partial tiles: red[wave][rt][r][lane]
+  // ---- 5. sum the K-slices of each row tile: red[rw][kw][r][lane]
   __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lds[((wave * RT + rt) * 4 + r) * 64 + lane] = yacc[rt][r];
+  for (int r = 0; r < 4; ++r) red[((rw * KS + kw) * 4 + r) * 64 + lane] = yacc[r];
   __syncthreads();
-  // thread t -> (rt, lg, m): 4 consecutive outputs n = n0 + rt*16 + 4*lg + r
-  for (int t = threadIdx.x; t < RT * 64; t += blockDim.x) {
+  // thread t -> (row tile, lane): outputs n = 16*tile + 4*(ln/16) + r, row m = ln%16
+  for (int t = threadIdx.x; t < RW * 64; t += blockDim.x) {
     const int rt = t >> 6, ln = t & 63;
     const int m = ln & 15, lgg = ln >> 4;
-    if (m >= M) continue;
+    const int nb = (tile0 + rt) * 16 + lgg * 4;
+    if (m >= M || nb >= N) continue;
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float acc = 0.f;
-      for (int ww = 0; ww < KS; ++ww) acc += lds[((ww * RT + rt) * 4 + r) * 64 + ln];
+      for (int k2 = 0; k2 < KS; ++k2) acc += red[((rt * KS + k2) * 4 + r) * 64 + ln];
       v[r] = acc;
     }
-    const int nb = n0 + rt * 16 + lgg * 4;
     uint16_t* yp = y + (int64_t)m * N + nb;
     if (nb + 3 < N && (N & 3) == 0) {
       uint2 o;
@@ -213,39 +374,63 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
   }
 }
 
-template <int RT, bool ASYM>
-hipError_t launch_rt(const void* x, int M, const void* w, const void* s, const void* z, int N,
-                     int K, void* y, hipStream_t stream) {
-  constexpr int TR = 16 * RT;
+// Launch shape (measured on MI355X for the Llama-3-8B decode shapes): about
+// 1024 waves in the grid (4 per CU) with 8-16 groups per wave -- KS K-slices
+// per 16-row tile -- and 2 row tiles per workgroup once there are more than
+// 1024 tiles.  Deeper rings and more waves measured slower: the kernels are
+// bound by the latency of their prologue and epilogue, not by the bytes in
+// flight.
+template <bool ASYM, bool XLDS, bool SVEC>
+hipError_t launch_t(const void* x, int M, const void* w, const void* s, const void* z, int N,
+                    int K, void* y, hipStream_t stream) {
   const int G = K / kGroup;
-  const int blocks = (N + TR - 1) / TR;
-  int ks = (2048 + blocks - 1) / blocks;
-  if (ks > 16) ks = 16;
+  const int tiles = (N + 15) / 16;
+  int ks = (1024 + tiles - 1) / tiles;
+  ks = ks < 1 ? 1 : (ks > 16 ? 16 : ks);
+  while (ks < 16 && (G + ks - 1) / ks > 16) ++ks;
   if (ks > G) ks = G;
-  if (ks < 1) ks = 1;
-  const size_t sc_bytes = (size_t)G * TR * 2 * sizeof(float);
-  const size_t red_bytes = (size_t)ks * RT * 4 * 64 * sizeof(float);
-  const size_t lds = sc_bytes > red_bytes ? sc_bytes : red_bytes;
-  hipLaunchKernelGGL((qgemv_kernel<RT, ASYM>), dim3(blocks), dim3(64 * ks), lds, stream,
-                     (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
-                     (const uint16_t*)z, N, K, (uint16_t*)y);
+  int rw = tiles > 1024 ? 2 : 1;
+  if (rw * ks > 16) rw = 1;
+  const size_t x_bytes = XLDS ? (size_t)M * K * 2 + (((size_t)M * G * 4 + 15) & ~(size_t)15) : 0;
+  auto lds_for = [&](int r) {
+    const size_t sc = (size_t)G * r * 16 * 2 * sizeof(float);
+    const size_t red = (size_t)r * ks * 4 * 64 * sizeof(float);
+    return (x_bytes + sc) > red ? (x_bytes + sc) : red;
+  };
+  // keep the staged scales within 32 KiB and the workgroup within 64 KiB of LDS
+  while (rw > 1 && ((size_t)G * rw * 16 * 8 > 32 * 1024 || lds_for(rw) > 64 * 1024)) --rw;
+  const int blocks = (tiles + rw - 1) / rw;
+  hipLaunchKernelGGL((qgemv_kernel<ASYM, XLDS, SVEC>), dim3(blocks), dim3(64 * rw * ks), lds_for(rw),
+                     stream, (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
+                     (const uint16_t*)z, N, K, ks, rw, (uint16_t*)y, 0x000F000Fu,
+                     ASYM ? 0x43004300u : 0x43084308u);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// LDS per workgroup is G * 16*RT * 8 bytes of staged scales; RT = 2 while
-// that stays within 64 KiB (K <= 32768), RT = 1 up to K = 65536.
+// LDS per workgroup: x (M*K*2 bytes when staged, <= 48 KiB) + (s, c) pairs
+// (G * RW * 128 bytes <= 32 KiB for RW > 1; G * 128 bytes = 64 KiB at the
+// API's K limit of 65536 with RW = 1, where x is never staged).
 hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
                         const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
                         hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (K <= 32768) {
-    return asym ? launch_rt<2, true>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
-                : launch_rt<2, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  const int G = k / kGroup;
+  // staged x must leave room for the (s, c) pairs of one row tile in 64 KiB
+  const bool xlds = M * K * 2 <= kXldsMaxBytes &&
+                    M * K * 2 + M * G * 4 + 16 + (int64_t)G * 128 <= 64 * 1024;
+  // 16-byte scale loads need whole 16-byte pieces per row (G % 8 == 0); the
+  // cache path stages scales with the generic loop
+  const bool svec = (G & 7) == 0;
+  if (asym) {
+    if (!xlds) return launch_t<true, false, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+    return svec ? launch_t<true, true, true>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
+                : launch_t<true, true, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
   }
-  return asym ? launch_rt<1, true>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
-              : launch_rt<1, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  if (!xlds) return launch_t<false, false, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  return svec ? launch_t<false, true, true>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
+              : launch_t<false, true, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
 }
 
 }  // namespace qg

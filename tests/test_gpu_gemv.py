@@ -36,6 +36,10 @@ def run_case(m, k, n, asym, seed, outliers=(0.01, 20.0)):
     y = host(qg.qgemv(to_dev(c["x"], dev), codes, scales, zeros, fmt))
     ref = og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, 128)
     finite_checks(y)
+    if y.size < 1024:      # too few outputs for the statistical bar: per-element bound
+        floor = 1e-3 * np.sqrt(np.mean(ref ** 2))
+        assert (np.abs(y - ref) <= 2.0 ** -8 * np.abs(ref) + floor).all()
+        return 0.0
     err = og.rel_fro(y, ref)
     assert err <= TOL, f"rel_fro {err}"
     assert cosine(y, ref) > 0.99
