@@ -46,6 +46,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-detail", action="store_true", help="headline only")
+    p.add_argument("--counters", action="store_true",
+                   help="launch only the dominant kernel (gate+up GEMV, M=1) over rotating "
+                        "weight copies, then a 256 MiB device copy of known size, for "
+                        "rocprofv3 kernel-trace and counter runs; prints one line")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 counter-collection CSVs of --counters runs "
+                        "(FETCH_SIZE, WRITE_SIZE) into profiles/hbm_traffic.json and exit")
     return p.parse_args()
 
 
@@ -263,10 +270,10 @@ def bench_gemv_4096(qg, torch, dev, stream):
 
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(layer):
+def cpu_baseline(layer, min_seconds=10.0, max_passes=12):
     """The oracle as it stands on one layer at M = 1 (quantize the weights,
-    then the fp64 product of the dequantized operands)."""
-    import numpy as np
+    then the fp64 product of the dequantized operands), repeated over whole
+    layers until at least min_seconds of CPU work."""
     from oracle import gemm as og, intquant as oi
     from synthetic import bf16_as_f32
     try:
@@ -276,21 +283,110 @@ def cpu_baseline(layer):
         blas_threads = 1
     t0 = time.perf_counter()
     nbytes = 0
-    for p in layer:
-        q, s, z = oi.quantize_asym(p["w_host"], 128)
-        packed = oi.pack_int4(q)
-        og.w4a16_reference(bf16_as_f32(p["x_host"][:1]), packed, s, z, 128)
-        nbytes += packed.nbytes + s.nbytes + z.nbytes + p["k"] * 2 + p["n"] * 2
+    passes = 0
+    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        for p in layer:
+            q, s, z = oi.quantize_asym(p["w_host"], 128)
+            packed = oi.pack_int4(q)
+            og.w4a16_reference(bf16_as_f32(p["x_host"][:1]), packed, s, z, 128)
+            nbytes += packed.nbytes + s.nbytes + z.nbytes + p["k"] * 2 + p["n"] * 2
+        passes += 1
     t = time.perf_counter() - t0
     return dict(value=nbytes / t / 1e9, unit="GB/s", cores=int(blas_threads), kind="oracle",
-                sample="one Llama-3-8B layer (QKV, O, gate+up, down) at M=1: oracle INT4 "
-                       f"quantization + fp64 dequantized product, {t:.1f} s")
+                sample=f"{passes} passes over one Llama-3-8B layer (QKV, O, gate+up, down) at "
+                       f"M=1: oracle asymmetric INT4 g128 quantization + fp64 product of the "
+                       f"dequantized operands, {t:.1f} s")
+
+
+# ------------------------------------------------------- counter runs
+
+COPY_BYTES = 256 << 20
+DOMINANT_KEY = "qgemv_gate_up_m1"
+DOMINANT_SRC = os.path.join(ROOT, "quantized_gemm_group_amd", "csrc", "qg_gemv.hip")
+
+
+def run_counters(reps=8):
+    """Launches for rocprofv3: the gate+up GEMV (4096 -> 28672, asymmetric
+    INT4 g128, M=1) over weight copies spanning > 2x the last-level cache,
+    then three plain copies of COPY_BYTES (read COPY_BYTES, write COPY_BYTES)
+    whose counter readings calibrate FETCH_SIZE and WRITE_SIZE."""
+    import torch
+    import quantized_gemm_group_amd as qg
+    from synthetic import WORKLOADS, workload_case
+    dev = torch.device("cuda:0")
+    idx = [i for i, p in enumerate(WORKLOADS["llama3_8b_decode"].projections)
+           if p.name == "gate_up"][0]
+    c = workload_case("llama3_8b_decode", idx)
+    codes, s, z = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_asym", 128)
+    per = codes.numel() * 4 + s.numel() * 4
+    ncopies = max(2, -(-2 * MALL_BYTES // per))
+    bufs = [(codes, s, z)] + [(codes.clone(), s.clone(), z.clone()) for _ in range(ncopies - 1)]
+    x = c["x"][:1].to(dev)
+    y = torch.empty((1, c["n"]), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for b in bufs:
+            qg.qgemv(x, b[0], b[1], b[2], "int4_asym", out=y)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters": DOMINANT_KEY, "launches": reps * ncopies,
+                      "bytes_per_launch": proj_bytes(dict(codes=codes, s=s, k=c["k"], n=c["n"]), 1),
+                      "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def write_traffic(fetch_csv, write_csv):
+    """profiles/hbm_traffic.json from the counter CSVs of two --counters runs.
+    Per dispatch, FETCH_SIZE and WRITE_SIZE (KiB) of the GEMV launches are
+    averaged and scaled by COPY_BYTES over the same counter's median reading
+    for the plain copies that follow the GEMV launches."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
+        gemv = [r for r in rows if "qgemv_kernel" in r["Kernel_Name"]]
+        if not gemv:
+            raise SystemExit(f"{path}: no {counter} rows for the GEMV")
+        last = max(int(r["Dispatch_Id"]) for r in gemv)
+        copies = sorted(float(r["Counter_Value"]) for r in rows
+                        if int(r["Dispatch_Id"]) > last and "copyBuffer" in r["Kernel_Name"])
+        if not copies:
+            raise SystemExit(f"{path}: no {counter} rows for the calibration copy")
+        copy_kib = copies[len(copies) // 2]
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        vals = [float(r["Counter_Value"]) for r in gemv]
+        out[counter] = dict(gemv_kib_per_dispatch=sum(vals) / len(vals), dispatches=len(vals),
+                            copy_kib=copy_kib, scale=scale,
+                            bytes_per_launch=sum(vals) / len(vals) * 1024.0 * scale)
+    ent = dict(source_sha256_16=source_hash(DOMINANT_SRC),
+               bytes_per_launch=out["FETCH_SIZE"]["bytes_per_launch"]
+               + out["WRITE_SIZE"]["bytes_per_launch"], counters=out)
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[DOMINANT_KEY] = ent
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps({DOMINANT_KEY: ent}))
 
 
 # ------------------------------------------------------------------- main
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic(*args.traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -301,6 +397,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     qg.load_library()
+    if args.counters:
+        run_counters()
+        return
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(dev)
 
@@ -317,8 +416,7 @@ def main():
 
     dom_t, dom_b = bench_dominant(qg, torch, copies, stream)
     achieved = dom_b / dom_t / 1e9
-    traffic = traffic_from_profile(os.path.join(ROOT, "quantized_gemm_group_amd", "csrc",
-                                                "qg_gemv.hip"), "qgemv_gate_up_m1")
+    traffic = traffic_from_profile(DOMINANT_SRC, DOMINANT_KEY)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "qgemv_kernel<asym, x in LDS> (gate+up 4096->28672, M=1)",
@@ -356,7 +454,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights x bf16 activations, fp32 accumulate",
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights with 1% outlier input channels x20, N(0,1) bf16 activations)",
         "config": {"workload": "llama3_8b_decode: one layer's QKV 4096->6144, O 4096->4096, "
                                "gate+up 4096->28672, down 14336->4096 W4A16 GEMVs, M=1, "
