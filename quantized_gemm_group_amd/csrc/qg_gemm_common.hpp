@@ -41,6 +41,14 @@ __device__ __forceinline__ int swz(int r, int c, int row_bytes) {
   return r * row_bytes + ((c ^ (r & 7)) << 4);
 }
 
+// Two fp32 values rounded to bf16 (nearest even) by the hardware conversion,
+// low half first.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Store 4 consecutive outputs n..n+3 of row m (already scaled) as bf16.
 __device__ __forceinline__ void store_out4(uint16_t* __restrict__ y, int M, int N, int m, int n,
                                            float v0, float v1, float v2, float v3) {

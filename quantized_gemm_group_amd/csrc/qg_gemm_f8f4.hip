@@ -15,16 +15,24 @@
 //
 // Tiling: a 256-thread workgroup owns a 256x256 output tile and its 4 waves a
 // 128x128 quarter each (4x4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4, 256
-// fp32 accumulators per lane), which halves the LDS bytes read per MFMA
-// compared with 64x64 quarters; the 64-deep K of the 32x32 shape keeps the
-// operand registers of one sub-step small.
-// Each k-step stages 128 bytes per row of both operands (128 FP8 or 256 FP4
-// codes) into one of two LDS buffers through registers: the next k-step's
-// global loads are issued first, the current buffer is multiplied, then the
-// registers are written to the other buffer -- one barrier per k-step.
+// fp32 accumulators per lane in the AGPRs).
+//
+// Operand pipeline: a k-step covers 64 bytes of every operand row (64 FP8 or
+// 128 FP4 codes).  Operand tiles go from HBM straight into LDS with buffer
+// loads that write LDS (no VGPR round trip), into a ring of 4 stages, so the
+// loads of k-step k + 4 are issued three k-steps before they are needed.  One
+// barrier per k-step: it certifies that stage k + 1 has landed and that
+// every wave has finished reading stage k, which is then refilled.  During
+// k-step k the matrix cores work on fragments already in registers while the
+// fragments of k-step k + 1 are read from LDS.  The compiler does not track
+// the LDS writes of these loads, so the waits for them are explicit.
+// Within a 64-byte row the four 16-byte chunks are stored XOR-swizzled by
+// bits 2..3 of the row, so the 16 rows read by 16 lanes cover all banks.
 // Workgroups are dispatched round-robin over the 8 XCDs; each XCD is given a
 // contiguous range of tiles walked in column groups, so concurrently running
 // workgroups of one XCD share operand panels in its L2.
+
+#include <type_traits>
 
 #include "qg_gemm_common.hpp"
 #include "qg_internal.hpp"
@@ -32,11 +40,20 @@
 namespace qg {
 namespace {
 
-constexpr int BM = 256, BN = 256, BKB = 128;   // tile rows and bytes per row per k-step
-constexpr int kStageBytes = (BM + BN) * BKB;   // 64 KiB per buffer
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int BM = 256, BN = 256;   // workgroup tile
+constexpr int BK = 64;              // bytes of each operand row per k-step
+constexpr int kStages = 4;
+constexpr int kOpBytes = BM * BK;   // one operand, one stage: 16 KiB
+constexpr int kStageBytes = 2 * kOpBytes;
+// epilogue: each wave's 128 x 128 bf16 quarter with a 272-byte row pitch
+// (8-byte LDS writes of 32 rows spread over the banks, 16-byte aligned reads)
+constexpr int kEpiPitch = 272;
+constexpr int kEpiBytes = 4 * 128 * kEpiPitch;
 
 // Tile of workgroup `bid`: XCD-contiguous ranges (when the tile count divides
-// evenly over the XCDs), then column groups of `group_m` tile rows.
+// evenly over the XCDs), then column groups of 4 tile rows.
 __device__ __forceinline__ void xcd_tile(int bid, int tiles_m, int tiles_n, int* tm, int* tn) {
   constexpr int kXcd = 8;
   const int tiles = tiles_m * tiles_n;
@@ -45,17 +62,46 @@ __device__ __forceinline__ void xcd_tile(int bid, int tiles_m, int tiles_n, int*
   tile_coords(lin, tiles_m, tiles_n, 4, tm, tn);
 }
 
-template <bool MX> struct FragT { typedef i32x8 type; };
-template <> struct FragT<true> { typedef i32x4 type; };
+// Byte offset of 16-byte chunk c of row r in a stage operand tile.
+__device__ __forceinline__ int sw_off(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 4); }
 
-template <bool MX, bool SVEC>
+template <bool MX> struct FragT { typedef i32x8 type; };   // FP8: 32 codes
+template <> struct FragT<true> { typedef i32x4 type; };    // FP4: 32 codes
+
+template <bool MX, bool SALIGN> struct Frags;
+template <bool SALIGN> struct Frags<false, SALIGN> {
+  i32x8 a[4], w[4];
+};
+template <bool SALIGN> struct Frags<true, SALIGN> {
+  i32x4 a[2][4], w[2][4];                 // [sub-step][tile]
+  uint32_t as[4], ws[4];                  // exponent dword of each row
+};
+
+// Wait until at most N vector-memory loads of this wave are outstanding and
+// its LDS operations are done, then meet the other waves.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// SALIGN (MX only): every row's exponents of a k-step are one aligned dword
+// (K a multiple of 128); otherwise its 4 bytes are loaded one by one.
+template <bool MX, bool SALIGN>
 __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
                                                         const void* __restrict__ a_aux, int M,
                                                         const uint8_t* __restrict__ W,
                                                         const void* __restrict__ w_aux, int N,
                                                         int K, uint16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sscale[MX ? 2 * (BM + BN) * 8 : 16];
+  // exponent staging per row and k-step: one dword (SALIGN) or its 4 bytes
+  // loaded one by one, each landing zero-extended in a dword of its own
+  constexpr int kSWords = MX ? (SALIGN ? 1 : 4) : 0;
+  constexpr int kScaleStage = (BM + BN) * 4 * kSWords;
+  constexpr int kRing = kStages * (kStageBytes + kScaleStage);
+  constexpr int kLds = kRing > kEpiBytes ? kRing : kEpiBytes;
+  // loads per wave per k-step: 8 operand blocks of 1 KiB + exponent loads
+  constexpr int kGroup = 8 + 2 * kSWords;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  uint8_t* const sscale = smem + kStages * kStageBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -69,122 +115,109 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int kbytes = MX ? K / 2 : K;           // bytes per operand row
-  const int nk = (kbytes + BKB - 1) / BKB;
+  const int nk = (kbytes + BK - 1) / BK;
+  const int kblocks = K / 32;                  // MX exponents per row
   // rows past M (N) fall outside the buffer's byte range and read as zero
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (int64_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (int64_t)N * kbytes);
 
-  // staging map: chunk q = tid + 256 i (i < 8) of each operand tile sits at
-  // row (tid >> 3) + 32 i, 16-byte chunk tid & 7
-  const int srow = tid >> 3, scol = (tid & 7) * 16;
-  const uint32_t va0 = (uint32_t)(m0 + srow) * kbytes + scol;
-  const uint32_t vw0 = (uint32_t)(n0 + srow) * kbytes + scol;
-  const uint32_t rstep = 32u * (uint32_t)kbytes;
-  // MX scales: thread t stages the 8 block exponents of A row t and W row t
-  const int kblocks = K / 32;
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(a_aux, MX ? (int64_t)M * kblocks : 0);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(w_aux, MX ? (int64_t)N * kblocks : 0);
-  const bool sa_ok = m0 + tid < M, sw_ok = n0 + tid < N;
-
-  u32x4 rar[8], rwr[8];
-  uint32_t sa_lo = 0, sa_hi = 0, sw_lo = 0, sw_hi = 0;
-
-  // global -> registers for k-step kb; a k-step past the end reads zeros
-  auto gload = [&](int kb) {
-    const bool kin = kb * BKB + scol < kbytes;     // K tail: mask whole chunks
+  // Operand loads: wave w fills 1 KiB blocks 4w .. 4w+3 (16 rows each) of
+  // both operand tiles; lane i brings row 16 b + i / 4, chunk (i & 3) ^
+  // ((i >> 4) & 3), which lands at LDS position i of the block.
+  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t voa[4], vow[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      rar[i] = buf_load16(ra, kin ? va0 + i * rstep : kOutOfRange, kb * BKB);
-      rwr[i] = buf_load16(rw, kin ? vw0 + i * rstep : kOutOfRange, kb * BKB);
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (4 * wave + j) + (lane >> 2);
+    voa[j] = (uint32_t)(m0 + r) * kbytes + dchunk * 16;
+    vow[j] = (uint32_t)(n0 + r) * kbytes + dchunk * 16;
+  }
+  // Exponent loads (MX): wave w brings the dwords of tile rows 128 w .. +127
+  // (rows 0..255 of A, then 256..511 of W), 64 rows per load.
+  __amdgpu_buffer_rsrc_t rsx = make_rsrc(a_aux, 0);
+  uint32_t vos[2] = {0, 0};
+  if constexpr (MX) {
+    const bool wop = wave >= 2;
+    rsx = make_rsrc(wop ? w_aux : a_aux, (int64_t)(wop ? N : M) * kblocks);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int grow = (wop ? n0 - 256 : m0) + 128 * wave + 64 * q + lane;
+      vos[q] = (uint32_t)grow * kblocks;
     }
-    if constexpr (MX && SVEC) {
-      // a row's 8 exponents of this k-step are 8 aligned bytes
-      const bool bin = kb * 8 < kblocks;
-      const uint32_t oa = (sa_ok && bin) ? (uint32_t)(m0 + tid) * kblocks + kb * 8 : kOutOfRange;
-      const uint32_t ow = (sw_ok && bin) ? (uint32_t)(n0 + tid) * kblocks + kb * 8 : kOutOfRange;
-      const uint2 a8 = buf_load8(rsa, oa, 0), w8 = buf_load8(rsw, ow, 0);
-      sa_lo = a8.x;
-      sa_hi = a8.y;
-      sw_lo = w8.x;
-      sw_hi = w8.y;
+  }
+
+  // One load of the k-step group: d < 8 -> operand block 4 w + d / 2 of A
+  // (d even) or W (d odd); then exponent loads (MX).
+  auto issue_piece = [&](int k, int d) {
+    const int st = k & (kStages - 1);
+    uint8_t* sA = smem + st * kStageBytes;
+    if (d < 8) {
+      const int j = d >> 1;
+      const bool kin = k * BK + dchunk * 16 < kbytes;   // K tail: whole chunks
+      const int blk = 4 * wave + j;
+      if (d & 1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sA + kOpBytes + blk * 1024), 16,
+                                                 kin ? vow[j] : kOutOfRange, k * BK, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + blk * 1024), 16,
+                                                 kin ? voa[j] : kOutOfRange, k * BK, 0, 0);
     } else if constexpr (MX) {
-      sa_lo = sa_hi = sw_lo = sw_hi = 0;
+      const int j = (d - 8) >> 1, q = (d - 8) & 1;
+      uint8_t* ss = sscale + st * kScaleStage;
+      lds_void* dst = (lds_void*)(ss + (j * 512 + 128 * wave + 64 * q) * 4);
+      const uint32_t vo = k * 4 + j < kblocks ? vos[q] + j : kOutOfRange;
+      if constexpr (SALIGN)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 4, vo, k * 4, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 1, vo, k * 4, 0, 0);
+    }
+  };
+
+  typedef Frags<MX, SALIGN> frags_t;
+  // Fragment reads of k-step k, in the order the MFMAs consume them: entry
+  // e of kOrd is A tile e (e < 4) or W tile e - 4.
+  constexpr int kOrd[8] = {0, 4, 1, 2, 3, 5, 6, 7};
+  constexpr int kReads = MX ? 16 + 8 * kSWords : 16;
+  auto read_piece = [&](int k, frags_t& f, int p) {
+    const int st = k & (kStages - 1);
+    const uint8_t* sA = smem + st * kStageBytes;
+    const uint8_t* sW = sA + kOpBytes;
+    if constexpr (!MX) {
+      // the lane holds bytes 32 * lh .. +32 of the k-step's 64 for its row
+      // (half h = 16 of them); both operands use the same byte -> k map
+      const int e = kOrd[p >> 1], h = p & 1;
+      const bool isw = e >= 4;
+      const int r = (isw ? wn : wm) * 128 + (e & 3) * 32 + l32;
+      const u32x4 v = *reinterpret_cast<const u32x4*>((isw ? sW : sA) + sw_off(r, 2 * lh + h));
+      i32x8& dst = isw ? f.w[e & 3] : f.a[e & 3];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int blk = kb * 8 + j;
-        const bool bin = blk < kblocks;
-        const uint32_t oa = (sa_ok && bin) ? (uint32_t)(m0 + tid) * kblocks + blk : kOutOfRange;
-        const uint32_t ow = (sw_ok && bin) ? (uint32_t)(n0 + tid) * kblocks + blk : kOutOfRange;
-        const uint32_t ba = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsa, oa, 0, 0);
-        const uint32_t bw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsw, ow, 0, 0);
-        if (j < 4) {
-          sa_lo |= ba << (8 * j);
-          sw_lo |= bw << (8 * j);
-        } else {
-          sa_hi |= ba << (8 * (j - 4));
-          sw_hi |= bw << (8 * (j - 4));
-        }
+      for (int i = 0; i < 4; ++i) dst[4 * h + i] = (int)v[i];
+    } else {
+      const uint32_t* ss = reinterpret_cast<const uint32_t*>(sscale + st * kScaleStage);
+      if (p < 8 * kSWords) {
+        // exponents first: row entry p / kSWords (A rows 0..3, W rows 4..7)
+        const int e = p / kSWords, j = p % kSWords;
+        const bool isw = e >= 4;
+        const int r = (isw ? 256 + wn * 128 : wm * 128) + (e & 3) * 32 + l32;
+        uint32_t& dst = isw ? f.ws[e & 3] : f.as[e & 3];
+        const uint32_t v = ss[j * 512 + r];
+        if (j == 0)
+          dst = v;
+        else
+          dst |= v << (8 * j);
+      } else {
+        // sub-step s: the lane holds block 2 s + lh of the k-step (16 bytes)
+        const int q = p - 8 * kSWords;
+        const int sub = q >> 3, e = kOrd[q & 7];
+        const bool isw = e >= 4;
+        const int r = (isw ? wn : wm) * 128 + (e & 3) * 32 + l32;
+        const i32x4 v = *reinterpret_cast<const i32x4*>((isw ? sW : sA) + sw_off(r, 2 * sub + lh));
+        if (isw)
+          f.w[sub][e & 3] = v;
+        else
+          f.a[sub][e & 3] = v;
       }
     }
-  };
-  // registers -> LDS buffer `buf`; exponents are stored per row as the dword
-  // of the even blocks (0, 2, 4, 6) followed by the dword of the odd blocks,
-  // so the lanes of each half of a wave find theirs at one dword
-  auto lstore = [&](int buf) {
-    uint8_t* sA = smem + buf * kStageBytes;
-    uint8_t* sW = sA + BM * BKB;
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = srow + 32 * i;
-      *reinterpret_cast<u32x4*>(sA + swz(row, c, BKB)) = rar[i];
-      *reinterpret_cast<u32x4*>(sW + swz(row, c, BKB)) = rwr[i];
-    }
-    if constexpr (MX) {
-      uint8_t* ss = sscale + buf * (BM + BN) * 8;
-      *reinterpret_cast<uint2*>(ss + tid * 8) =
-          make_uint2(__builtin_amdgcn_perm(sa_hi, sa_lo, 0x06040200u),
-                     __builtin_amdgcn_perm(sa_hi, sa_lo, 0x07050301u));
-      *reinterpret_cast<uint2*>(ss + (BM + tid) * 8) =
-          make_uint2(__builtin_amdgcn_perm(sw_hi, sw_lo, 0x06040200u),
-                     __builtin_amdgcn_perm(sw_hi, sw_lo, 0x07050301u));
-    }
-  };
-
-  // Operand fragments of one sub-step of 64 K.  FP8: the lane holds 32 codes
-  // (bytes 32 * lh .. +32 of the sub-step's 64) of row l32; both operands use
-  // the same byte -> k assignment, so the products pair equal k.  FP4: the
-  // lane holds the 32 codes of block 2 * s + lh of the k-step (16 bytes).
-  typedef typename FragT<MX>::type frag_t;
-  struct Frags {
-    frag_t a[4], w[4];
-  };
-  auto ldfrag = [&](const uint8_t* p, int r, int s) -> frag_t {
-    if constexpr (MX) {
-      return *reinterpret_cast<const frag_t*>(p + swz(r, 2 * s + lh, BKB));
-    } else {
-      const int c0 = 4 * s + 2 * lh;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(p + swz(r, c0, BKB));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(p + swz(r, c0 + 1, BKB));
-      return frag_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-  };
-  auto lfrag = [&](int buf, int s, Frags& f) {
-    const uint8_t* sA = smem + buf * kStageBytes;
-    const uint8_t* sW = sA + BM * BKB;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) f.a[t] = ldfrag(sA, wm * 128 + t * 32 + l32, s);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) f.w[u] = ldfrag(sW, wn * 128 + u * 32 + l32, s);
-  };
-  // the lane's exponent dword (even or odd blocks) of each of its 8 rows
-  auto lscale = [&](int buf, uint32_t* asc, uint32_t* wsc) {
-    const uint32_t* ss = reinterpret_cast<const uint32_t*>(sscale + buf * (BM + BN) * 8);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) asc[t] = ss[(wm * 128 + t * 32 + l32) * 2 + lh];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) wsc[u] = ss[(BM + wn * 128 + u * 32 + l32) * 2 + lh];
   };
 
   // 4 x 4 tiles of 32x32 per wave (128 x 128), D[n][m] in 16 fp32 per lane
@@ -196,145 +229,151 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  uint32_t asc[4] = {0, 0, 0, 0}, wsc[4] = {0, 0, 0, 0};
-  auto mma = [&](const Frags& f, int s, int u0, int u1) {
-#pragma unroll
-    for (int u = u0; u < u1; ++u)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if constexpr (MX) {
-          const i32x8 wf = i32x8{f.w[u][0], f.w[u][1], f.w[u][2], f.w[u][3], 0, 0, 0, 0};
-          const i32x8 af = i32x8{f.a[t][0], f.a[t][1], f.a[t][2], f.a[t][3], 0, 0, 0, 0};
-          acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              wf, af, acc[u][t], 4, 4, 0, (int)__builtin_amdgcn_ubfe(wsc[u], 8 * s, 8), 0,
-              (int)__builtin_amdgcn_ubfe(asc[t], 8 * s, 8));
-        } else {
-          acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[u], f.a[t], acc[u][t],
-                                                                      0, 0, 0, 127, 0, 127);
-        }
-      }
+  // MFMA i of k-step k: FP8 tile (u, t) = (i / 4, i % 4); MX sub-step i / 16
+  constexpr int kMfma = MX ? 32 : 16;
+  auto mma_piece = [&](const frags_t& f, int k, int i) {
+    const int u = (i >> 2) & 3, t = i & 3;
+    if constexpr (!MX) {
+      acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[u], f.a[t], acc[u][t], 0, 0,
+                                                                  0, 127, 0, 127);
+    } else {
+      // blocks past K (last k-step, K not a multiple of 128) have zero codes
+      // and zero exponent bytes; 2^0 is used for them
+      const int sub = i >> 4;
+      const int q = 2 * sub + lh;
+      const bool qok = SALIGN || q < kblocks - 4 * k;
+      const i32x8 wf = i32x8{f.w[sub][u][0], f.w[sub][u][1], f.w[sub][u][2], f.w[sub][u][3], 0, 0, 0, 0};
+      const i32x8 af = i32x8{f.a[sub][t][0], f.a[sub][t][1], f.a[sub][t][2], f.a[sub][t][3], 0, 0, 0, 0};
+      const int ws = qok ? (int)__builtin_amdgcn_ubfe(f.ws[u], 8 * q, 8) : 127;
+      const int as = qok ? (int)__builtin_amdgcn_ubfe(f.as[t], 8 * q, 8) : 127;
+      acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, acc[u][t], 4, 4, 0, ws, 0, as);
+    }
   };
 
-  constexpr int S = MX ? 4 : 2;   // sub-steps of 64 K per k-step
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  Frags cur;
-  lfrag(0, 0, cur);
-  if constexpr (MX) lscale(0, asc, wsc);
-  // One k-step: the next k-step's global loads go out first; sub-step s is
-  // multiplied while sub-step s + 1's fragments are read; during the last
-  // sub-step the staged registers are written to the other buffer, and after
-  // the barrier the first fragments of the next k-step are read while the
-  // last MFMAs run.  The loop body is one basic block (no conditionals), so
-  // the interleave hints below apply to all of it.
-  for (int kb = 0; kb < nk; ++kb) {
-    const int buf = kb & 1;
-    gload(kb + 1);
+  // k-step k: stage k + 1 has landed and stage k (and k - 1) are free.  The
+  // loads go out in pairs of k-steps (k + 3, k + 4) at odd k, interleaved so
+  // that the two 64-byte halves of every 128-byte row segment are requested
+  // back to back and each cache line crosses from L2 once.  Meanwhile the
+  // MFMAs of k-step k (in cur) run, each followed by its share of the
+  // fragment reads of k + 1 (all issued in the first three quarters of the
+  // k-step, so they have landed by the next barrier) and of the loads.
+  // Loads past the last k-step read zeros and keep the wait counts uniform.
+  // At the barrier of an even step the pair (k + 2, k + 3) may still be in
+  // flight; at an odd step the pair holding k + 1 is waited for entirely.
+  constexpr int kReadsPer = (kReads + (3 * kMfma / 4) - 1) / (3 * kMfma / 4);
+  constexpr int kLoadsPer = (2 * kGroup + kMfma - 1) / kMfma;
+  auto step = [&](int k, frags_t& cur, frags_t& nxt, auto odd_t) {
+    constexpr bool odd = decltype(odd_t)::value;
+    wait_vm_barrier<odd ? 0 : 2 * kGroup>();
 #pragma unroll
-    for (int s = 0; s + 1 < S; ++s) {
-      Frags nxt;
-      lfrag(buf, s + 1, nxt);
-      mma(cur, s, 0, 4);
-      cur = nxt;
-    }
-    mma(cur, S - 1, 0, 2);
-    lstore(buf ^ 1);
-    // issue order (interleave hints for the scheduler)
-    if constexpr (!MX) {
-      // sub-step 0: 16 MFMAs, 16 global loads, 16 fragment reads
+    for (int i = 0; i < kMfma; ++i) {
+      mma_piece(cur, k, i);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      for (int r = 0; r < kReadsPer; ++r)
+        if (i * kReadsPer + r < kReads) read_piece(k + 1, nxt, i * kReadsPer + r);
+      if constexpr (odd) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    } else {
-      // sub-step 0: 16 MFMAs, 18 global loads, 8 fragment reads
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 7; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      // sub-steps 1 and 2: 16 MFMAs and 8 fragment reads each
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int r = 0; r < kLoadsPer; ++r) {
+          const int x = i * kLoadsPer + r;     // x / 2 = piece, x % 2 = which k-step
+          if (x < 2 * kGroup) issue_piece(k + 3 + (x & 1), x >> 1);
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // first half of the last sub-step: 8 MFMAs and the LDS stores
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-    }
-    if constexpr (MX) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-    __syncthreads();
-    Frags nxt;
-    lfrag(buf ^ 1, 0, nxt);
-    uint32_t nasc[4], nwsc[4];
-    if constexpr (MX) lscale(buf ^ 1, nasc, nwsc);
-    mma(cur, S - 1, 2, 4);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    cur = nxt;
-    if constexpr (MX) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        asc[i] = nasc[i];
-        wsc[i] = nwsc[i];
-      }
-    }
-  }
+  };
 
-  // epilogue: lane holds D[n = 8*(r/4) + 4*lh + r%4][m = l32] of each 32x32 tile
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int m = m0 + wm * 128 + t * 32 + l32;
-    float sxm = 1.f;
-    if constexpr (!MX) sxm = (m < M) ? reinterpret_cast<const float*>(a_aux)[m] : 0.f;
+  for (int k0 = 0; k0 < 4; k0 += 2)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int x = 0; x < 2 * kGroup; ++x) issue_piece(k0 + (x & 1), x >> 1);
+  wait_vm_barrier<3 * kGroup>();
+  frags_t f0, f1;
+#pragma unroll
+  for (int p = 0; p < kReads; ++p) read_piece(0, f0, p);
+  int k = 0;
+  for (; k + 1 < nk; k += 2) {
+    step(k, f0, f1, std::false_type{});
+    step(k + 1, f1, f0, std::true_type{});
+  }
+  if (k < nk) step(k, f0, f1, std::false_type{});
+  // the trailing loads (zeros) must land before the LDS is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue.  The lane holds D[n = 8 * (r / 4) + 4 * lh + r % 4][m = l32] of
+  // each 32x32 tile.  FP8 rescales by s_x[m] * s_w[n] (all scale loads issued
+  // together, out-of-range channels read as zero); the bf16 results go
+  // through LDS so that each row of the tile leaves in 16-byte pieces that
+  // fill whole cache lines.
+  f32x4 swv[4][4];
+  float sxv[4];
+  if constexpr (!MX) {
+    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(a_aux, (int64_t)M * 4);
+    const __amdgpu_buffer_rsrc_t rsn = make_rsrc(w_aux, (int64_t)N * 4);
+    const bool edge_n = n0 + BN > N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      sxv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rsx, (uint32_t)(m0 + wm * 128 + t * 32 + l32) * 4, 0, 0));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int n = n0 + wn * 128 + u * 32 + 8 * b + 4 * lh;
-        float s[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (!MX) {
+        const uint32_t n = (uint32_t)(n0 + wn * 128 + u * 32 + 8 * b + 4 * lh);
+        if (!edge_n) {
+          swv[u][b] = __builtin_bit_cast(f32x4, buf_load16(rsn, n * 4, 0));
+        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            s[r] = (n + r < N) ? reinterpret_cast<const float*>(w_aux)[n + r] * sxm : 0.f;
+          for (int r = 0; r < 4; ++r)   // one dword each: in or out of range as a whole
+            swv[u][b][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                         rsn, (n + r) * 4, 0, 0));
         }
-        store_out4(Y, M, N, m, n, acc[u][t][4 * b] * s[0], acc[u][t][4 * b + 1] * s[1],
-                   acc[u][t][4 * b + 2] * s[2], acc[u][t][4 * b + 3] * s[3]);
+      }
+  }
+  __syncthreads();   // every wave is done with the operand buffers
+  uint8_t* so = smem + wave * (128 * kEpiPitch);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[u][t][4 * b + r];
+          if constexpr (!MX) v[r] *= sxv[t] * swv[u][b][r];
+        }
+        const int ml = t * 32 + l32, nl = u * 32 + 8 * b + 4 * lh;
+        *reinterpret_cast<uint2*>(so + ml * kEpiPitch + nl * 2) =
+            make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
+      }
+  __syncthreads();
+  // 4 rows per instruction, 16 lanes x 8 outputs per row
+  const int nbase = n0 + wn * 128 + (lane & 15) * 8;
+  const bool full_n = nbase + 7 < N && (N & 7) == 0;
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int ml = 4 * i + (lane >> 4);
+    const int m = m0 + wm * 128 + ml;
+    const u32x4 o = *reinterpret_cast<const u32x4*>(so + ml * kEpiPitch + (lane & 15) * 16);
+    if (m < M) {
+      uint16_t* py = Y + (int64_t)m * N + nbase;
+      if (full_n) {
+        *reinterpret_cast<u32x4*>(py) = o;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (nbase + j < N) py[j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
       }
     }
   }
 }
 
-template <bool MX, bool SVEC>
+template <bool MX, bool SALIGN>
 hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, const void* w_aux,
                   int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SVEC>), dim3(tiles), dim3(256), 0, stream,
+  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN>), dim3(tiles), dim3(256), 0, stream,
                      (const uint8_t*)a, a_aux, (int)M, (const uint8_t*)w, w_aux, (int)N, (int)K,
                      (uint16_t*)y);
   return hipGetLastError();
@@ -345,14 +384,14 @@ hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, co
 hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const void* w,
                            const void* w_scales, int64_t N, int64_t K, void* y,
                            hipStream_t stream) {
-  return launch<false, false>(a, a_scales, M, w, w_scales, N, K, y, stream);
+  return launch<false, true>(a, a_scales, M, w, w_scales, N, K, y, stream);
 }
 
 hipError_t launch_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
                           const void* b_codes, const void* b_e8m0, int64_t N, int64_t K, void* y,
                           hipStream_t stream) {
-  // 8-byte exponent loads when each row's exponents start 8-byte aligned
-  if (K % 256 == 0) return launch<true, true>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
+  // one aligned exponent dword per row and k-step when K is a multiple of 128
+  if (K % 128 == 0) return launch<true, true>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
   return launch<true, false>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
 }
 
