@@ -101,6 +101,11 @@ __device__ __forceinline__ void group_math(const u32x4& a, const bf16x8 (&bx)[4]
   yacc[3] = __builtin_fmaf(p23.z, __builtin_fmaf(-p23.w, sx, acc[3]), yacc[3]);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_g(const void* p, int64_t bytes) {
+  const int64_t lim = bytes > 0x7ffff000LL ? 0x7ffff000LL : bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)lim, 0x00020000);
+}
+
 // Stage the (s, c) pairs of rows [n0, n0 + TR) for all G groups into
 // scl[(g * TR + r) * 2 + {0, 1}]; four elements per thread in flight.
 template <bool ASYM>
@@ -374,6 +379,129 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
   }
 }
 
+// Per-wave GEMV for M <= MM (1 or 4) rows of x and G % 8 == 0.  Workgroup =
+// one 16-row tile, KS waves; wave kw owns groups [NG kw, NG kw + NG).  Each
+// wave issues all of its loads at once and waits only for its own: its slice
+// of x (coalesced 1 KiB loads), the fp16 scales / zero points of its rows
+// (one lane per row, NG of them per load) and its NG weight groups.  The x
+// slice goes through a private LDS region to be pair-permuted; no barrier
+// until the K-slices are summed at the end.
+// The matrix cores take x as the first operand and the codes as the second,
+// so lane (l % 16, l / 16) accumulates D[m = 4 (l / 16) + r][n = l % 16]: its
+// outputs, scale and zero point all belong to weight row n0 + l % 16, and a
+// second MFMA against 1.0 gives the group sums of x in the same layout.
+// LDS: [x slices: KS * MM * NG * 256 bytes][partials: KS * 1 KiB].
+template <bool ASYM, int NG, int MM>
+__global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __restrict__ x, int M,
+                                                          const uint32_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ s16,
+                                                          const uint16_t* __restrict__ z16, int N,
+                                                          int K, int KS,
+                                                          uint16_t* __restrict__ y, uint32_t mask,
+                                                          uint32_t cmag) {
+  extern __shared__ float4 lds4[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds4);
+  constexpr int kXBytes = MM * NG * 256;       // one wave's x slice
+  constexpr int kXLoads = NG / 4;              // 1 KiB loads per row of x
+  const int G = K / kGroup;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int kw = wave;
+  const int n0 = blockIdx.x * 16;
+  const int gb = kw * NG;
+
+  // ---- 1. loads: x slice, scales / zero points, weights (all in flight)
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x, (int64_t)M * K * 2);
+  u32x4 xr[MM * kXLoads];
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q)
+      xr[m * kXLoads + q] = bload(xres, m < M ? (uint32_t)(m * K + gb * 128 + q * 512 + 8 * lane) * 2
+                                              : 0x80000000u, 0);
+  const int n = n0 + li;
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * G * 2);
+  const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
+  const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
+  u32x4 sv, zv = {0u, 0u, 0u, 0u};
+  if constexpr (NG == 8) {
+    sv = bload(sres, soff, 0);
+    if (ASYM) zv = bload(zres, soff, 0);
+  } else {
+    const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
+    sv = u32x4{s2.x, s2.y, 0u, 0u};
+    if (ASYM) {
+      const uint2 z2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0));
+      zv = u32x4{z2.x, z2.y, 0u, 0u};
+    }
+  }
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, (int64_t)N * K / 2);
+  const uint32_t woff = n < N ? (uint32_t)n * (uint32_t)(K / 2) + lg * 16 : 0x80000000u;
+  u32x4 wr[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) wr[j] = bload(wres, woff, (gb + j) * 64);
+
+  // ---- 2. the x slice, pair-permuted, into this wave's LDS region: row m,
+  //      16-byte piece c (covering k = 8 c .. 8 c + 7 of the slice)
+  uint8_t* const xw = lds + wave * kXBytes;
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q)
+      reinterpret_cast<u32x4*>(xw)[m * NG * 16 + q * 64 + lane] =
+          pair_activations(xr[m * kXLoads + q]);
+
+  // ---- 3. groups.  Rows m >= M of the first operand repeat row 0: their
+  //      results are never stored.
+  const int mrow = li < M ? li : 0;
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(xw) + mrow * NG * 16 + lg * 4;
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    bf16x8 bx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bx[i] = as_bf16x8(xrow[j * 16 + i]);
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, sacc = acc0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 cw = as_bf16x8(unpack_word<ASYM>(wr[j][i], mask, cmag));
+      if (i & 1)
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], cw, acc1, 0, 0, 0);
+      else
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], cw, acc0, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], as_bf16x8(ones), sacc, 0, 0, 0);
+    }
+    const uint32_t sb = (sv[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    const float sc = f16_bits_to_f32(sb);
+    float cc = 136.f;
+    if constexpr (ASYM) cc = 128.f + f16_bits_to_f32((zv[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      yacc[r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sacc[r], acc0[r] + acc1[r]), yacc[r]);
+  }
+
+  // ---- 4. sum the K-slices: red[kw][r][lane]; lane (li, lg) of the first
+  //      wave writes y[m = 4 lg + r][n0 + li] for m < M
+  float* red = reinterpret_cast<float*>(lds + KS * kXBytes);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(kw * 4 + r) * 64 + lane] = yacc[r];
+  __syncthreads();
+  if (wave == 0 && n < N) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r;
+      if (m < M) {
+        float v = 0.f;
+        for (int k2 = 0; k2 < KS; ++k2) v += red[(k2 * 4 + r) * 64 + lane];
+        y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
 // Launch shape (measured on MI355X for the Llama-3-8B decode shapes): about
 // 1024 waves in the grid (4 per CU) with 8-16 groups per wave -- KS K-slices
 // per 16-row tile -- and 2 row tiles per workgroup once there are more than
@@ -407,6 +535,53 @@ hipError_t launch_t(const void* x, int M, const void* w, const void* s, const vo
   return hipGetLastError();
 }
 
+template <bool ASYM, int NG, int MM>
+hipError_t launch_wave_t(const void* x, int M, const void* w, const void* s, const void* z, int N,
+                         int K, void* y, hipStream_t stream) {
+  const int G = K / kGroup;
+  const int ks = G / NG;
+  const int tiles = (N + 15) / 16;
+  const size_t lds = (size_t)ks * (MM * NG * 256 + 1024);
+  hipLaunchKernelGGL((qgemv_wave_kernel<ASYM, NG, MM>), dim3(tiles), dim3(64 * ks), lds, stream,
+                     (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
+                     (const uint16_t*)z, N, K, ks, (uint16_t*)y, 0x000F000Fu,
+                     ASYM ? 0x43004300u : 0x43084308u);
+  return hipGetLastError();
+}
+
+// Per-wave kernel for M <= 4 when K splits into slices of NG groups with at
+// most 16 slices (G % NG == 0, G / NG <= 16) and the LDS fits.
+hipError_t launch_wave(bool asym, int ng, const void* x, int M, const void* w, const void* s,
+                       const void* z, int N, int K, void* y, hipStream_t stream) {
+  if (M == 1) {
+    if (ng == 4) return asym ? launch_wave_t<true, 4, 1>(x, M, w, s, z, N, K, y, stream)
+                             : launch_wave_t<false, 4, 1>(x, M, w, s, z, N, K, y, stream);
+    return asym ? launch_wave_t<true, 8, 1>(x, M, w, s, z, N, K, y, stream)
+                : launch_wave_t<false, 8, 1>(x, M, w, s, z, N, K, y, stream);
+  }
+  if (ng == 4) return asym ? launch_wave_t<true, 4, 4>(x, M, w, s, z, N, K, y, stream)
+                           : launch_wave_t<false, 4, 4>(x, M, w, s, z, N, K, y, stream);
+  return asym ? launch_wave_t<true, 8, 4>(x, M, w, s, z, N, K, y, stream)
+              : launch_wave_t<false, 8, 4>(x, M, w, s, z, N, K, y, stream);
+}
+
+// Groups per wave for the per-wave kernel (0: not applicable).
+int pick_wave_ng(int M, int N, int K) {
+  const int G = K / kGroup;
+  if (M > 4 || G % 4 != 0) return 0;
+  const int mm = M == 1 ? 1 : 4;
+  const int tiles = (N + 15) / 16;
+  auto fits = [&](int ng) {
+    const int ks = G / ng;
+    return G % ng == 0 && ks <= 16 && (size_t)ks * (mm * ng * 256 + 1024) <= 160 * 1024;
+  };
+  // about 2048 waves or more: 8 groups per wave when that keeps enough waves
+  if (fits(8) && (int64_t)tiles * (G / 8) >= 2048) return 8;
+  if (fits(4)) return 4;
+  if (fits(8)) return 8;
+  return 0;
+}
+
 }  // namespace
 
 // LDS per workgroup: x (M*K*2 bytes when staged, <= 48 KiB) + (s, c) pairs
@@ -417,6 +592,8 @@ hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
                         hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   const int G = k / kGroup;
+  const int ng = pick_wave_ng(m, n, k);
+  if (ng) return launch_wave(asym, ng, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   // staged x must leave room for the (s, c) pairs of one row tile in 64 KiB
   const bool xlds = M * K * 2 <= kXldsMaxBytes &&
                     M * K * 2 + M * G * 4 + 16 + (int64_t)G * 128 <= 64 * 1024;
