@@ -425,16 +425,26 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * G * 2);
   const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
   const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
-  u32x4 sv, zv = {0u, 0u, 0u, 0u};
-  if constexpr (NG == 8) {
-    sv = bload(sres, soff, 0);
-    if (ASYM) zv = bload(zres, soff, 0);
-  } else {
+  // NG fp16 scales (zero points) of row n: NG / 2 dwords
+  uint32_t sv[NG / 2], zv[NG / 2];
+  if constexpr (NG == 4) {
     const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
-    sv = u32x4{s2.x, s2.y, 0u, 0u};
-    if (ASYM) {
-      const uint2 z2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0));
-      zv = u32x4{z2.x, z2.y, 0u, 0u};
+    sv[0] = s2.x;
+    sv[1] = s2.y;
+    const uint2 z2 = ASYM ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0))
+                          : uint2{0u, 0u};
+    zv[0] = z2.x;
+    zv[1] = z2.y;
+  } else {
+#pragma unroll
+    for (int c = 0; c < NG / 8; ++c) {
+      const u32x4 s4 = bload(sres, soff, 16 * c);
+      const u32x4 z4 = ASYM ? bload(zres, soff, 16 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[4 * c + e] = s4[e];
+        zv[4 * c + e] = z4[e];
+      }
     }
   }
   const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, (int64_t)N * K / 2);
@@ -442,6 +452,7 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
   u32x4 wr[NG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) wr[j] = bload(wres, woff, (gb + j) * 64);
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
 
   // ---- 2. the x slice, pair-permuted, into this wave's LDS region: row m,
   //      16-byte piece c (covering k = 8 c .. 8 c + 7 of the slice)
@@ -478,6 +489,7 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
     const float sc = f16_bits_to_f32(sb);
     float cc = 136.f;
     if constexpr (ASYM) cc = 128.f + f16_bits_to_f32((zv[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+    static_assert(NG % 4 == 0, "groups per wave: a multiple of 4");
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       yacc[r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sacc[r], acc0[r] + acc1[r]), yacc[r]);
@@ -556,6 +568,8 @@ hipError_t launch_wave(bool asym, int ng, const void* x, int M, const void* w, c
   if (M == 1) {
     if (ng == 4) return asym ? launch_wave_t<true, 4, 1>(x, M, w, s, z, N, K, y, stream)
                              : launch_wave_t<false, 4, 1>(x, M, w, s, z, N, K, y, stream);
+    if (ng == 16) return asym ? launch_wave_t<true, 16, 1>(x, M, w, s, z, N, K, y, stream)
+                              : launch_wave_t<false, 16, 1>(x, M, w, s, z, N, K, y, stream);
     return asym ? launch_wave_t<true, 8, 1>(x, M, w, s, z, N, K, y, stream)
                 : launch_wave_t<false, 8, 1>(x, M, w, s, z, N, K, y, stream);
   }
@@ -565,20 +579,21 @@ hipError_t launch_wave(bool asym, int ng, const void* x, int M, const void* w, c
               : launch_wave_t<false, 8, 4>(x, M, w, s, z, N, K, y, stream);
 }
 
-// Groups per wave for the per-wave kernel (0: not applicable).
+// Groups per wave for the per-wave kernel (0: not applicable).  Measured on
+// MI355X for the Llama-3-8B decode shapes: 8 groups per wave, else 4; 16
+// (M = 1 only: 128 VGPRs) when K is too long for 16 slices of 8.
 int pick_wave_ng(int M, int N, int K) {
   const int G = K / kGroup;
   if (M > 4 || G % 4 != 0) return 0;
+  (void)N;
   const int mm = M == 1 ? 1 : 4;
-  const int tiles = (N + 15) / 16;
   auto fits = [&](int ng) {
     const int ks = G / ng;
     return G % ng == 0 && ks <= 16 && (size_t)ks * (mm * ng * 256 + 1024) <= 160 * 1024;
   };
-  // about 2048 waves or more: 8 groups per wave when that keeps enough waves
-  if (fits(8) && (int64_t)tiles * (G / 8) >= 2048) return 8;
-  if (fits(4)) return 4;
   if (fits(8)) return 8;
+  if (fits(4)) return 4;
+  if (M == 1 && fits(16)) return 16;
   return 0;
 }
 
