@@ -352,7 +352,7 @@ def write_traffic(fetch_csv, write_csv):
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
-        gemv = [r for r in rows if "qgemv_kernel" in r["Kernel_Name"]]
+        gemv = [r for r in rows if "qgemv" in r["Kernel_Name"]]
         if not gemv:
             raise SystemExit(f"{path}: no {counter} rows for the GEMV")
         last = max(int(r["Dispatch_Id"]) for r in gemv)
@@ -419,7 +419,7 @@ def main():
     traffic = traffic_from_profile(DOMINANT_SRC, DOMINANT_KEY)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "qgemv_kernel<asym, x in LDS> (gate+up 4096->28672, M=1)",
+                "traffic": traffic, "kernel": "qgemv_wave_kernel<asym, 8 groups/wave, M<=1> (gate+up 4096->28672, M=1)",
                 "us_per_launch": round(dom_t * 1e6, 3), "bytes_per_launch": dom_b}
 
     detail = {}
