@@ -105,7 +105,7 @@ typedef enum {
  *   fmt        QG_INT4_SYM | QG_INT4_ASYM | QG_INT8_SYM | QG_INT8_ASYM |
  *              QG_FP8_E4M3.
  *   src        [rows][K] of src_dtype (QG_BF16 or QG_F32), row-major.
- *   group      > 0, divides K; for INT4 a multiple of 8.
+ *   group      > 0, divides K, and a multiple of 8 (every format).
  *   codes, scales, zeros   outputs in the storage format above; zeros is
  *              required for *_ASYM and must be NULL otherwise.
  * Errors: QG_ERR_GEOMETRY (rows < 1, K < 1, bad group), QG_ERR_FORMAT,
@@ -140,8 +140,9 @@ qg_status qg_dequant(qg_format fmt, const void* codes, const void* scales, const
  *              [N][K/group];  y bf16 [M][N].
  *   group      must be 128 (QG_ERR_UNSUPPORTED otherwise); K % 128 == 0.
  * Errors: QG_ERR_GEOMETRY (M outside 1..16, N < 1, K not a multiple of
- * group), QG_ERR_UNSUPPORTED, QG_ERR_FORMAT, QG_ERR_NULL, QG_ERR_ALIGN,
- * QG_ERR_HIP.
+ * group), QG_ERR_UNSUPPORTED (group != 128, K > 65536, or codes / x padded
+ * by 256 rows larger than 2 GiB - 4 KiB), QG_ERR_FORMAT, QG_ERR_NULL,
+ * QG_ERR_ALIGN, QG_ERR_HIP.
  */
 qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
                    const void* wcodes, const void* wscales, const void* wzeros,
@@ -159,8 +160,10 @@ qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
  *       [L6] section 3 cross terms); per-row scales/zeros (group == K).
  *   y          bf16 [M][N].
  * Errors: QG_ERR_GEOMETRY (M, N, K < 1; K % 128 for W4A16; K % 16 for the
- * 8-bit formats; group), QG_ERR_FORMAT, QG_ERR_UNSUPPORTED, QG_ERR_NULL,
- * QG_ERR_ALIGN, QG_ERR_HIP.
+ * 8-bit formats; group), QG_ERR_FORMAT, QG_ERR_UNSUPPORTED (also when an
+ * operand, padded by 256 rows, exceeds 2 GiB - 4 KiB: the kernels address
+ * each array with 32-bit byte offsets), QG_ERR_NULL, QG_ERR_ALIGN,
+ * QG_ERR_HIP.
  */
 qg_status qg_qgemm(qg_format wfmt, qg_format afmt,
                    const void* a, const void* a_scales, const void* a_zeros, int64_t M,
@@ -185,7 +188,8 @@ qg_status qg_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t
  *   a_codes uint8 [M][K/2], a_e8m0 uint8 [M][K/32]; b_codes uint8 [N][K/2],
  *   b_e8m0 uint8 [N][K/32] (the layout qg_mx_quant writes); y bf16 [M][N].
  * Errors: QG_ERR_GEOMETRY (M, N < 1; K < 32 or K % 32 != 0), QG_ERR_NULL,
- * QG_ERR_ALIGN, QG_ERR_HIP.
+ * QG_ERR_ALIGN, QG_ERR_UNSUPPORTED (an operand, padded by 256 rows, larger
+ * than 2 GiB - 4 KiB), QG_ERR_HIP.
  */
 qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
                      const void* b_codes, const void* b_e8m0, int64_t N, int64_t K,

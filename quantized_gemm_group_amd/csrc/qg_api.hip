@@ -56,6 +56,13 @@ qg_status check_quant_operand(qg_format fmt, int64_t rows, int64_t K, int64_t gr
   return QG_OK;
 }
 
+// The GEMM and GEMV kernels address every operand with 32-bit byte offsets
+// inside a buffer resource of at most 0x7ffff000 bytes; tiles may run up to
+// 256 rows past the end of an operand.
+bool fits_offsets(int64_t rows, int64_t row_bytes) {
+  return (rows + 256) * row_bytes <= 0x7ffff000LL;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +124,8 @@ qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M, const void* wcodes,
   if (st != QG_OK) return st;
   if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemv: only group 128 is implemented");
   if (K > 65536) return fail(QG_ERR_UNSUPPORTED, "qgemv: K above 65536 is not implemented");
+  if (!fits_offsets(N, K / 2) || !fits_offsets(M, K * 2))
+    return fail(QG_ERR_UNSUPPORTED, "qgemv: operand larger than 2 GiB");
   if (!x || !y) return fail(QG_ERR_NULL, "qgemv: x and y are required");
   if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemv: x, y must be 16-byte aligned");
   return from_hip(qg::launch_qgemv(wfmt == QG_INT4_ASYM, x, M, wcodes, wscales, wzeros, N, K, y,
@@ -133,6 +142,12 @@ qg_status qg_qgemm(qg_format wfmt, qg_format afmt, const void* a, const void* a_
   if (!a || !y) return fail(QG_ERR_NULL, "qgemm: a and y are required");
   if (!aligned16(a) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemm: a, y must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
+  {
+    const int64_t wrow = is_int4(wfmt) ? K / 2 : K;
+    const int64_t arow = afmt == QG_BF16_ACT ? K * 2 : K;
+    if (!fits_offsets(N, wrow) || !fits_offsets(M, arow))
+      return fail(QG_ERR_UNSUPPORTED, "qgemm: operand larger than 2 GiB");
+  }
   if (is_int4(wfmt) && afmt == QG_BF16_ACT) {
     qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
     if (st != QG_OK) return st;
@@ -181,6 +196,8 @@ qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M, const v
     return fail(QG_ERR_GEOMETRY, "mx_gemm: M, N >= 1 and K a positive multiple of 32");
   if (M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
     return fail(QG_ERR_GEOMETRY, "mx_gemm: size out of range");
+  if (!fits_offsets(M, K / 2) || !fits_offsets(N, K / 2))
+    return fail(QG_ERR_UNSUPPORTED, "mx_gemm: operand larger than 2 GiB");
   if (!a_codes || !a_e8m0 || !b_codes || !b_e8m0 || !y) return fail(QG_ERR_NULL, "mx_gemm: NULL pointer");
   if (!aligned16(a_codes) || !aligned16(a_e8m0) || !aligned16(b_codes) || !aligned16(b_e8m0) ||
       !aligned16(y))

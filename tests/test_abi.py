@@ -109,3 +109,17 @@ def test_python_raises_value_error_for_geometry(lib):
         _lib.check(_lib.ERR_GEOMETRY)
     with pytest.raises(_lib.QGError):
         _lib.check(_lib.ERR_ALIGN)
+
+
+def test_operands_past_32_bit_offsets_are_rejected(lib):
+    # the kernels address each operand with 32-bit byte offsets (plus up to
+    # 256 rows of tile overhang): larger operands are refused before any launch
+    i4, bf, f8 = _lib.INT4_SYM, _lib.BF16_ACT, _lib.FP8_E4M3
+    big = 1 << 19
+    assert lib.qg_qgemm(f8, f8, A16, A16d, None, big, A16b, A16c, None, 8, 8192, 8192, A16e,
+                        None) == _lib.ERR_UNSUPPORTED
+    assert lib.qg_qgemm(i4, bf, A16, None, None, big, A16b, A16c, None, 8, 8192, 128, A16e,
+                        None) == _lib.ERR_UNSUPPORTED
+    assert lib.qg_mx_gemm(A16, A16b, 8, A16c, A16d, big * 2, 8192, A16e, None) == _lib.ERR_UNSUPPORTED
+    assert lib.qg_qgemv(i4, A16, 1, A16b, A16c, None, 1 << 20, 8192, 128, A16e,
+                        None) == _lib.ERR_UNSUPPORTED
