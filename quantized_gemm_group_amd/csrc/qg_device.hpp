@@ -58,23 +58,6 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
 
 // ------------------------------------------------------------------ FP8 E4M3
 
-// Saturating OCP E4M3FN encoder: nearest value, ties to the even code, |v| >=
-// 448 -> +-448 (0x7E), sign kept (so tiny negatives give 0x80).
-__device__ __forceinline__ uint32_t e4m3_encode_sat(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = __builtin_fabsf(v);
-  if (!(a < 448.f)) return sign | 0x7Eu;
-  if (a < 0.015625f) {                            // below 2^-6: steps of 2^-9
-    return sign | (uint32_t)__builtin_rintf(a * 512.f);   // exact scaling, RNE
-  }
-  uint32_t ua = __float_as_uint(a);
-  ua += 0x7ffffu + ((ua >> 20) & 1u);             // round the 20 dropped bits
-  uint32_t e = (ua >> 23) - 127u + 7u;            // biased E4M3 exponent (1..15)
-  uint32_t code = (e << 3) | ((ua >> 20) & 7u);
-  return sign | code;
-}
-
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;
   float mag = e ? __builtin_ldexpf((float)(8u + m), (int)e - 10)
@@ -83,17 +66,6 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 }
 
 // ------------------------------------------------------------------ FP4 E2M1
-
-// E2M1 magnitudes by code: 0, .5, 1, 1.5, 2, 3, 4, 6.  Nearest value with ties
-// to the even code (midpoints .25 .75 1.25 1.75 2.5 3.5 5), saturating at 6;
-// the sign of v is kept (bit 3).
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  float a = __builtin_fabsf(v);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-               (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
-}
 
 __device__ __forceinline__ float e2m1_decode(uint32_t c) {
   const uint32_t m = c & 7u;

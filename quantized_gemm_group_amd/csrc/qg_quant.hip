@@ -17,9 +17,11 @@
 // order, so the group of vec v is v / T.
 //  - T a power of two <= 64: one lane per vec, the group's T lanes reduce
 //    with xor-shuffles (no LDS, one pass over HBM).
-//  - otherwise (large groups, per-row scales): one 256-thread workgroup per
-//    group, a block reduction, then a second pass that re-reads the group
-//    from cache and writes the codes.
+//  - groups of 64, 128, 256, 512 or 1024 vecs (per-row scales of rows up to
+//    8192 elements): one wave per group, kept in registers, one pass.
+//  - otherwise (other large groups): one 256-thread workgroup per group, a
+//    block reduction, then a second pass that re-reads the group from cache
+//    and writes the codes.
 // Every kernel is HBM bound (4 B read + <= 1 B written per fp32 weight).
 
 #include "qg_device.hpp"
@@ -132,13 +134,21 @@ __device__ __forceinline__ void quantize_store(const float (&v)[8], const Params
       word |= ((uint32_t)(int)q & 0xFu) << (4 * i);
     }
     reinterpret_cast<uint32_t*>(codes)[vec] = word;
+  } else if constexpr (K == K_FP8) {
+    // the gfx950 conversion rounds to nearest even into OCP E4M3; |x / s| <=
+    // 448 (1 + 2^-23) by construction of s, which rounds to 448, so the
+    // saturating and the plain conversion agree
+    uint2 out;
+    out.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / p.s, v[1] / p.s, 0u, false);
+    out.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] / p.s, v[3] / p.s, out.x, true);
+    out.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / p.s, v[5] / p.s, 0u, false);
+    out.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] / p.s, v[7] / p.s, out.y, true);
+    reinterpret_cast<uint2*>(codes)[vec] = out;
   } else {
     uint32_t b[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if constexpr (K == K_FP8) {
-        b[i] = e4m3_encode_sat(v[i] / p.s);
-      } else {
+      {
         constexpr float lo = (K == K_INT8_SYM) ? -127.f : 0.f;
         constexpr float hi = (K == K_INT8_SYM) ? 127.f : 255.f;
         float q = __builtin_rintf(v[i] / p.s) + p.z;
@@ -153,33 +163,82 @@ __device__ __forceinline__ void quantize_store(const float (&v)[8], const Params
   }
 }
 
+// A wave covers 64 * kVpl consecutive vecs: lane l takes vecs l + 64 i, so
+// every load is a coalesced 1 KiB (bf16) piece; all loads go out before the
+// first reduction.
+constexpr int kVpl = 4;
+
 template <int K, bool BF16>
 __global__ __launch_bounds__(kThreads) void quant_wave_kernel(const void* __restrict__ src,
                                                               int64_t total_vecs, int t_log2,
                                                               void* __restrict__ codes,
                                                               void* __restrict__ scales,
                                                               void* __restrict__ zeros) {
-  const int64_t vec = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool valid = vec < total_vecs;
-  float v[8];
-  if (valid) {
-    load_vec<BF16>(src, vec, v);
-  } else {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 64 * kVpl;
+  float v[kVpl][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int i = 0; i < kVpl; ++i) {
+    const int64_t vec = base + 64 * i + lane;
+    if (vec < total_vecs) {
+      load_vec<BF16>(src, vec, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
   }
-  Stats st = stats_of(v);
   const int seg = 1 << t_log2;
-  // segments never straddle valid and invalid lanes (total_vecs % seg == 0)
-  for (int o = 1; o < seg; o <<= 1) {
+#pragma unroll
+  for (int i = 0; i < kVpl; ++i) {
+    const int64_t vec = base + 64 * i + lane;
+    Stats st = stats_of(v[i]);
+    // segments never straddle valid and invalid lanes (total_vecs % seg == 0)
+    for (int o = 1; o < seg; o <<= 1) {
+      st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
+      st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
+      st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+    }
+    if (vec < total_vecs) {
+      const Params p = make_params<K>(st);
+      quantize_store<K>(v[i], p, codes, vec);
+      if ((vec & (seg - 1)) == 0) store_params<K>(p, scales, zeros, vec >> t_log2);
+    }
+  }
+}
+
+// One wave per group of 64 * VPL vecs (per-row scales of rows up to 8192
+// elements): the group stays in registers, the statistics are reduced across
+// the wave, the codes are written from the registers (one pass over HBM).
+template <int K, bool BF16, int VPL>
+__global__ __launch_bounds__(kThreads) void quant_rowwave_kernel(const void* __restrict__ src,
+                                                                 int64_t groups,
+                                                                 void* __restrict__ codes,
+                                                                 void* __restrict__ scales,
+                                                                 void* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (g >= groups) return;
+  const int64_t v0 = g * 64 * VPL;
+  float v[VPL][8];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) load_vec<BF16>(src, v0 + 64 * i + lane, v[i]);
+  Stats st{0.f, __builtin_inff(), -__builtin_inff()};
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const Stats s = stats_of(v[i]);
+    st.amax = __builtin_fmaxf(st.amax, s.amax);
+    st.lo = __builtin_fminf(st.lo, s.lo);
+    st.hi = __builtin_fmaxf(st.hi, s.hi);
+  }
+  for (int o = 1; o < 64; o <<= 1) {
     st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
     st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
     st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
   }
-  if (!valid) return;
   const Params p = make_params<K>(st);
-  quantize_store<K>(v, p, codes, vec);
-  if ((vec & (seg - 1)) == 0) store_params<K>(p, scales, zeros, vec >> t_log2);
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) quantize_store<K>(v[i], p, codes, v0 + 64 * i + lane);
+  if (lane == 0) store_params<K>(p, scales, zeros, g);
 }
 
 template <int K, bool BF16>
@@ -285,36 +344,57 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const void* __restric
 
 // ---------------------------------------------------------------- MXFP4
 
-// One lane per 8 elements, 4 lanes per 32-element block.
+// One lane per 8 elements, 4 lanes per 32-element block; a wave covers 64 *
+// kVpl consecutive vecs (lane l: vecs l + 64 i), all loads issued first.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const void* __restrict__ src,
                                                             int64_t total_vecs,
                                                             void* __restrict__ codes,
                                                             void* __restrict__ e8m0) {
-  const int64_t vec = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool valid = vec < total_vecs;
-  float v[8];
-  if (valid) {
-    load_vec<BF16>(src, vec, v);
-  } else {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 64 * kVpl;
+  float v[kVpl][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  for (int i = 0; i < kVpl; ++i) {
+    const int64_t vec = base + 64 * i + lane;
+    if (vec < total_vecs) {
+      load_vec<BF16>(src, vec, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
   }
-  float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
-  m = __builtin_fmaxf(m, shfl_xor(m, 1));
-  m = __builtin_fmaxf(m, shfl_xor(m, 2));
-  if (!valid) return;
-  const int e = mx_shared_exponent(m);
-  uint32_t word = 0;
+  for (int i = 0; i < kVpl; ++i) {
+    const int64_t vec = base + 64 * i + lane;
+    float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= e2m1_encode(__builtin_ldexpf(v[i], -e)) << (4 * i);
-  reinterpret_cast<uint32_t*>(codes)[vec] = word;
-  if ((vec & 3) == 0) reinterpret_cast<uint8_t*>(e8m0)[vec >> 2] = (uint8_t)(e + 127);
+    for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[i][e]));
+    m = __builtin_fmaxf(m, shfl_xor(m, 1));
+    m = __builtin_fmaxf(m, shfl_xor(m, 2));
+    if (vec < total_vecs) {
+      const int e = mx_shared_exponent(m);
+      // x / 2^e (exact) is within [-6, 6]; the gfx950 conversion (scale 1)
+      // rounds to the nearest E2M1 value, ties to the even code, element 2 j
+      // into the low nibble of byte j
+      float t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = __builtin_ldexpf(v[i][k], -e);
+      uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[0], t[1], 1.0f, 0);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, t[2], t[3], 1.0f, 1);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, t[4], t[5], 1.0f, 2);
+      word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, t[6], t[7], 1.0f, 3);
+      reinterpret_cast<uint32_t*>(codes)[vec] = word;
+      if ((vec & 3) == 0) reinterpret_cast<uint8_t*>(e8m0)[vec >> 2] = (uint8_t)(e + 127);
+    }
+  }
 }
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+// workgroups for kernels whose waves each cover 64 * kVpl vecs
+inline unsigned blocks_for_vpl(int64_t n) {
+  return (unsigned)((n + kThreads * kVpl - 1) / (kThreads * kVpl));
+}
 
 template <int K, bool BF16>
 void launch_quant_t(const void* src, int64_t rows, int64_t Kdim, int64_t group, void* codes,
@@ -324,8 +404,39 @@ void launch_quant_t(const void* src, int64_t rows, int64_t Kdim, int64_t group, 
   if (t_vecs <= 64 && (t_vecs & (t_vecs - 1)) == 0) {
     int t_log2 = 0;
     while ((1LL << t_log2) < t_vecs) ++t_log2;
-    hipLaunchKernelGGL((quant_wave_kernel<K, BF16>), dim3(blocks_for(total)), dim3(kThreads), 0,
-                       stream, src, total, t_log2, codes, scales, zeros);
+    hipLaunchKernelGGL((quant_wave_kernel<K, BF16>), dim3(blocks_for_vpl(total)), dim3(kThreads),
+                       0, stream, src, total, t_log2, codes, scales, zeros);
+  } else if (t_vecs % 64 == 0 && t_vecs <= 64 * 16) {
+    // groups of 512, 1024, 2048, 4096 or 8192 elements: one wave per group
+    // (other multiples of 512 take the workgroup kernel below)
+    const int64_t groups = rows * (Kdim / group);
+    const unsigned blocks = (unsigned)((groups + kThreads / 64 - 1) / (kThreads / 64));
+    switch (t_vecs / 64) {
+      case 1:
+        hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 1>), dim3(blocks), dim3(kThreads), 0,
+                           stream, src, groups, codes, scales, zeros);
+        break;
+      case 2:
+        hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 2>), dim3(blocks), dim3(kThreads), 0,
+                           stream, src, groups, codes, scales, zeros);
+        break;
+      case 4:
+        hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 4>), dim3(blocks), dim3(kThreads), 0,
+                           stream, src, groups, codes, scales, zeros);
+        break;
+      case 8:
+        hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 8>), dim3(blocks), dim3(kThreads), 0,
+                           stream, src, groups, codes, scales, zeros);
+        break;
+      case 16:
+        hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 16>), dim3(blocks), dim3(kThreads), 0,
+                           stream, src, groups, codes, scales, zeros);
+        break;
+      default:
+        hipLaunchKernelGGL((quant_block_kernel<K, BF16>), dim3((unsigned)groups), dim3(kThreads),
+                           0, stream, src, t_vecs, codes, scales, zeros);
+        break;
+    }
   } else {
     const int64_t groups = rows * (Kdim / group);
     hipLaunchKernelGGL((quant_block_kernel<K, BF16>), dim3((unsigned)groups), dim3(kThreads), 0,
@@ -405,10 +516,10 @@ hipError_t launch_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, in
                            void* codes, void* e8m0, hipStream_t stream) {
   const int64_t total = rows * K / 8;
   if (src_dtype == QG_BF16)
-    hipLaunchKernelGGL((mx_quant_kernel<true>), dim3(blocks_for(total)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((mx_quant_kernel<true>), dim3(blocks_for_vpl(total)), dim3(kThreads), 0,
                        stream, src, total, codes, e8m0);
   else
-    hipLaunchKernelGGL((mx_quant_kernel<false>), dim3(blocks_for(total)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((mx_quant_kernel<false>), dim3(blocks_for_vpl(total)), dim3(kThreads), 0,
                        stream, src, total, codes, e8m0);
   return hipGetLastError();
 }

@@ -66,7 +66,7 @@ def _same_bits(a, b):
 
 
 @pytest.mark.parametrize("src", ["f32", "bf16"])
-@pytest.mark.parametrize("group", [8, 32, 128, 1024, 1536])
+@pytest.mark.parametrize("group", [8, 32, 128, 512, 1024, 1536, 3072])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_pack_bit_exact(fmt, group, src):
     dev = device()
@@ -99,6 +99,24 @@ def test_quantize_pack_single_row_and_single_group(fmt):
         assert _same_bits(host(codes), c_o) and _same_bits(host(scales), s_o)
         if z_o is not None:
             assert _same_bits(host(zeros), z_o)
+
+
+@pytest.mark.parametrize("k", [2048, 4096, 8192])
+@pytest.mark.parametrize("fmt", ["fp8_e4m3", "int8_sym", "int8_asym"])
+def test_per_row_quant_one_wave_per_row(fmt, k):
+    # per-row scales (group == K) of rows of 2048..8192 elements: one wave per
+    # row holds it in registers; 13 rows leave a partly filled workgroup
+    dev = device()
+    x = rng_for(k + 7).standard_normal((13, k), dtype=np.float32)
+    x[3] = 0.0                     # all-zero row: scale 1
+    x[5, ::97] *= np.float32(300)  # outliers
+    xt = to_bf16(x)
+    print(f"per-row quant fmt={fmt} K={k}", flush=True)
+    codes, scales, zeros = qg.quantize_pack(to_dev(xt, dev), fmt, k)
+    c_o, s_o, z_o = oracle_quant(fmt, bf16_as_f32(xt), k)
+    assert _same_bits(host(codes), c_o) and _same_bits(host(scales), s_o)
+    if z_o is not None:
+        assert _same_bits(host(zeros), z_o)
 
 
 def test_fp8_dynamic_activation_quant_with_outliers():
@@ -187,3 +205,55 @@ def test_geometry_errors_raise_value_error():
         qg.mx_quant(x[:, :48].contiguous())
     with pytest.raises(ValueError, match="invalid quantization geometry"):
         qg.quantize_pack(x, "int4_sym", 64)
+
+
+def _bf16_patterns_up_to(limit_bits):
+    """Every finite bf16 value with magnitude bits <= limit_bits, both signs."""
+    mags = np.arange(0, limit_bits + 1, dtype=np.uint32)
+    pats = np.concatenate([mags, mags | 0x8000]).astype(np.uint32)
+    return (pats << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("group", [128, 8192])
+def test_fp8_codes_of_every_bf16_value(group):
+    # each group holds 448 so its scale is exactly 1: the codes are the E4M3
+    # encoding of every bf16 value in [-448, 448] (0x43E0 = 448)
+    dev = device()
+    vals = _bf16_patterns_up_to(0x43E0)
+    per = group - 1
+    groups = -(-vals.size // per)
+    groups = -(-groups // (8192 // group)) * (8192 // group)    # whole rows of 8192
+    body = np.zeros(groups * per, np.float32)
+    body[:vals.size] = vals
+    x = np.concatenate([np.full((groups, 1), 448.0, np.float32), body.reshape(groups, per)], axis=1)
+    x = x.reshape(-1, 8192)
+    print(f"fp8 encoding of {vals.size} bf16 values, group {group}", flush=True)
+    codes, scales, _ = qg.quantize_pack(to_dev(to_bf16(x), dev), "fp8_e4m3", group)
+    c_o, s_o, _ = oracle_quant("fp8_e4m3", x, group)
+    assert (host(scales) == 1.0).all()
+    assert _same_bits(host(codes), c_o)
+
+
+def test_mx_codes_at_e2m1_ties():
+    # blocks with max 6 (exponent 0) holding every E2M1 midpoint, its bf16
+    # neighbours and the grid values themselves
+    dev = device()
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    mids = (grid[1:] + grid[:-1]) / 2
+    pts = np.concatenate([grid, mids])
+    b = to_bf16(pts.astype(np.float32)).view(torch.int16).numpy().astype(np.int32)
+    near = np.concatenate([b - 1, b + 1, b])
+    near = near[(near >= 0) & (near <= 0x40C0)].astype(np.uint32)     # 0x40C0 = 6.0
+    vals = (near << 16).view(np.float32)
+    vals = np.concatenate([vals, -vals])
+    per = 31
+    n = -(-vals.size // per) * per
+    body = np.zeros(n, np.float32)
+    body[:vals.size] = vals
+    x = np.concatenate([np.full((n // per, 1), 6.0, np.float32), body.reshape(-1, per)], axis=1)
+    x = x.reshape(1, -1)
+    print(f"mx encoding at {vals.size} tie points", flush=True)
+    c, e = qg.mx_quant(to_dev(to_bf16(x), dev))
+    c_o, e_o = omx.quantize(bf16_as_f32(to_bf16(x)))
+    assert (host(e) == 127).all() and (e_o == 127).all()
+    assert (host(c) == c_o).all()
