@@ -3,20 +3,37 @@
 // 1.3; 《第 6 课：量化源码走读》 section 2: the weights are dequantized inside
 // the GEMM; section 3: the asymmetric zero-point cross term is kept).
 //
-// The matrix cores multiply exact integers: nibbles are unpacked in registers
-// to the bf16 values 128 + u (one and/or per pair, as in the decode GEMV) and
-// fed to v_mfma_f32_16x16x32_bf16 against the bf16 activations, whose pairs
-// (x_j, x_{j+4}) are formed once when X is staged into LDS.  Each group of
-// 128 has its own fp32 accumulator; at the group's end
-//     y += s * (acc_g - c * sum_x),  c = 136 (symmetric) or 128 + z,
-// with sum_x from an extra MFMA against 1.0.  Rounding dequantized weights
-// to bf16 before the matrix cores is avoided on purpose: it would add an
-// error of the same size as the bf16 output rounding itself.
+// The matrix cores multiply exact integers: each nibble u becomes the bf16
+// value 128 + u in registers (a byte permute and one bitop per pair of
+// codes) and meets the bf16 activations in v_mfma_f32_32x32x16_bf16.  With
+// c = 136 for symmetric codes (u = q + 8) and c = 128 + z for asymmetric ones
+//     y = sum_g s_g * (acc_g - c_g * sum_x_g),
+// where acc_g is the group's fp32 accumulator.  The two terms are kept apart:
+//   * s_g * acc_g is one fused multiply-add per output and group;
+//   * the cross term -sum_g (s_g c_g) sum_x_g is a rank-G product that the
+//     fp32 matrix instruction v_mfma_f32_32x32x2_f32 adds straight into the
+//     output accumulators, two groups per instruction, with the row sums
+//     sum_x_g computed from the activation tile in LDS (bf16 dot products
+//     against 1.0, each row's sum split over the four waves sharing it).
+// Rounding dequantized weights to bf16 before the matrix cores is avoided on
+// purpose: its error is of the size of the bf16 output rounding itself.
 //
-// Tiling: 256-thread workgroup, 128 (tokens) x 128 (channels) output tile,
-// 4 waves of 64x64; one k-step = one group of 128.  X is staged as bf16
-// (32 KiB), the codes as packed nibbles (8 KiB) and the tile's (s, c) pairs
-// (1 KiB), through registers so the next group's loads overlap the math.
+// The activations are the first MFMA operand and the codes the second, so
+// lane (l % 32, l / 32) of a 32x32 tile accumulates D[m][n = l % 32]: one
+// weight row per lane, hence one scale per lane and tile.
+//
+// Tiling: 512-thread workgroup (two waves per SIMD, so one wave's unpacking
+// and scaling overlaps the other's matrix instructions), 128 (tokens) x 256
+// (channels) output tile, 8 waves of 64 x 64 (2 x 2 tiles of 32x32); one
+// k-step = one group.  The operands travel HBM -> LDS with buffer loads that
+// write LDS directly, into a ring of 3 stages: X (128 rows x 256 bytes,
+// 16-byte chunks XOR-swizzled by row bits 0..3), the codes (256 rows x 64
+// bytes, swizzled by row bits 2..3) and the group's fp16 scales and zero
+// points (one 2-byte load per row).  The loads of k-step k + 2 go out after
+// the barrier of k-step k; the compiler does not track loads that write LDS,
+// so the waits are explicit.  Within a group, lane half h and MFMA j cover
+// k = 64 h + 8 j .. + 7 in natural order, so a lane's codes of the group are
+// 32 contiguous bytes and its X pieces 128.
 
 #include "qg_gemm_common.hpp"
 #include "qg_internal.hpp"
@@ -24,58 +41,75 @@
 namespace qg {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int XROW = BK * 2;       // bytes of one staged X row (bf16)
-constexpr int WROW = BK / 2;       // bytes of one staged code row
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+constexpr int BM = 128, BN = 256, BK = 128;
+constexpr int kThreads = 512;
+constexpr int XROW = BK * 2;              // bytes of one X row per k-step
+constexpr int WROW = BK / 2;              // bytes of one code row per k-step
+constexpr int kStages = 3;
+constexpr int kXBytes = BM * XROW;        // 32 KiB
+constexpr int kWBytes = BN * WROW;        // 16 KiB
+constexpr int kSBytes = BN * 4;           // one dword per row (zero-extended fp16)
+constexpr int kStageBytes = kXBytes + kWBytes + 2 * kSBytes;
+constexpr int kSumBytes = BM * 16;        // four partial sums per X row
+constexpr int kSumBufs = 3;
+constexpr int kLdsBytes = kStages * kStageBytes + kSumBufs * kSumBytes;
+constexpr int kGroupLoads = 4 + 2 + 1;    // loads per wave per k-step
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+// Codes of one 32-bit word (elements 8 w .. 8 w + 7, element i in bits
+// 4 i .. 4 i + 3) as four bf16 pairs (128 + u_{2d}, 128 + u_{2d+1}): byte d
+// of w and byte d of w >> 4 are moved to the two halves, the mask keeps their
+// low nibbles and the xor adds the bf16 exponent of 128.  For symmetric
+// (two's-complement) codes the xor also flips bit 3 of each nibble, which
+// gives u = q + 8.  Mask and constant arrive as kernel arguments so that the
+// compiler selects one v_bitop3 per pair.
+__device__ __forceinline__ u32x4 unpack_word(uint32_t w, uint32_t mask, uint32_t c) {
+  const uint32_t t = w >> 4;
+  u32x4 r;
+  r[0] = (__builtin_amdgcn_perm(t, w, 0x0C040C00u) & mask) ^ c;
+  r[1] = (__builtin_amdgcn_perm(t, w, 0x0C050C01u) & mask) ^ c;
+  r[2] = (__builtin_amdgcn_perm(t, w, 0x0C060C02u) & mask) ^ c;
+  r[3] = (__builtin_amdgcn_perm(t, w, 0x0C070C03u) & mask) ^ c;
+  return r;
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ u32x4 pair_activations(const u32x4& d) {
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
-  return r;
+// Byte offsets within a stage: X chunk c (16 bytes) of row r, code chunk c of
+// row r.
+__device__ __forceinline__ int x_off(int r, int c) { return r * XROW + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ int w_off(int r, int c) {
+  return kXBytes + r * WROW + ((c ^ ((r >> 2) & 3)) << 4);
 }
 
-// (w >> 4j) & 0x000F000F combined with the bf16 exponent of 128 gives the
-// pair (128 + u_j, 128 + u_{j+4}); for symmetric (two's-complement) codes
-// flipping bit 3 of each nibble first gives u = q + 8.  Both are one xor
-// with a constant after the mask: xor 0x43004300 (asymmetric) or
-// 0x43084308 (symmetric; bit 3 of the masked nibble is flipped too).
-template <bool ASYM>
-__device__ __forceinline__ u32x4 unpack_word(uint32_t w) {
-  constexpr uint32_t C = ASYM ? 0x43004300u : 0x43084308u;
-  u32x4 r;
-  r[0] = (w & 0x000F000Fu) ^ C;
-  r[1] = ((w >> 4) & 0x000F000Fu) ^ C;
-  r[2] = ((w >> 8) & 0x000F000Fu) ^ C;
-  r[3] = ((w >> 12) & 0x000F000Fu) ^ C;
-  return r;
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ int swz_w(int row, int c) {
-  return row * WROW + ((c ^ ((row >> 1) & 3)) << 4);
-}
+template <int V>
+struct Parity {
+  static constexpr int value = V;
+};
 
 template <bool ASYM>
-__global__ __launch_bounds__(256) void gemm_w4a16_kernel(const uint16_t* __restrict__ X, int M,
-                                                         const uint32_t* __restrict__ Wc,
-                                                         const uint16_t* __restrict__ S,
-                                                         const uint16_t* __restrict__ Z, int N,
-                                                         int K, uint16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint8_t sX[BM * XROW];
-  __shared__ __attribute__((aligned(16))) uint8_t sW[BN * WROW];
-  __shared__ __attribute__((aligned(16))) float sSC[BN * 2];
+__global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
+    const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ Wc,
+    const uint16_t* __restrict__ S, const uint16_t* __restrict__ Z, int N, int K,
+    uint16_t* __restrict__ Y, uint32_t mask, uint32_t cmag) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+  uint8_t* const sums = smem + kStages * kStageBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int li = lane & 15, lg = lane >> 4;
+  const int l32 = lane & 31, lh = lane >> 5;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -83,125 +117,196 @@ __global__ __launch_bounds__(256) void gemm_w4a16_kernel(const uint16_t* __restr
   const int m0 = tm * BM, n0 = tn * BN;
   const int G = K / BK;
 
+  // rows past M (N) fall outside the buffers' byte ranges and read as zero
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)M * K * 2);
   const __amdgpu_buffer_rsrc_t rwc = make_rsrc(Wc, (int64_t)N * K / 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (int64_t)N * G * 2);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(Z, ASYM ? (int64_t)N * G * 2 : 0);
 
-  // staging map: X 8 chunks of 16 B per thread (row q>>4, chunk q&15), codes 2
-  uint32_t vx[8];
-  int ox[8];
+  // Load map.  X: wave w brings rows 16 w .. 16 w + 15 in 4 loads of 4 rows x
+  // 256 bytes; lane i -> row 16 w + 4 q + i / 16, LDS position i % 16 holding
+  // chunk (i % 16) ^ (row & 15).  Codes: 2 loads of 16 rows x 64 bytes; lane
+  // i -> row 32 w + 16 q + i / 4, position i % 4 holding chunk
+  // (i % 4) ^ ((row >> 2) & 3).  Scales: waves 0..3 bring s of rows
+  // 64 (w % 4) + i, waves 4..7 the zero points (symmetric: a load of nothing,
+  // which keeps the counts equal).
+  uint32_t vx[4], vw[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int q = tid + 256 * i, row = q >> 4, c = q & 15;
-    ox[i] = row * XROW + ((c ^ (row & 7)) << 4);
-    vx[i] = (m0 + row < M) ? (uint32_t)(m0 + row) * (uint32_t)(K * 2) + c * 16 : kOutOfRange;
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * wave + 4 * q + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    vx[q] = (uint32_t)(m0 + r) * (uint32_t)(K * 2) + c * 16;
   }
-  uint32_t vw[2];
-  int ow[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = tid + 256 * i, row = q >> 2, c = q & 3;
-    ow[i] = swz_w(row, c);
-    vw[i] = (n0 + row < N) ? (uint32_t)(n0 + row) * (uint32_t)(K / 2) + c * 16 : kOutOfRange;
+  for (int q = 0; q < 2; ++q) {
+    const int r = 32 * wave + 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    vw[q] = (uint32_t)(n0 + r) * (uint32_t)(K / 2) + c * 16;
   }
-  const int srow = tid & 127;
-  const bool s_ok = tid < 128 && n0 + srow < N;
+  const int srow = 64 * (wave & 3) + lane;
+  const bool zwave = wave >= 4;
+  const uint32_t vs = (zwave && !ASYM) ? kOutOfRange : (uint32_t)(n0 + srow) * (uint32_t)(G * 2);
 
-  u32x4 rxr[8], rwr[2];
-  float s_reg = 0.f, c_reg = 0.f;
-  auto gload = [&](int g) {
+  // Loads of group g into stage g % 3.  Past the last group the last group is
+  // loaded again (into a stage nobody reads), so every k-step issues the same
+  // number of loads and the wait counts stay uniform.
+  auto issue = [&](int g) {
+    uint8_t* st = smem + (g % kStages) * kStageBytes;
+    const int gl = g < G ? g : G - 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rxr[i] = buf_load16(rx, vx[i], g * XROW);
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + (16 * wave + 4 * q) * XROW), 16,
+                                               vx[q], gl * XROW, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) rwr[i] = buf_load16(rwc, vw[i], g * WROW);
-    if (s_ok) {
-      const int64_t idx = (int64_t)(n0 + srow) * G + g;
-      s_reg = f16_bits_to_f32(S[idx]);
-      c_reg = ASYM ? 128.f + f16_bits_to_f32(Z[idx]) : 136.f;
-    } else {
-      s_reg = 0.f;
-      c_reg = 0.f;
+    for (int q = 0; q < 2; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rwc, (lds_void*)(st + kXBytes + (32 * wave + 16 * q) * WROW), 16, vw[q], gl * WROW, 0, 0);
+    lds_void* sd = (lds_void*)(st + kXBytes + kWBytes + (zwave ? kSBytes : 0) + 256 * (wave & 3));
+    if (zwave)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, sd, 2, vs, gl * 2, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, sd, 2, vs, gl * 2, 0, 0);
+  };
+
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                         0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 yacc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) yacc[mt][nt] = zero16;
+  // s_g * c_g of this lane's two channels for the last two groups, by parity
+  float scp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+
+  // Cross term of groups g0 (even) and g0 + 1: lane half h supplies group
+  // g0 + h (sum_x of the lane's row as the first operand, -(s c) of its
+  // channel as the second); without `pair` group g0 + 1 does not exist.
+  auto cross = [&](int g0, bool pair) {
+    const uint8_t* sb = sums + ((g0 + lh) % kSumBufs) * kSumBytes;
+    float sx[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const u32x4 p = *reinterpret_cast<const u32x4*>(sb + (64 * wm + 32 * mt + l32) * 16);
+      sx[mt] = (__uint_as_float(p[0]) + __uint_as_float(p[1])) +
+               (__uint_as_float(p[2]) + __uint_as_float(p[3]));
+      if (!pair && lh) sx[mt] = 0.f;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float b = -(lh ? scp[1][nt] : scp[0][nt]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        yacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(sx[mt], b, yacc[mt][nt], 0, 0, 0);
     }
   };
-  auto lstore = [&]() {
+
+  // One k-step over group g (P = g % 2).
+  auto step = [&](int g, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    // group g has landed for every wave; stage (g - 1) % 3 is free and the
+    // row sums of the groups before g are in LDS
+    wait_vm_barrier<kGroupLoads>();
+    issue(g + 2);
+    const uint8_t* st = smem + (g % kStages) * kStageBytes;
+    if (P == 0 && g >= 2) cross(g - 2, true);
+
+    // this wave's share of the row sums of group g: the rows of m-tile
+    // wn % 2, k = 64 h + 32 (wn / 2) .. + 31
+    {
+      const int mt = wn & 1, jq = wn >> 1;
+      const int r = 64 * wm + 32 * mt + l32;
+      float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sX + ox[i]) = pair_activations(rxr[i]);
+      for (int h = 0; h < 4; ++h) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + x_off(r, 8 * lh + 4 * jq + h));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(sW + ow[i]) = rwr[i];
-    if (tid < 128) *reinterpret_cast<float2*>(sSC + 2 * srow) = make_float2(s_reg, c_reg);
+        for (int d = 0; d < 4; ++d) {
+          // (a bit cast of a vector element itself would read element 0)
+          const uint32_t e = v[d];
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e), ones2, ps, false);
+        }
+      }
+      *reinterpret_cast<float*>(sums + (g % kSumBufs) * kSumBytes + r * 16 + (2 * jq + lh) * 4) = ps;
+    }
+
+    // codes: 32 contiguous bytes of the lane's row (words 8 lh .. 8 lh + 7)
+    u32x4 cw[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = wn * 64 + nt * 32 + l32;
+      cw[nt][0] = *reinterpret_cast<const u32x4*>(st + w_off(r, 2 * lh));
+      cw[nt][1] = *reinterpret_cast<const u32x4*>(st + w_off(r, 2 * lh + 1));
+    }
+    float sv[2];
+    const uint32_t* sl = reinterpret_cast<const uint32_t*>(st + kXBytes + kWBytes);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = wn * 64 + nt * 32 + l32;
+      sv[nt] = f16_bits_to_f32((uint16_t)sl[r]);
+      const float c = ASYM ? 128.f + f16_bits_to_f32((uint16_t)sl[BN + r]) : 136.f;
+      scp[P][nt] = sv[nt] * c;
+    }
+
+    f32x16 gacc[2][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16x8 a[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int r = wm * 64 + mt * 32 + l32;
+        a[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + x_off(r, 8 * lh + j)));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const bf16x8 b = as_bf16x8(unpack_word(cw[nt][j >> 2][j & 3], mask, cmag));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          gacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b, j ? gacc[mt][nt] : zero16,
+                                                                 0, 0, 0);
+      }
+    }
+    // y += s * acc: lane (l32, lh) register r holds m = 8 (r / 4) + 4 lh + r % 4
+    // of its m-tile and n = l32 of its n-tile
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          yacc[mt][nt][r] = __builtin_fmaf(sv[nt], gacc[mt][nt][r], yacc[mt][nt][r]);
   };
 
-  f32x4 yacc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) yacc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  issue(1);
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    step(g, Parity<0>{});
+    step(g + 1, Parity<1>{});
+  }
+  if (g < G) step(g, Parity<0>{});
+  // cross terms not yet added: groups (G - 2, G - 1) for even G, G - 1 alone
+  // for odd G; their row sums come from the last k-steps of every wave
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (G & 1)
+    cross(G - 1, false);
+  else
+    cross(G - 2, true);
+  // the trailing loads (a repeat of the last group) must land before the
+  // workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    if (g + 1 < G) gload(g + 1);
-
-    // codes of this wave's 4 channel tiles: 16 B = words 4lg..4lg+3 of the group
-    u32x4 wf[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = wn * 64 + u * 16 + li;
-      wf[u] = *reinterpret_cast<const u32x4*>(sW + swz_w(r, lg));
-    }
-    f32x4 gacc[4][4], sacc[4];
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      bf16x8 bx[4];
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = n0 + wn * 64 + nt * 32 + l32;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = wm * 64 + t * 16 + li;
-        const int c = 4 * lg + kc;
-        bx[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(sX + r * XROW + ((c ^ (r & 7)) << 4)));
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ones), bx[t],
-                                                          kc ? sacc[t] : zero4, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 a = as_bf16x8(unpack_word<ASYM>(wf[u][kc]));
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          gacc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx[t], kc ? gacc[u][t] : zero4,
-                                                               0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
       }
     }
-    // flush: rows n = 4lg + r of channel tile u
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4* p = reinterpret_cast<const float4*>(sSC + 2 * (wn * 64 + u * 16 + 4 * lg));
-      const float4 p01 = p[0], p23 = p[1];
-      const float sv[4] = {p01.x, p01.z, p23.x, p23.z};
-      const float cv[4] = {p01.y, p01.w, p23.y, p23.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          yacc[u][t][r] =
-              __builtin_fmaf(sv[r], __builtin_fmaf(-cv[r], sacc[t][0], gacc[u][t][r]), yacc[u][t][r]);
-    }
-    __syncthreads();
-    if (g + 1 < G) {
-      lstore();
-      __syncthreads();
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int m = m0 + wm * 64 + t * 16 + li;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int n = n0 + wn * 64 + u * 16 + 4 * lg;
-      store_out4(Y, M, N, m, n, yacc[u][t][0], yacc[u][t][1], yacc[u][t][2], yacc[u][t][3]);
-    }
-  }
 }
 
 }  // namespace
@@ -211,15 +316,15 @@ hipError_t launch_gemm_w4a16(bool asym, const void* x, int64_t M, const void* wc
                              void* y, hipStream_t stream) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   if (asym)
-    hipLaunchKernelGGL((gemm_w4a16_kernel<true>), dim3(tiles), dim3(256), 0, stream,
+    hipLaunchKernelGGL((gemm_w4a16_kernel<true>), dim3(tiles), dim3(kThreads), 0, stream,
                        (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
                        (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
-                       (uint16_t*)y);
+                       (uint16_t*)y, 0x000F000Fu, 0x43004300u);
   else
-    hipLaunchKernelGGL((gemm_w4a16_kernel<false>), dim3(tiles), dim3(256), 0, stream,
+    hipLaunchKernelGGL((gemm_w4a16_kernel<false>), dim3(tiles), dim3(kThreads), 0, stream,
                        (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
                        (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
-                       (uint16_t*)y);
+                       (uint16_t*)y, 0x000F000Fu, 0x43084308u);
   return hipGetLastError();
 }
 

@@ -170,7 +170,8 @@ def test_int8_gemm_4096_sampled():
 # --------------------------------------------------------------- W4A16 prefill
 
 @pytest.mark.parametrize("asym", [False, True])
-@pytest.mark.parametrize("m,k,n", [(64, 256, 80), (200, 1024, 136), (1, 128, 16), (300, 2048, 520)])
+@pytest.mark.parametrize("m,k,n", [(64, 256, 80), (200, 1024, 136), (1, 128, 16), (300, 2048, 520),
+                                   (130, 384, 300), (70, 640, 260)])
 def test_w4a16_gemm_small(m, k, n, asym):
     dev = device()
     c = small_case(m, k, n, seed=m + 11 * n, w_outlier=(0.01, 20.0))
