@@ -514,6 +514,218 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
   }
 }
 
+// Codes of one word in natural order: dword d holds the bf16 pair
+// (128 + u_{2d}, 128 + u_{2d+1}), so activations read straight from memory
+// need no permute.  Byte d of w and of w >> 4 go to the two halves (one
+// byte permute), then the same mask / xor as above.
+__device__ __forceinline__ u32x4 unpack_word_nat(uint32_t w, uint32_t mask, uint32_t c) {
+  const uint32_t t = w >> 4;
+  u32x4 r;
+  r[0] = (__builtin_amdgcn_perm(t, w, 0x0C040C00u) & mask) ^ c;
+  r[1] = (__builtin_amdgcn_perm(t, w, 0x0C050C01u) & mask) ^ c;
+  r[2] = (__builtin_amdgcn_perm(t, w, 0x0C060C02u) & mask) ^ c;
+  r[3] = (__builtin_amdgcn_perm(t, w, 0x0C070C03u) & mask) ^ c;
+  return r;
+}
+
+// 4x4 transpose across the four 16-lane rows: row r, register e receives
+// row e, register r (two swaps of lane halves, two of odd / even rows).
+__device__ __forceinline__ u32x4 transpose_rows(const u32x4& v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  u32x4 r;
+  r[0] = c[0];
+  r[1] = c[1];
+  r[2] = d[0];
+  r[3] = d[1];
+  return r;
+}
+
+// Per-wave GEMV for 5 <= M <= 16.  Workgroup = R tiles of 16 output channels
+// and KS waves; wave kw owns groups [NG kw, NG kw + NG).  With all 16 rows
+// of the MFMA in use, every matrix instruction takes its activations straight
+// from memory (served by the caches: x is shared by every workgroup), no LDS
+// staging and no barrier until the K-slices are summed.  Within a group,
+// lane (li, lg) and MFMA i cover k = 32 i + 8 lg .. + 7 for both operands:
+// each activation load reads 64 contiguous bytes of every row (two loads
+// fill a cache line).  The lane's 16-byte code load holds words
+// 4 lg .. 4 lg + 3 of its channel; a transpose across the lane rows turns
+// them into words lg, 4 + lg, 8 + lg, 12 + lg, the ones its MFMAs need.
+// D groups are kept in flight in registers.
+// The matrix cores take x as the first operand: lane (li, lg) accumulates
+// D[m = 4 lg + r][n = li] of each channel tile, and an MFMA against 1.0
+// gives the group sums of x in the same layout.
+// LDS: partial sums [KS][R][4][64] floats.
+template <bool ASYM, int NG, int R>
+__global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restrict__ x, int M,
+                                                         const uint32_t* __restrict__ w,
+                                                         const uint16_t* __restrict__ s16,
+                                                         const uint16_t* __restrict__ z16, int N,
+                                                         int K, int KS,
+                                                         uint16_t* __restrict__ y, uint32_t mask,
+                                                         uint32_t cmag) {
+  extern __shared__ float4 lds4[];
+  float* red = reinterpret_cast<float*>(lds4);
+  constexpr int D = NG == 16 ? 2 : (R == 1 ? 4 : 3);   // groups in flight
+  static_assert(NG % 4 == 0, "groups per wave: a multiple of 4");
+  const int G = K / kGroup;
+  const int lane = threadIdx.x & 63;
+  const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16 * R;
+  const int gb = kw * NG;
+
+  // rows m >= M and channels n >= N read as zero (out of the buffer ranges)
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x, (int64_t)M * K * 2);
+  const uint32_t xoff = li < M ? (uint32_t)(li * K + gb * kGroup + 8 * lg) * 2 : 0x80000000u;
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, (int64_t)N * K / 2);
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * G * 2);
+  const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
+  uint32_t woff[R];
+  uint32_t sv[R][NG / 2], zv[R][NG / 2];
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const int n = n0 + 16 * t + li;
+    woff[t] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(gb * 64 + lg * 16) : 0x80000000u;
+    const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
+    if constexpr (NG == 4) {
+      const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
+      const uint2 z2 = ASYM ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0))
+                            : uint2{0u, 0u};
+      sv[t][0] = s2.x;
+      sv[t][1] = s2.y;
+      zv[t][0] = z2.x;
+      zv[t][1] = z2.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < NG / 8; ++c) {
+        const u32x4 s4 = bload(sres, soff, 16 * c);
+        const u32x4 z4 = ASYM ? bload(zres, soff, 16 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[t][4 * c + e] = s4[e];
+          zv[t][4 * c + e] = z4[e];
+        }
+      }
+    }
+  }
+
+  u32x4 xr[D][4], wr[D][R];
+  auto load = [&](int j, int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[slot][i] = bload(xres, xoff, j * 256 + i * 64);
+#pragma unroll
+    for (int t = 0; t < R; ++t) wr[slot][t] = bload(wres, woff[t], j * 64);
+  };
+#pragma unroll
+  for (int j = 0; j < D; ++j) load(j, j);
+
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  float yacc[R][4];
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yacc[t][r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int slot = j % D;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    u32x4 wt[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) wt[t] = transpose_rows(wr[slot][t]);
+    f32x4 acc[R][2];
+#pragma unroll
+    for (int t = 0; t < R; ++t) acc[t][0] = acc[t][1] = sacc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 a = as_bf16x8(xr[slot][i]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(ones), sacc, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+        acc[t][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, as_bf16x8(unpack_word_nat(wt[t][i], mask, cmag)), acc[t][i & 1], 0, 0, 0);
+    }
+    if (j + D < NG) load(j + D, slot);
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const float sc = f16_bits_to_f32((sv[t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      float cc = 136.f;
+      if constexpr (ASYM) cc = 128.f + f16_bits_to_f32((zv[t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        yacc[t][r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sacc[r], acc[t][0][r] + acc[t][1][r]),
+                                    yacc[t][r]);
+    }
+  }
+
+  // sum the K-slices: red[kw][t][r][lane]; the first wave writes
+  // y[m = 4 lg + r][n0 + 16 t + li] for m < M, n < N
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((kw * R + t) * 4 + r) * 64 + lane] = yacc[t][r];
+  __syncthreads();
+  if (kw == 0) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int n = n0 + 16 * t + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * lg + r;
+        if (m < M && n < N) {
+          float v = 0.f;
+          for (int k2 = 0; k2 < KS; ++k2) v += red[((k2 * R + t) * 4 + r) * 64 + lane];
+          y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+template <bool ASYM, int NG, int R>
+hipError_t launch_m16_t(const void* x, int M, const void* w, const void* s, const void* z, int N,
+                        int K, void* y, hipStream_t stream) {
+  const int G = K / kGroup;
+  const int ks = G / NG;
+  const int blocks = (N + 16 * R - 1) / (16 * R);
+  const size_t lds = (size_t)ks * R * 4 * 64 * sizeof(float);
+  hipLaunchKernelGGL((qgemv_m16_kernel<ASYM, NG, R>), dim3(blocks), dim3(64 * ks), lds, stream,
+                     (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
+                     (const uint16_t*)z, N, K, ks, (uint16_t*)y, 0x000F000Fu,
+                     ASYM ? 0x43004300u : 0x43084308u);
+  return hipGetLastError();
+}
+
+// Groups per wave for the M <= 16 kernel (0: not applicable): 8 when K
+// splits into at most 16 slices of 8 groups, else 4, else 16.
+int pick_m16_ng(int K) {
+  const int G = K / kGroup;
+  if (G % 8 == 0 && G / 8 <= 16) return 8;
+  if (G % 4 == 0 && G / 4 <= 16) return 4;
+  if (G % 16 == 0 && G / 16 <= 16) return 16;
+  return 0;
+}
+
+hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, const void* s,
+                      const void* z, int N, int K, void* y, hipStream_t stream) {
+  // two channel tiles per wave (4 groups each, to stay within 128 VGPRs)
+  // once there are enough tiles for the chip
+  const int G = K / kGroup;
+  if (N >= 16384 && G % 4 == 0 && G / 4 <= 16)
+    return asym ? launch_m16_t<true, 4, 2>(x, M, w, s, z, N, K, y, stream)
+                : launch_m16_t<false, 4, 2>(x, M, w, s, z, N, K, y, stream);
+  if (asym) {
+    if (ng == 4) return launch_m16_t<true, 4, 1>(x, M, w, s, z, N, K, y, stream);
+    if (ng == 16) return launch_m16_t<true, 16, 1>(x, M, w, s, z, N, K, y, stream);
+    return launch_m16_t<true, 8, 1>(x, M, w, s, z, N, K, y, stream);
+  }
+  if (ng == 4) return launch_m16_t<false, 4, 1>(x, M, w, s, z, N, K, y, stream);
+  if (ng == 16) return launch_m16_t<false, 16, 1>(x, M, w, s, z, N, K, y, stream);
+  return launch_m16_t<false, 8, 1>(x, M, w, s, z, N, K, y, stream);
+}
+
 // Launch shape (measured on MI355X for the Llama-3-8B decode shapes): about
 // 1024 waves in the grid (4 per CU) with 8-16 groups per wave -- KS K-slices
 // per 16-row tile -- and 2 row tiles per workgroup once there are more than
@@ -609,6 +821,10 @@ hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
   const int G = k / kGroup;
   const int ng = pick_wave_ng(m, n, k);
   if (ng) return launch_wave(asym, ng, x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  if (m > 4) {
+    const int ng16 = pick_m16_ng(k);
+    if (ng16) return launch_m16(asym, ng16, x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  }
   // staged x must leave room for the (s, c) pairs of one row tile in 64 KiB
   const bool xlds = M * K * 2 <= kXldsMaxBytes &&
                     M * K * 2 + M * G * 4 + 16 + (int64_t)G * 128 <= 64 * 1024;

@@ -51,7 +51,10 @@ def run_case(m, k, n, asym, seed, outliers=(0.01, 20.0)):
                                    (16, 2048, 333), (7, 14336, 96), (16, 640, 48),
                                    # per-wave kernel: 16 groups per wave (K = 18432), 14 K-slices,
                                    # 4 groups per wave (G = 4, 12), M = 2 in the 4-row layout
-                                   (1, 18432, 40), (2, 14336, 70), (4, 512, 33), (1, 1536, 17)])
+                                   (1, 18432, 40), (2, 14336, 70), (4, 512, 33), (1, 1536, 17),
+                                   # 5..16 rows: 16 groups per wave (G = 144), two channel tiles
+                                   # per wave with a ragged last tile, 4 groups per wave (G = 12)
+                                   (9, 18432, 50), (12, 1024, 16400), (5, 1536, 77)])
 def test_qgemv_small(m, k, n, asym):
     run_case(m, k, n, asym, seed=m * 1000 + n)
 
