@@ -45,12 +45,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BM = 256, BN = 256;   // workgroup tile
 constexpr int BK = 64;              // bytes of each operand row per k-step
 constexpr int kStages = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kOpBytes = BM * BK;   // one operand, one stage: 16 KiB
 constexpr int kStageBytes = 2 * kOpBytes;
-// epilogue: each wave's 128 x 128 bf16 quarter with a 272-byte row pitch
+// epilogue: each wave's 128 (m) x 64 (n) bf16 piece with a 144-byte row pitch
 // (8-byte LDS writes of 32 rows spread over the banks, 16-byte aligned reads)
-constexpr int kEpiPitch = 272;
-constexpr int kEpiBytes = 4 * 128 * kEpiPitch;
+constexpr int kEpiPitch = 144;
+constexpr int kEpiBytes = kWaves * 128 * kEpiPitch;
 
 // Tile of workgroup `bid`: XCD-contiguous ranges (when the tile count divides
 // evenly over the XCDs), then column groups of 4 tile rows.
@@ -65,16 +67,13 @@ __device__ __forceinline__ void xcd_tile(int bid, int tiles_m, int tiles_n, int*
 // Byte offset of 16-byte chunk c of row r in a stage operand tile.
 __device__ __forceinline__ int sw_off(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 4); }
 
-template <bool MX> struct FragT { typedef i32x8 type; };   // FP8: 32 codes
-template <> struct FragT<true> { typedef i32x4 type; };    // FP4: 32 codes
-
 template <bool MX, bool SALIGN> struct Frags;
 template <bool SALIGN> struct Frags<false, SALIGN> {
-  i32x8 a[4], w[4];
+  i32x8 a[4], w[2];                       // [A tile], [W tile]: 32 codes each
 };
 template <bool SALIGN> struct Frags<true, SALIGN> {
-  i32x4 a[2][4], w[2][4];                 // [sub-step][tile]
-  uint32_t as[4], ws[4];                  // exponent dword of each row
+  i32x4 a[2][4], w[2][2];                 // [sub-step][tile]: 32 codes each
+  uint32_t as[4], ws[2];                  // exponent dword of each row, >> 8 lh
 };
 
 // Wait until at most N vector-memory loads of this wave are outstanding and
@@ -87,26 +86,26 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // SALIGN (MX only): every row's exponents of a k-step are one aligned dword
 // (K a multiple of 128); otherwise its 4 bytes are loaded one by one.
 template <bool MX, bool SALIGN>
-__global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
-                                                        const void* __restrict__ a_aux, int M,
-                                                        const uint8_t* __restrict__ W,
-                                                        const void* __restrict__ w_aux, int N,
-                                                        int K, uint16_t* __restrict__ Y) {
+__global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
+                                                             const void* __restrict__ a_aux, int M,
+                                                             const uint8_t* __restrict__ W,
+                                                             const void* __restrict__ w_aux, int N,
+                                                             int K, uint16_t* __restrict__ Y) {
   // exponent staging per row and k-step: one dword (SALIGN) or its 4 bytes
   // loaded one by one, each landing zero-extended in a dword of its own
   constexpr int kSWords = MX ? (SALIGN ? 1 : 4) : 0;
   constexpr int kScaleStage = (BM + BN) * 4 * kSWords;
   constexpr int kRing = kStages * (kStageBytes + kScaleStage);
   constexpr int kLds = kRing > kEpiBytes ? kRing : kEpiBytes;
-  // loads per wave per k-step: 8 operand blocks of 1 KiB + exponent loads
-  constexpr int kGroup = 8 + 2 * kSWords;
+  // loads per wave per k-step: 4 operand blocks of 1 KiB + exponent loads
+  constexpr int kGroup = 4 + kSWords;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   uint8_t* const sscale = smem + kStages * kStageBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;     // A rows 128 wm.., W rows 64 wn..
   const int l32 = lane & 31, lh = lane >> 5;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -121,40 +120,37 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (int64_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (int64_t)N * kbytes);
 
-  // Operand loads: wave w fills 1 KiB blocks 4w .. 4w+3 (16 rows each) of
-  // both operand tiles; lane i brings row 16 b + i / 4, chunk (i & 3) ^
+  // Operand loads: wave w fills 1 KiB blocks 2w, 2w+1 (16 rows each) of both
+  // operand tiles; lane i brings row 16 b + i / 4, chunk (i & 3) ^
   // ((i >> 4) & 3), which lands at LDS position i of the block.
   const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t voa[4], vow[4];
+  uint32_t voa[2], vow[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * (4 * wave + j) + (lane >> 2);
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * wave + j) + (lane >> 2);
     voa[j] = (uint32_t)(m0 + r) * kbytes + dchunk * 16;
     vow[j] = (uint32_t)(n0 + r) * kbytes + dchunk * 16;
   }
-  // Exponent loads (MX): wave w brings the dwords of tile rows 128 w .. +127
-  // (rows 0..255 of A, then 256..511 of W), 64 rows per load.
+  // Exponent loads (MX): wave w brings the dwords of tile rows 64 w .. +63
+  // (rows 0..255 of A, then 256..511 of W), one load per k-step and byte.
   __amdgpu_buffer_rsrc_t rsx = make_rsrc(a_aux, 0);
-  uint32_t vos[2] = {0, 0};
+  uint32_t vos = 0;
   if constexpr (MX) {
-    const bool wop = wave >= 2;
+    const bool wop = wave >= 4;
     rsx = make_rsrc(wop ? w_aux : a_aux, (int64_t)(wop ? N : M) * kblocks);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int grow = (wop ? n0 - 256 : m0) + 128 * wave + 64 * q + lane;
-      vos[q] = (uint32_t)grow * kblocks;
-    }
+    const int grow = (wop ? n0 : m0) + 64 * (wave & 3) + lane;
+    vos = (uint32_t)grow * kblocks;
   }
 
-  // One load of the k-step group: d < 8 -> operand block 4 w + d / 2 of A
+  // One load of the k-step group: d < 4 -> operand block 2 w + d / 2 of A
   // (d even) or W (d odd); then exponent loads (MX).
   auto issue_piece = [&](int k, int d) {
     const int st = k & (kStages - 1);
     uint8_t* sA = smem + st * kStageBytes;
-    if (d < 8) {
+    if (d < 4) {
       const int j = d >> 1;
       const bool kin = k * BK + dchunk * 16 < kbytes;   // K tail: whole chunks
-      const int blk = 4 * wave + j;
+      const int blk = 2 * wave + j;
       if (d & 1)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sA + kOpBytes + blk * 1024), 16,
                                                  kin ? vow[j] : kOutOfRange, k * BK, 0, 0);
@@ -162,10 +158,10 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + blk * 1024), 16,
                                                  kin ? voa[j] : kOutOfRange, k * BK, 0, 0);
     } else if constexpr (MX) {
-      const int j = (d - 8) >> 1, q = (d - 8) & 1;
+      const int j = d - 4;
       uint8_t* ss = sscale + st * kScaleStage;
-      lds_void* dst = (lds_void*)(ss + (j * 512 + 128 * wave + 64 * q) * 4);
-      const uint32_t vo = k * 4 + j < kblocks ? vos[q] + j : kOutOfRange;
+      lds_void* dst = (lds_void*)(ss + (j * 512 + 64 * wave) * 4);
+      const uint32_t vo = k * 4 + j < kblocks ? vos + j : kOutOfRange;
       if constexpr (SALIGN)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 4, vo, k * 4, 0, 0);
       else
@@ -176,8 +172,8 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
   typedef Frags<MX, SALIGN> frags_t;
   // Fragment reads of k-step k, in the order the MFMAs consume them: entry
   // e of kOrd is A tile e (e < 4) or W tile e - 4.
-  constexpr int kOrd[8] = {0, 4, 1, 2, 3, 5, 6, 7};
-  constexpr int kReads = MX ? 16 + 8 * kSWords : 16;
+  constexpr int kOrd[6] = {4, 0, 1, 2, 3, 5};
+  constexpr int kReads = MX ? 12 + 6 * kSWords : 12;
   auto read_piece = [&](int k, frags_t& f, int p) {
     const int st = k & (kStages - 1);
     const uint8_t* sA = smem + st * kStageBytes;
@@ -187,66 +183,71 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
       // (half h = 16 of them); both operands use the same byte -> k map
       const int e = kOrd[p >> 1], h = p & 1;
       const bool isw = e >= 4;
-      const int r = (isw ? wn : wm) * 128 + (e & 3) * 32 + l32;
+      const int r = isw ? wn * 64 + (e - 4) * 32 + l32 : wm * 128 + e * 32 + l32;
       const u32x4 v = *reinterpret_cast<const u32x4*>((isw ? sW : sA) + sw_off(r, 2 * lh + h));
-      i32x8& dst = isw ? f.w[e & 3] : f.a[e & 3];
+      i32x8& dst = isw ? f.w[e - 4] : f.a[e];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[4 * h + i] = (int)v[i];
     } else {
       const uint32_t* ss = reinterpret_cast<const uint32_t*>(sscale + st * kScaleStage);
-      if (p < 8 * kSWords) {
-        // exponents first: row entry p / kSWords (A rows 0..3, W rows 4..7)
+      if (p < 6 * kSWords) {
+        // exponents first: row entry p / kSWords (A rows 0..3, W rows 4..5)
         const int e = p / kSWords, j = p % kSWords;
         const bool isw = e >= 4;
-        const int r = (isw ? 256 + wn * 128 : wm * 128) + (e & 3) * 32 + l32;
-        uint32_t& dst = isw ? f.ws[e & 3] : f.as[e & 3];
+        const int r = isw ? 256 + wn * 64 + (e - 4) * 32 + l32 : wm * 128 + e * 32 + l32;
+        uint32_t& dst = isw ? f.ws[e - 4] : f.as[e];
         const uint32_t v = ss[j * 512 + r];
         if (j == 0)
           dst = v;
         else
           dst |= v << (8 * j);
+        // the lane's block in sub-step s is byte 2 s + lh: shifted to byte 2 s
+        if (j == kSWords - 1) dst >>= 8 * lh;
       } else {
         // sub-step s: the lane holds block 2 s + lh of the k-step (16 bytes)
-        const int q = p - 8 * kSWords;
-        const int sub = q >> 3, e = kOrd[q & 7];
+        const int q = p - 6 * kSWords;
+        const int sub = q / 6, e = kOrd[q % 6];
         const bool isw = e >= 4;
-        const int r = (isw ? wn : wm) * 128 + (e & 3) * 32 + l32;
+        const int r = isw ? wn * 64 + (e - 4) * 32 + l32 : wm * 128 + e * 32 + l32;
         const i32x4 v = *reinterpret_cast<const i32x4*>((isw ? sW : sA) + sw_off(r, 2 * sub + lh));
         if (isw)
-          f.w[sub][e & 3] = v;
+          f.w[sub][e - 4] = v;
         else
-          f.a[sub][e & 3] = v;
+          f.a[sub][e] = v;
       }
     }
   };
 
-  // 4 x 4 tiles of 32x32 per wave (128 x 128), D[n][m] in 16 fp32 per lane
-  f32x16 acc[4][4];
+  // 2 x 4 tiles of 32x32 per wave (64 channels x 128 rows), D[n][m] in 16
+  // fp32 per lane
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // MFMA i of k-step k: FP8 tile (u, t) = (i / 4, i % 4); MX sub-step i / 16
-  constexpr int kMfma = MX ? 32 : 16;
+  // MFMA i of k-step k: tile (u, t) = ((i / 4) % 2, i % 4); MX sub-step i / 8
+  constexpr int kMfma = MX ? 16 : 8;
   auto mma_piece = [&](const frags_t& f, int k, int i) {
-    const int u = (i >> 2) & 3, t = i & 3;
+    const int u = (i >> 2) & 1, t = i & 3;
     if constexpr (!MX) {
       acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[u], f.a[t], acc[u][t], 0, 0,
                                                                   0, 127, 0, 127);
     } else {
+      // the scale operands are the exponent dwords with byte 2 s selected;
       // blocks past K (last k-step, K not a multiple of 128) have zero codes
-      // and zero exponent bytes; 2^0 is used for them
-      const int sub = i >> 4;
-      const int q = 2 * sub + lh;
-      const bool qok = SALIGN || q < kblocks - 4 * k;
+      // and zero exponent bytes, so their products are zero
+      const int sub = i >> 3;
       const i32x8 wf = i32x8{f.w[sub][u][0], f.w[sub][u][1], f.w[sub][u][2], f.w[sub][u][3], 0, 0, 0, 0};
       const i32x8 af = i32x8{f.a[sub][t][0], f.a[sub][t][1], f.a[sub][t][2], f.a[sub][t][3], 0, 0, 0, 0};
-      const int ws = qok ? (int)__builtin_amdgcn_ubfe(f.ws[u], 8 * q, 8) : 127;
-      const int as = qok ? (int)__builtin_amdgcn_ubfe(f.as[t], 8 * q, 8) : 127;
-      acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, acc[u][t], 4, 4, 0, ws, 0, as);
+      if (sub == 0)
+        acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, acc[u][t], 4, 4, 0,
+                                                                    (int)f.ws[u], 0, (int)f.as[t]);
+      else
+        acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, acc[u][t], 4, 4, 2,
+                                                                    (int)f.ws[u], 2, (int)f.as[t]);
     }
   };
 
@@ -282,11 +283,13 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
     }
   };
 
+  // prologue: k-steps 0..3 in two interleaved pairs; stage 0 (all of the
+  // first pair) must land before its fragments are read
 #pragma unroll
   for (int k0 = 0; k0 < 4; k0 += 2)
 #pragma unroll
     for (int x = 0; x < 2 * kGroup; ++x) issue_piece(k0 + (x & 1), x >> 1);
-  wait_vm_barrier<3 * kGroup>();
+  wait_vm_barrier<2 * kGroup>();
   frags_t f0, f1;
 #pragma unroll
   for (int p = 0; p < kReads; ++p) read_piece(0, f0, p);
@@ -304,21 +307,21 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
   // together, out-of-range channels read as zero); the bf16 results go
   // through LDS so that each row of the tile leaves in 16-byte pieces that
   // fill whole cache lines.
-  f32x4 swv[4][4];
+  f32x4 swv[2][4];
   float sxv[4];
   if constexpr (!MX) {
-    const __amdgpu_buffer_rsrc_t rsx = make_rsrc(a_aux, (int64_t)M * 4);
+    const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a_aux, (int64_t)M * 4);
     const __amdgpu_buffer_rsrc_t rsn = make_rsrc(w_aux, (int64_t)N * 4);
     const bool edge_n = n0 + BN > N;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       sxv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             rsx, (uint32_t)(m0 + wm * 128 + t * 32 + l32) * 4, 0, 0));
+                                             rsm, (uint32_t)(m0 + wm * 128 + t * 32 + l32) * 4, 0, 0));
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint32_t n = (uint32_t)(n0 + wn * 128 + u * 32 + 8 * b + 4 * lh);
+        const uint32_t n = (uint32_t)(n0 + wn * 64 + u * 32 + 8 * b + 4 * lh);
         if (!edge_n) {
           swv[u][b] = __builtin_bit_cast(f32x4, buf_load16(rsn, n * 4, 0));
         } else {
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         float v[4];
@@ -348,14 +351,14 @@ __global__ __launch_bounds__(256) void gemm_f8f4_kernel(const uint8_t* __restric
             make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
   __syncthreads();
-  // 4 rows per instruction, 16 lanes x 8 outputs per row
-  const int nbase = n0 + wn * 128 + (lane & 15) * 8;
+  // 8 rows per instruction, 8 lanes x 8 outputs per row
+  const int nbase = n0 + wn * 64 + (lane & 7) * 8;
   const bool full_n = nbase + 7 < N && (N & 7) == 0;
 #pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
-    const int ml = 4 * i + (lane >> 4);
+  for (int i = 0; i < 16; ++i) {
+    const int ml = 8 * i + (lane >> 3);
     const int m = m0 + wm * 128 + ml;
-    const u32x4 o = *reinterpret_cast<const u32x4*>(so + ml * kEpiPitch + (lane & 15) * 16);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(so + ml * kEpiPitch + (lane & 7) * 16);
     if (m < M) {
       uint16_t* py = Y + (int64_t)m * N + nbase;
       if (full_n) {
@@ -373,7 +376,7 @@ template <bool MX, bool SALIGN>
 hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, const void* w_aux,
                   int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN>), dim3(tiles), dim3(256), 0, stream,
+  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN>), dim3(tiles), dim3(kThreads), 0, stream,
                      (const uint8_t*)a, a_aux, (int)M, (const uint8_t*)w, w_aux, (int)N, (int)K,
                      (uint16_t*)y);
   return hipGetLastError();
