@@ -180,6 +180,41 @@ qg_status qg_qgemm(qg_format wfmt, qg_format afmt,
 qg_status qg_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
                       void* codes, void* e8m0, void* stream);
 
+typedef enum {
+    QG_NORM_LAYER = 0,   /* (x - mean) / sqrt(var + eps) * gamma + beta */
+    QG_NORM_RMS = 1      /* x / sqrt(mean(x^2) + eps) * gamma */
+} qg_norm;
+
+/*
+ * qg_norm_quant -- fused LayerNorm / RMSNorm of each row followed by its
+ * per-row dynamic quantization, written once ([SRV] section 4.4: the row's
+ * statistics, the normalization and the quantization scale in one kernel,
+ * codes and scale written once; RMSNorm + quantization as the same kind of
+ * fusion).  The result equals the normalized rows passed to
+ * qg_quantize_pack with group == K.
+ *   norm       QG_NORM_LAYER or QG_NORM_RMS.
+ *   fmt        QG_FP8_E4M3 | QG_INT8_SYM | QG_INT8_ASYM.
+ *   src        [rows][K] of src_dtype (QG_BF16 or QG_F32), row-major.
+ *   gamma      fp32 [K]; beta fp32 [K] for QG_NORM_LAYER, NULL for
+ *              QG_NORM_RMS.
+ *   eps        >= 0 and finite.
+ *   codes      [rows][K] (int8 / uint8 / E4M3 bytes); scales fp32 [rows];
+ *              zeros fp32 [rows] for QG_INT8_ASYM, NULL otherwise.
+ * Arithmetic (bit-exact reference): the row sums (of x and of (x - mean)^2,
+ * or of x^2) are accumulated in fp64 and the variance is the biased one
+ * (divide by K); mean and r = 1 / sqrt(var + eps) are rounded once to fp32;
+ * then t = x - mean, u = t * r, y = u * gamma, y = y + beta, each one fp32
+ * operation rounded to nearest even (no fused multiply-add); y is quantized
+ * as by qg_quantize_pack.
+ * Limits: K a multiple of 8, 8 <= K <= 16384 (QG_ERR_GEOMETRY when not a
+ * multiple of 8, QG_ERR_UNSUPPORTED above 16384); rows <= 2^31 - 1.
+ * Errors: QG_ERR_GEOMETRY, QG_ERR_FORMAT, QG_ERR_NULL, QG_ERR_ALIGN,
+ * QG_ERR_UNSUPPORTED, QG_ERR_HIP.
+ */
+qg_status qg_norm_quant(qg_norm norm, qg_format fmt, const void* src, qg_dtype src_dtype,
+                        const float* gamma, const float* beta, float eps, int64_t rows,
+                        int64_t K, void* codes, void* scales, void* zeros, void* stream);
+
 /*
  * qg_mx_gemm -- block-scaled MXFP4 product
  *   y[m][n] = bf16( sum_b 2^(ea[m][b] + eb[n][b] - 254) *

@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(HERE, "libqgemm.so")
 INT4_SYM, INT4_ASYM, INT8_SYM, INT8_ASYM, FP8_E4M3, BF16_ACT, MXFP4 = range(7)
 # qg_dtype
 BF16, F32 = 0, 1
+# qg_norm
+NORM_LAYER, NORM_RMS = 0, 1
 # qg_status
 OK, ERR_GEOMETRY, ERR_ALIGN, ERR_FORMAT, ERR_NULL, ERR_HIP, ERR_UNSUPPORTED = range(7)
 
 EXPORTS = [
     "qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant", "qg_mx_gemm",
-    "qg_status_str", "qg_last_error", "qg_abi_version",
+    "qg_norm_quant", "qg_status_str", "qg_last_error", "qg_abi_version",
 ]
 
 _lib = None
@@ -44,8 +46,10 @@ def load() -> ctypes.CDLL:
     lib.qg_qgemm.argtypes = [i32, i32, vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
     lib.qg_mx_quant.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     lib.qg_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp]
+    lib.qg_norm_quant.argtypes = [i32, i32, vp, i32, vp, vp, ctypes.c_float, i64, i64, vp, vp,
+                                  vp, vp]
     for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
-                 "qg_mx_gemm"]:
+                 "qg_mx_gemm", "qg_norm_quant"]:
         getattr(lib, name).restype = i32
     lib.qg_status_str.argtypes = [i32]
     lib.qg_status_str.restype = ctypes.c_char_p

@@ -83,6 +83,35 @@ def quantize_pack(x: torch.Tensor, fmt: str, group: int | None = None):
     return codes, scales, zeros
 
 
+NORMS = {"layer": _lib.NORM_LAYER, "rms": _lib.NORM_RMS}
+
+
+def norm_quant(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None = None,
+               fmt: str = "fp8_e4m3", norm: str = "layer", eps: float = 1e-5):
+    """Fused LayerNorm ("layer", needs beta) or RMSNorm ("rms", beta None) of
+    each row of x [rows][K] (bf16 or fp32) followed by its per-row dynamic
+    quantization ("fp8_e4m3", "int8_sym", "int8_asym").  gamma, beta: fp32
+    [K].  Returns (codes [rows][K], scales fp32 [rows][1], zeros or None)."""
+    lib = _lib.load()
+    dev = _dev(x)
+    if norm not in NORMS:
+        raise ValueError(f"unknown normalization {norm}")
+    if fmt not in ("fp8_e4m3", "int8_sym", "int8_asym"):
+        raise ValueError(f"norm_quant: unsupported format {fmt}")
+    for t in (gamma, beta):
+        if t is not None and (t.dtype != torch.float32 or _dev(t) != dev):
+            raise ValueError("gamma and beta must be fp32 tensors on the input's device")
+    rows, k = x.shape
+    cshape, cdt, sdt = _code_shapes(fmt, rows, k, k)
+    codes = torch.empty(cshape, dtype=cdt, device=dev)
+    scales = torch.empty((rows, 1), dtype=sdt, device=dev)
+    zeros = torch.empty_like(scales) if fmt in _ASYM else None
+    _lib.check(lib.qg_norm_quant(NORMS[norm], FORMATS[fmt], _ptr(x), _src_dtype(x), _ptr(gamma),
+                                 _ptr(beta), ctypes.c_float(eps), rows, k, _ptr(codes),
+                                 _ptr(scales), _ptr(zeros), _stream(dev)))
+    return codes, scales, zeros
+
+
 def dequant(codes: torch.Tensor, scales: torch.Tensor, zeros, fmt: str, k: int,
             group: int | None = None, out_dtype=torch.float32) -> torch.Tensor:
     """x_hat = s * (q - z) (or 2^e * e2m1 for "mxfp4") as [rows][K]."""

@@ -19,6 +19,11 @@ hipError_t launch_dequant(qg_format fmt, const void* codes, const void* scales,
                           const void* zeros, int64_t rows, int64_t K, int64_t group, void* dst,
                           qg_dtype dst_dtype, hipStream_t stream);
 
+hipError_t launch_norm_quant(bool rms, qg_format fmt, const void* src, qg_dtype src_dtype,
+                             const void* gamma, const void* beta, float eps, int64_t rows,
+                             int64_t K, void* codes, void* scales, void* zeros,
+                             hipStream_t stream);
+
 hipError_t launch_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
                            void* codes, void* e8m0, hipStream_t stream);
 

@@ -472,6 +472,196 @@ void launch_dequant_t(const void* codes, const void* scales, const void* zeros, 
                        stream, codes, scales, zeros, total, t_vecs, dst);
 }
 
+// --------------------------------------------------------------- fused norm + quant
+
+// LayerNorm or RMSNorm of one row followed by its per-row dynamic
+// quantization, written once (《推理优化与量化算子深度技术调研》 section 4.4:
+// statistics, normalization and the quantization scale of a row in one
+// kernel, codes and scale written once).  One workgroup per row; thread t
+// holds vecs t + kThreads i (i < VPT) of the row in registers.  The row
+// statistics are summed in fp64 (sum of x, then of (x - mean)^2; or sum of
+// x^2), mean and r = 1 / sqrt(var + eps) are rounded once to fp32, and the
+// normalized value is formed in fp32 with one rounding per operation and no
+// fused multiply-add: t = x - mean, u = t * r, y = u * gamma (+ beta).  The
+// codes are then those of the per-row quantizer above.
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();   // the previous use of red is over
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+  return t;
+}
+
+template <int K, bool BF16, bool RMS, int VPT>
+__global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __restrict__ src,
+                                                              int64_t kvecs,
+                                                              const float* __restrict__ gamma,
+                                                              const float* __restrict__ beta,
+                                                              float eps, void* __restrict__ codes,
+                                                              void* __restrict__ scales,
+                                                              void* __restrict__ zeros) {
+  __shared__ double redd[kThreads / 64];
+  __shared__ float red[3][kThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t v0 = row * kvecs;
+  float v[VPT][8];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t vec = tid + (int64_t)kThreads * i;
+    if (vec < kvecs) {
+      load_vec<BF16>(src, v0 + vec, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.f;   // contributes nothing to the sums
+    }
+  }
+  const double kd = (double)(kvecs * 8);
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double d = (double)v[i][e];
+      acc += RMS ? d * d : d;
+    }
+  const double s1 = block_sum_f64(acc, redd);
+  const double mean64 = RMS ? 0.0 : s1 / kd;
+  double var64 = s1 / kd;
+  if constexpr (!RMS) {
+    double acc2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      if (tid + (int64_t)kThreads * i >= kvecs) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double d = (double)v[i][e] - mean64;
+        acc2 += d * d;
+      }
+    }
+    var64 = block_sum_f64(acc2, redd) / kd;
+  }
+  const float mean32 = (float)mean64;
+  const float r32 = (float)(1.0 / __builtin_sqrt(var64 + (double)eps));
+
+  Stats st{0.f, __builtin_inff(), -__builtin_inff()};
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t vec = tid + (int64_t)kThreads * i;
+    if (vec >= kvecs) continue;
+    const f32x4* gp = reinterpret_cast<const f32x4*>(gamma) + 2 * vec;
+    const f32x4 g0 = gp[0], g1 = gp[1];
+    f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+    if constexpr (!RMS) {
+      const f32x4* bp = reinterpret_cast<const f32x4*>(beta) + 2 * vec;
+      b0 = bp[0];
+      b1 = bp[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = e < 4 ? g0[e] : g1[e - 4];
+      const float t = RMS ? v[i][e] : v[i][e] - mean32;
+      float y = (t * r32) * g;
+      // the product is rounded before beta is added: the empty asm keeps the
+      // compiler from fusing the two into one multiply-add (which
+      // -ffp-contract=fast would do regardless of a contract pragma)
+      asm volatile("" : "+v"(y));
+      if constexpr (!RMS) y = y + (e < 4 ? b0[e] : b1[e - 4]);
+      v[i][e] = y;
+    }
+    const Stats s = stats_of(v[i]);
+    st.amax = __builtin_fmaxf(st.amax, s.amax);
+    st.lo = __builtin_fminf(st.lo, s.lo);
+    st.hi = __builtin_fmaxf(st.hi, s.hi);
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
+    st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
+    st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+  }
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
+    red[0][w] = st.amax;
+    red[1][w] = st.lo;
+    red[2][w] = st.hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    st.amax = __builtin_fmaxf(st.amax, red[0][i]);
+    st.lo = __builtin_fminf(st.lo, red[1][i]);
+    st.hi = __builtin_fmaxf(st.hi, red[2][i]);
+  }
+  const Params p = make_params<K>(st);
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t vec = tid + (int64_t)kThreads * i;
+    if (vec < kvecs) quantize_store<K>(v[i], p, codes, v0 + vec);
+  }
+  if (tid == 0) store_params<K>(p, scales, zeros, row);
+}
+
+template <int K, bool BF16, bool RMS>
+void launch_norm_quant_t(const void* src, int64_t rows, int64_t kvecs, const float* gamma,
+                         const float* beta, float eps, void* codes, void* scales, void* zeros,
+                         hipStream_t stream) {
+  const dim3 grid((unsigned)rows), block(kThreads);
+  if (kvecs <= kThreads)
+    hipLaunchKernelGGL((norm_quant_kernel<K, BF16, RMS, 1>), grid, block, 0, stream, src, kvecs,
+                       gamma, beta, eps, codes, scales, zeros);
+  else if (kvecs <= 2 * kThreads)
+    hipLaunchKernelGGL((norm_quant_kernel<K, BF16, RMS, 2>), grid, block, 0, stream, src, kvecs,
+                       gamma, beta, eps, codes, scales, zeros);
+  else if (kvecs <= 4 * kThreads)
+    hipLaunchKernelGGL((norm_quant_kernel<K, BF16, RMS, 4>), grid, block, 0, stream, src, kvecs,
+                       gamma, beta, eps, codes, scales, zeros);
+  else
+    hipLaunchKernelGGL((norm_quant_kernel<K, BF16, RMS, 8>), grid, block, 0, stream, src, kvecs,
+                       gamma, beta, eps, codes, scales, zeros);
+}
+
+template <bool BF16, bool RMS>
+void launch_norm_quant_fmt(qg_format fmt, const void* src, int64_t rows, int64_t kvecs,
+                           const float* gamma, const float* beta, float eps, void* codes,
+                           void* scales, void* zeros, hipStream_t stream) {
+  if (fmt == QG_INT8_SYM)
+    launch_norm_quant_t<K_INT8_SYM, BF16, RMS>(src, rows, kvecs, gamma, beta, eps, codes, scales,
+                                              zeros, stream);
+  else if (fmt == QG_INT8_ASYM)
+    launch_norm_quant_t<K_INT8_ASYM, BF16, RMS>(src, rows, kvecs, gamma, beta, eps, codes,
+                                               scales, zeros, stream);
+  else
+    launch_norm_quant_t<K_FP8, BF16, RMS>(src, rows, kvecs, gamma, beta, eps, codes, scales,
+                                         zeros, stream);
+}
+
+}  // namespace
+
+hipError_t launch_norm_quant(bool rms, qg_format fmt, const void* src, qg_dtype src_dtype,
+                             const void* gamma, const void* beta, float eps, int64_t rows,
+                             int64_t K, void* codes, void* scales, void* zeros,
+                             hipStream_t stream) {
+  const int64_t kvecs = K / 8;
+  const float* g = (const float*)gamma;
+  const float* b = (const float*)beta;
+  if (src_dtype == QG_BF16) {
+    if (rms)
+      launch_norm_quant_fmt<true, true>(fmt, src, rows, kvecs, g, b, eps, codes, scales, zeros, stream);
+    else
+      launch_norm_quant_fmt<true, false>(fmt, src, rows, kvecs, g, b, eps, codes, scales, zeros, stream);
+  } else {
+    if (rms)
+      launch_norm_quant_fmt<false, true>(fmt, src, rows, kvecs, g, b, eps, codes, scales, zeros, stream);
+    else
+      launch_norm_quant_fmt<false, false>(fmt, src, rows, kvecs, g, b, eps, codes, scales, zeros, stream);
+  }
+  return hipGetLastError();
+}
+
+namespace {
 }  // namespace
 
 hipError_t launch_quantize(qg_format fmt, const void* src, qg_dtype src_dtype, int64_t rows,

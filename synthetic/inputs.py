@@ -30,7 +30,7 @@ import torch
 __all__ = [
     "rng_for", "normal_weights", "normal_activations", "to_bf16", "bf16_as_f32",
     "scale_input_channels", "scale_random_entries", "Projection", "WORKLOADS",
-    "workload_case", "small_case",
+    "workload_case", "small_case", "norm_weights",
 ]
 
 
@@ -131,6 +131,16 @@ def workload_case(name: str, proj_index: int = 0):
     if wl.x_outlier[0] > 0:
         scale_random_entries(rng, x, *wl.x_outlier)
     return dict(w=w, x=to_bf16(x), k=p.k, n=p.n, ms=wl.ms, asym=wl.asym, name=p.name)
+
+
+def norm_weights(k: int, seed: int):
+    """Seeded normalization weights of K channels: gamma ~ 1 + 0.1 N(0,1),
+    beta ~ 0.05 N(0,1), fp32 (the shape of trained norm weights: near one,
+    small shifts)."""
+    rng = rng_for(seed)
+    gamma = (np.float32(1.0) + np.float32(0.1) * rng.standard_normal(k, dtype=np.float32))
+    beta = np.float32(0.05) * rng.standard_normal(k, dtype=np.float32)
+    return gamma.astype(np.float32), beta.astype(np.float32)
 
 
 def small_case(m: int, k: int, n: int, seed: int, w_outlier=(0.0, 1.0), x_outlier=(0.0, 1.0),

@@ -102,6 +102,27 @@ def test_mx_validation(lib):
     assert lib.qg_mx_gemm(A16, A16b, 4, A16c, A16d, 4, 64, MIS, None) == _lib.ERR_ALIGN
 
 
+def test_norm_quant_validation(lib):
+    n = lib.qg_norm_quant
+    L, R = _lib.NORM_LAYER, _lib.NORM_RMS
+    f8, s8, a8 = _lib.FP8_E4M3, _lib.INT8_SYM, _lib.INT8_ASYM
+    e = ctypes.c_float(1e-5)
+    ok = (A16, _lib.BF16, A16b, A16c, e, 4, 256, A16d, A16e, None, None)
+    assert n(7, f8, *ok) == _lib.ERR_FORMAT
+    assert n(L, _lib.INT4_SYM, *ok) == _lib.ERR_FORMAT
+    assert n(L, f8, A16, 9, A16b, A16c, e, 4, 256, A16d, A16e, None, None) == _lib.ERR_FORMAT
+    assert n(L, f8, A16, _lib.BF16, A16b, A16c, e, 4, 260, A16d, A16e, None, None) == _lib.ERR_GEOMETRY
+    assert n(L, f8, A16, _lib.BF16, A16b, A16c, e, 0, 256, A16d, A16e, None, None) == _lib.ERR_GEOMETRY
+    assert n(L, f8, A16, _lib.BF16, A16b, A16c, ctypes.c_float(-1.0), 4, 256, A16d, A16e, None,
+             None) == _lib.ERR_GEOMETRY
+    assert n(L, f8, A16, _lib.BF16, A16b, None, e, 4, 256, A16d, A16e, None, None) == _lib.ERR_NULL
+    assert n(R, f8, *ok) == _lib.ERR_NULL                  # RMSNorm takes no beta
+    assert n(L, a8, *ok) == _lib.ERR_NULL                  # asymmetric needs zeros
+    assert n(L, s8, A16, _lib.BF16, MIS, A16c, e, 4, 256, A16d, A16e, None, None) == _lib.ERR_ALIGN
+    assert n(L, f8, A16, _lib.BF16, A16b, A16c, e, 4, 16392, A16d, A16e, None,
+             None) == _lib.ERR_UNSUPPORTED
+
+
 def test_python_raises_value_error_for_geometry(lib):
     assert lib.qg_qgemv(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e,
                         None) == _lib.ERR_GEOMETRY
