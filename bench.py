@@ -218,7 +218,23 @@ def bench_gemms(qg, torch, dev, stream):
                                 act_quant_us=tq * 1e6,
                                 act_quant_gbs=(8192 * 8192 * 3 + 8192 * 4) / tq / 1e9,
                                 end_to_end_tflops=fl / (t + tq) / 1e12)
-    del x, wq, sw, xq, sx, y, c
+    # fused RMSNorm / LayerNorm + per-token FP8 quantization of the same
+    # activations (one read of x, one write of codes and scales), against
+    # the unfused path: torch's layer norm writing bf16, then the quantizer
+    from synthetic import norm_weights
+    gamma, beta = (torch.from_numpy(a).to(dev) for a in norm_weights(8192, 4))
+    nbytes = 8192 * 8192 * 3 + 8192 * 4 + 2 * 8192 * 4
+    for norm in ("rms", "layer"):
+        b_ = beta if norm == "layer" else None
+        tn = timed(lambda: qg.norm_quant(x, gamma, b_, "fp8_e4m3", norm, 1e-5), 10)
+        out[f"{norm}_norm_fp8_quant_8192"] = dict(us=tn * 1e6, gbs=nbytes / tn / 1e9,
+                                                  frac=nbytes / tn / 1e9 / HBM_PEAK_GBS)
+    gb = gamma.to(torch.bfloat16)
+    bb = beta.to(torch.bfloat16)
+    tu = timed(lambda: qg.quantize_pack(torch.nn.functional.layer_norm(x, (8192,), gb, bb, 1e-5),
+                                        "fp8_e4m3"), 10)
+    out["layer_norm_fp8_quant_8192"]["unfused_us"] = tu * 1e6
+    del x, wq, sw, xq, sx, y, c, gamma, beta, gb, bb
     # MXFP4, M=4096, N=K=8192
     c = workload_case("mxfp4_4096x8192")
     x = c["x"].to(dev)

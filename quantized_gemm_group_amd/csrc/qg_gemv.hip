@@ -792,11 +792,12 @@ hipError_t launch_wave(bool asym, int ng, const void* x, int M, const void* w, c
 }
 
 // Groups per wave for the per-wave kernel (0: not applicable).  Measured on
-// MI355X for the Llama-3-8B decode shapes: 8 groups per wave, but 4 for
-// layers of at most 8192 channels (more waves in flight when there are few
-// 16-channel tiles: QKV 5.91 -> 5.76 us, O 4.53 -> 4.45 us; gate+up is
-// slower with 4); 16 (M = 1 only: 128 VGPRs) when K is too long for 16
-// slices of 8.
+// MI355X for the Llama-3-8B decode layer (four projections back to back in
+// a graph): 8 groups per wave; at M = 4, 4 for layers of at most 8192
+// channels (more waves in flight when there are few 16-channel tiles: layer
+// 2.81 -> 2.90 TB/s; at M = 1 the same choice is faster for each projection
+// alone but slower in the layer, 3.69 -> 3.61 TB/s); 16 (M = 1 only: 128
+// VGPRs) when K is too long for 16 slices of 8.
 int pick_wave_ng(int M, int N, int K) {
   const int G = K / kGroup;
   if (M > 4 || G % 4 != 0) return 0;
@@ -805,7 +806,7 @@ int pick_wave_ng(int M, int N, int K) {
     const int ks = G / ng;
     return G % ng == 0 && ks <= 16 && (size_t)ks * (mm * ng * 256 + 1024) <= 160 * 1024;
   };
-  if (N <= 8192 && fits(4)) return 4;
+  if (M > 1 && N <= 8192 && fits(4)) return 4;
   if (fits(8)) return 8;
   if (fits(4)) return 4;
   if (M == 1 && fits(16)) return 16;
