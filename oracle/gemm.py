@@ -14,6 +14,10 @@ carries no rounding beyond fp64 summation:
   per output channel; figure 6-2 of the same lesson (Out = acc * scale_x *
   scale_w).
 * MXFP4: both operands 2^e * e2m1(code) per 32-block.
+* SwiGLU (《推理优化与量化算子深度技术调研》 section 4.6): the gate and up
+  projections as one product over the concatenation [W_gate; W_up] (rows
+  0 .. I - 1 gate, I .. 2I - 1 up), then h = SiLU(gate) * up with
+  SiLU(g) = g / (1 + exp(-g)), all in float64.
 
 ``rel_fro`` is ||Y - Y_ref||_F / ||Y_ref||_F in float64.
 """
@@ -91,3 +95,23 @@ def int8_reference(xq, sx, zx, wq, sw, zw) -> np.ndarray:
 
 def mx_reference(a_packed, a_e8m0, b_packed, b_e8m0) -> np.ndarray:
     return reference_product(_mx.dequantize(a_packed, a_e8m0), _mx.dequantize(b_packed, b_e8m0))
+
+
+def silu(g) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + exp(-g)), float64."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_reference(x, packed, scales, zeros, group: int, channels=None) -> np.ndarray:
+    """h [M][I] = SiLU(x W_gate^T) * (x W_up^T) for the quantized [2I][K]
+    concatenation [W_gate; W_up] (W4A16 operands as in w4a16_reference).
+    ``channels`` optionally selects intermediate channels (columns of h)."""
+    n2 = np.asarray(packed).shape[0]
+    if n2 % 2:
+        raise ValueError("invalid quantization geometry")
+    i = n2 // 2
+    ch = np.arange(i) if channels is None else np.asarray(channels)
+    gate = w4a16_reference(x, packed, scales, zeros, group, rows=ch)
+    up = w4a16_reference(x, packed, scales, zeros, group, rows=ch + i)
+    return silu(gate) * up

@@ -89,3 +89,37 @@ def test_rel_fro_metric():
     assert gemm.rel_fro(y, y) == 0.0
     assert abs(gemm.rel_fro(y * 1.001, y) - 0.001) < 1e-12
     assert abs(gemm.rel_fro(np.array([[3.0, 0.0]]), y) - 0.8) < 1e-12
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+def test_silu_matches_torch_and_limits():
+    import torch
+    g = np.linspace(-30.0, 30.0, 601)
+    ref = torch.nn.functional.silu(torch.from_numpy(g)).numpy()
+    assert np.allclose(gemm.silu(g), ref, rtol=1e-15, atol=1e-300)
+    assert gemm.silu(np.array([0.0]))[0] == 0.0
+    assert abs(gemm.silu(np.array([40.0]))[0] - 40.0) < 1e-12          # -> g for large g
+    assert abs(gemm.silu(np.array([-40.0]))[0]) < 1e-15                 # -> 0 for very negative g
+
+
+def test_swiglu_reference_is_gate_then_up():
+    # tiny brute-force case: [W_gate; W_up] as one quantized [2I][K] matrix;
+    # gate rows come first (a swapped split fails the comparison)
+    rng = np.random.default_rng(3)
+    i, k, m = 3, 128, 2
+    w = (rng.standard_normal((2 * i, k)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    q, s = IQ.quantize_sym(w, 128)
+    packed = IQ.pack_int4(q)
+    w_hat = IQ.dequantize(q, s, None, 128)
+    y = gemm.brute_force_product(x, w_hat)
+    gate, up = y[:, :i], y[:, i:]
+    expect = gate / (1.0 + np.exp(-gate)) * up
+    h = gemm.swiglu_reference(x, packed, s, None, 128)
+    assert np.allclose(h, expect, rtol=1e-12, atol=1e-12)
+    swapped = up / (1.0 + np.exp(-up)) * gate
+    assert not np.allclose(h, swapped, rtol=1e-3)
+    # channel selection picks the same columns
+    assert np.allclose(gemm.swiglu_reference(x, packed, s, None, 128, channels=[2, 0]),
+                       expect[:, [2, 0]], rtol=1e-12, atol=1e-12)
