@@ -259,6 +259,17 @@ def bench_gemms(qg, torch, dev, stream):
         fl = 2 * 2048 * c["k"] * c["n"]
         out[f"w4a16_prefill_{name}"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
                                             frac=fl / t / 1e12 / PEAK_TFLOPS["bf16"])
+        if name == "ffn_up":
+            # the up shape is a fused gate+up (29568 = 2 x 14784 rows): the
+            # SwiGLU epilogue variant writes SiLU(gate) * up, [2048][14784]
+            h = torch.empty((2048, c["n"] // 2), dtype=torch.bfloat16, device=dev)
+            th = timed(lambda: qg.qgemm_swiglu(x, codes, s, None, "int4_sym", out=h), 5)
+            tm = timed(lambda: torch.mul(torch.nn.functional.silu(y[:, :c["n"] // 2]),
+                                         y[:, c["n"] // 2:], out=h), 5)
+            out["w4a16_prefill_ffn_gate_up_swiglu"] = dict(
+                us=th * 1e6, tflops=fl / th / 1e12, frac=fl / th / 1e12 / PEAK_TFLOPS["bf16"],
+                unfused_us=(t + tm) * 1e6)
+            del h
         del x, codes, s, y, c
     torch.cuda.empty_cache()
     return out

@@ -171,6 +171,25 @@ qg_status qg_qgemm(qg_format wfmt, qg_format afmt,
                    int64_t N, int64_t K, int64_t group, void* y, void* stream);
 
 /*
+ * qg_qgemm_swiglu -- fused SwiGLU projection of W4A16 prefill:
+ * H = SiLU(X W_gate^T) * (X W_up^T) ([SRV] section 4.6: the gate and up
+ * projections as one GEMM over the concatenation [W_gate; W_up], SiLU and the
+ * product formed in registers, H written once; SiLU(g) = g / (1 + e^-g)).
+ *   wfmt       QG_INT4_SYM | QG_INT4_ASYM; afmt QG_BF16_ACT; group 128.
+ *   a          bf16 [M][K].
+ *   wcodes, wscales, wzeros   the quantized [N2][K] concatenation: rows
+ *              0 .. N2/2 - 1 are W_gate, rows N2/2 .. N2 - 1 are W_up (the
+ *              storage format of qg_quantize_pack).
+ *   N2         2 I, even.
+ *   h          bf16 [M][I]; each value is the fp32 SiLU(gate) * up rounded
+ *              once (RNE).
+ * Errors as for qg_qgemm; QG_ERR_GEOMETRY for an odd N2.
+ */
+qg_status qg_qgemm_swiglu(qg_format wfmt, qg_format afmt, const void* a, int64_t M,
+                          const void* wcodes, const void* wscales, const void* wzeros,
+                          int64_t N2, int64_t K, int64_t group, void* h, void* stream);
+
+/*
  * qg_mx_quant -- OCP MXFP4 quantization of [rows][K] along K ([MX]; [L6]
  * section 2 micro-block scaling).  K must be a multiple of 32 ([L6]
  * section 3), else QG_ERR_GEOMETRY.

@@ -23,7 +23,7 @@ OK, ERR_GEOMETRY, ERR_ALIGN, ERR_FORMAT, ERR_NULL, ERR_HIP, ERR_UNSUPPORTED = ra
 
 EXPORTS = [
     "qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant", "qg_mx_gemm",
-    "qg_norm_quant", "qg_status_str", "qg_last_error", "qg_abi_version",
+    "qg_norm_quant", "qg_qgemm_swiglu", "qg_status_str", "qg_last_error", "qg_abi_version",
 ]
 
 _lib = None
@@ -48,8 +48,9 @@ def load() -> ctypes.CDLL:
     lib.qg_mx_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp]
     lib.qg_norm_quant.argtypes = [i32, i32, vp, i32, vp, vp, ctypes.c_float, i64, i64, vp, vp,
                                   vp, vp]
+    lib.qg_qgemm_swiglu.argtypes = [i32, i32, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
     for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
-                 "qg_mx_gemm", "qg_norm_quant"]:
+                 "qg_mx_gemm", "qg_norm_quant", "qg_qgemm_swiglu"]:
         getattr(lib, name).restype = i32
     lib.qg_status_str.argtypes = [i32]
     lib.qg_status_str.restype = ctypes.c_char_p

@@ -161,6 +161,24 @@ def qgemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_zero
     return y
 
 
+def qgemm_swiglu(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_zeros,
+                 wfmt: str, group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused SwiGLU projection h = SiLU(a W_gate^T) * (a W_up^T) with bf16 a
+    [M][K] and INT4 weights quantized as the [2I][K] concatenation
+    [W_gate; W_up].  Returns h bf16 [M][I]."""
+    lib = _lib.load()
+    dev = _dev(a)
+    if a.dtype != torch.bfloat16:
+        raise ValueError("a must be bf16")
+    m, k = a.shape
+    n2 = w_codes.shape[0]
+    h = torch.empty((m, n2 // 2), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_qgemm_swiglu(FORMATS[wfmt], FORMATS["bf16"], _ptr(a), m, _ptr(w_codes),
+                                   _ptr(w_scales), _ptr(w_zeros), n2, k, group, _ptr(h),
+                                   _stream(dev)))
+    return h
+
+
 def mx_quant(x: torch.Tensor):
     """OCP MXFP4 quantization of x [rows][K] along K.  Returns (codes uint8
     [rows][K/2], e8m0 uint8 [rows][K/32])."""

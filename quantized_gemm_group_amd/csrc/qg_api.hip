@@ -204,6 +204,27 @@ qg_status qg_qgemm(qg_format wfmt, qg_format afmt, const void* a, const void* a_
   return fail(QG_ERR_FORMAT, "qgemm: unsupported format pair");
 }
 
+qg_status qg_qgemm_swiglu(qg_format wfmt, qg_format afmt, const void* a, int64_t M,
+                          const void* wcodes, const void* wscales, const void* wzeros,
+                          int64_t N2, int64_t K, int64_t group, void* h, void* stream) {
+  if (!is_int4(wfmt) || afmt != QG_BF16_ACT)
+    return fail(QG_ERR_FORMAT, "qgemm_swiglu: weights INT4_SYM / INT4_ASYM with BF16_ACT activations");
+  if (M < 1 || N2 < 2 || K < 1 || N2 % 2 != 0)
+    return fail(QG_ERR_GEOMETRY, "qgemm_swiglu: M, K positive and N2 = 2 I even");
+  if (M > (int64_t)1 << 30 || N2 > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+    return fail(QG_ERR_GEOMETRY, "qgemm_swiglu: size out of range");
+  if (!a || !h) return fail(QG_ERR_NULL, "qgemm_swiglu: a and h are required");
+  if (!aligned16(a) || !aligned16(h))
+    return fail(QG_ERR_ALIGN, "qgemm_swiglu: a, h must be 16-byte aligned");
+  qg_status st = check_quant_operand(wfmt, N2, K, group, wcodes, wscales, wzeros);
+  if (st != QG_OK) return st;
+  if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemm_swiglu: only group 128 is implemented");
+  if (!fits_offsets(N2, K / 2) || !fits_offsets(M, K * 2))
+    return fail(QG_ERR_UNSUPPORTED, "qgemm_swiglu: operand larger than 2 GiB");
+  return from_hip(qg::launch_gemm_w4a16_swiglu(wfmt == QG_INT4_ASYM, a, M, wcodes, wscales, wzeros,
+                                               N2, K, h, (hipStream_t)stream));
+}
+
 qg_status qg_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K, void* codes,
                       void* e8m0, void* stream) {
   if (src_dtype != QG_BF16 && src_dtype != QG_F32)

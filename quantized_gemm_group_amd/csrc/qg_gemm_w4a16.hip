@@ -34,6 +34,15 @@
 // so the waits are explicit.  Within a group, lane half h and MFMA j cover
 // k = 64 h + 8 j .. + 7 in natural order, so a lane's codes of the group are
 // 32 contiguous bytes and its X pieces 128.
+//
+// SwiGLU variant (《推理优化与量化算子深度技术调研》 section 4.6: the gate and
+// up projections as one GEMM over [W_gate; W_up], SiLU(gate) * up formed in
+// registers and written once): the weight rows are the 2I rows of the
+// concatenation and the output is H[M][I].  A workgroup covers 128
+// intermediate channels: wave column wn takes gate rows n0 + 32 wn .. + 31 as
+// its first 32x32 channel tile and the up rows I + n0 + 32 wn .. + 31 as its
+// second, so each lane holds gate[n] and up[n] of the same channel n in the
+// same registers and the epilogue needs no exchange.
 
 #include "qg_gemm_common.hpp"
 #include "qg_internal.hpp"
@@ -97,7 +106,7 @@ struct Parity {
   static constexpr int value = V;
 };
 
-template <bool ASYM>
+template <bool ASYM, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ Wc,
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ Z, int N, int K,
@@ -111,10 +120,17 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   const int wm = wave & 1, wn = wave >> 1;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  // SWIGLU: N = 2 I weight rows, 128 intermediate channels per tile
+  const int NI = SWIGLU ? N / 2 : N;                 // output columns
+  const int TN = SWIGLU ? BN / 2 : BN;               // output columns per tile
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (NI + TN - 1) / TN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, 8, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * TN;
+  // weight row of LDS tile row r (0..255)
+  auto wrow = [&](int r) {
+    return SWIGLU ? ((r >> 5) & 1) * NI + n0 + 32 * (r >> 6) + (r & 31) : n0 + r;
+  };
   const int G = K / BK;
 
   // rows past M (N) fall outside the buffers' byte ranges and read as zero
@@ -141,11 +157,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   for (int q = 0; q < 2; ++q) {
     const int r = 32 * wave + 16 * q + (lane >> 2);
     const int c = (lane & 3) ^ ((r >> 2) & 3);
-    vw[q] = (uint32_t)(n0 + r) * (uint32_t)(K / 2) + c * 16;
+    vw[q] = (uint32_t)wrow(r) * (uint32_t)(K / 2) + c * 16;
   }
   const int srow = 64 * (wave & 3) + lane;
   const bool zwave = wave >= 4;
-  const uint32_t vs = (zwave && !ASYM) ? kOutOfRange : (uint32_t)(n0 + srow) * (uint32_t)(G * 2);
+  const uint32_t vs = (zwave && !ASYM) ? kOutOfRange : (uint32_t)wrow(srow) * (uint32_t)(G * 2);
 
   // Loads of group g into stage g % 3.  Past the last group the last group is
   // loaded again (into a stage nobody reads), so every k-step issues the same
@@ -296,17 +312,43 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   // workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if constexpr (SWIGLU) {
+    // h = SiLU(gate) * up = gate / (1 + exp(-gate)) * up, in fp32, rounded
+    // once to bf16
+    const int n = n0 + wn * 32 + l32;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = n0 + wn * 64 + nt * 32 + l32;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
+        const float g = yacc[mt][0][r], u = yacc[mt][1][r];
+        const float h = g / (1.f + __expf(-g)) * u;
+        if (m < M && n < NI) Y[(int64_t)m * NI + n] = (uint16_t)cvt_bf16x2(h, 0.f);
       }
-    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = n0 + wn * 64 + nt * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
+        }
+      }
+  }
+}
+
+template <bool ASYM, bool SWIGLU>
+void launch_t(const void* x, int64_t M, const void* wcodes, const void* wscales,
+              const void* wzeros, int64_t N, int64_t K, void* y, hipStream_t stream) {
+  const int64_t tn = SWIGLU ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  const int tiles = (int)(((M + BM - 1) / BM) * tn);
+  hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU>), dim3(tiles), dim3(kThreads), 0, stream,
+                     (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
+                     (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
+                     (uint16_t*)y, 0x000F000Fu, ASYM ? 0x43004300u : 0x43084308u);
 }
 
 }  // namespace
@@ -314,17 +356,20 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
 hipError_t launch_gemm_w4a16(bool asym, const void* x, int64_t M, const void* wcodes,
                              const void* wscales, const void* wzeros, int64_t N, int64_t K,
                              void* y, hipStream_t stream) {
-  const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   if (asym)
-    hipLaunchKernelGGL((gemm_w4a16_kernel<true>), dim3(tiles), dim3(kThreads), 0, stream,
-                       (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
-                       (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
-                       (uint16_t*)y, 0x000F000Fu, 0x43004300u);
+    launch_t<true, false>(x, M, wcodes, wscales, wzeros, N, K, y, stream);
   else
-    hipLaunchKernelGGL((gemm_w4a16_kernel<false>), dim3(tiles), dim3(kThreads), 0, stream,
-                       (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
-                       (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
-                       (uint16_t*)y, 0x000F000Fu, 0x43084308u);
+    launch_t<false, false>(x, M, wcodes, wscales, wzeros, N, K, y, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a16_swiglu(bool asym, const void* x, int64_t M, const void* wcodes,
+                                    const void* wscales, const void* wzeros, int64_t N2,
+                                    int64_t K, void* h, hipStream_t stream) {
+  if (asym)
+    launch_t<true, true>(x, M, wcodes, wscales, wzeros, N2, K, h, stream);
+  else
+    launch_t<false, true>(x, M, wcodes, wscales, wzeros, N2, K, h, stream);
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@ hipError_t launch_gemm_w4a16(bool asym, const void* x, int64_t M, const void* wc
                              const void* wscales, const void* wzeros, int64_t N, int64_t K,
                              void* y, hipStream_t stream);
 
+hipError_t launch_gemm_w4a16_swiglu(bool asym, const void* x, int64_t M, const void* wcodes,
+                                    const void* wscales, const void* wzeros, int64_t N2,
+                                    int64_t K, void* h, hipStream_t stream);
+
 hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const void* w,
                            const void* w_scales, int64_t N, int64_t K, void* y,
                            hipStream_t stream);

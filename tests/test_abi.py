@@ -123,6 +123,20 @@ def test_norm_quant_validation(lib):
              None) == _lib.ERR_UNSUPPORTED
 
 
+def test_qgemm_swiglu_validation(lib):
+    f = lib.qg_qgemm_swiglu
+    i4, bf = _lib.INT4_SYM, _lib.BF16_ACT
+    assert f(_lib.FP8_E4M3, bf, A16, 4, A16b, A16c, None, 64, 256, 128, A16e, None) == _lib.ERR_FORMAT
+    assert f(i4, _lib.INT8_SYM, A16, 4, A16b, A16c, None, 64, 256, 128, A16e, None) == _lib.ERR_FORMAT
+    assert f(i4, bf, A16, 4, A16b, A16c, None, 63, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert f(i4, bf, A16, 0, A16b, A16c, None, 64, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert f(i4, bf, A16, 4, A16b, A16c, None, 64, 256, 100, A16e, None) == _lib.ERR_GEOMETRY
+    assert f(i4, bf, None, 4, A16b, A16c, None, 64, 256, 128, A16e, None) == _lib.ERR_NULL
+    assert f(_lib.INT4_ASYM, bf, A16, 4, A16b, A16c, None, 64, 256, 128, A16e, None) == _lib.ERR_NULL
+    assert f(i4, bf, A16, 4, A16b, A16c, None, 64, 256, 128, MIS, None) == _lib.ERR_ALIGN
+    assert f(i4, bf, A16, 4, A16b, A16c, None, 64, 512, 256, A16e, None) == _lib.ERR_UNSUPPORTED
+
+
 def test_python_raises_value_error_for_geometry(lib):
     assert lib.qg_qgemv(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e,
                         None) == _lib.ERR_GEOMETRY
