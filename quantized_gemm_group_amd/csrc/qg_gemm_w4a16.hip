@@ -301,42 +301,66 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     step(g + 1, Parity<1>{});
   }
   if (g < G) step(g, Parity<0>{});
+  // Every wave's trailing loads (a repeat of the last group) have landed and
+  // every wave is past its last k-step: the row sums of the last groups are
+  // in LDS and the operand stages are free for the epilogue.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // cross terms not yet added: groups (G - 2, G - 1) for even G, G - 1 alone
-  // for odd G; their row sums come from the last k-steps of every wave
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // for odd G
   if (G & 1)
     cross(G - 1, false);
   else
     cross(G - 2, true);
-  // the trailing loads (a repeat of the last group) must land before the
-  // workgroup ends
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  // Epilogue through LDS (the operand stages, not the row-sum buffers): each
+  // wave writes its bf16 values at [m][n] with a 528-byte row pitch, then
+  // every thread moves 16-byte pieces of whole output rows to memory.  SWIGLU
+  // writes
+  // h = SiLU(gate) * up = gate / (1 + exp(-gate)) * up (fp32, one bf16
+  // rounding) for its 128 channels, the plain GEMM its 256.
+  constexpr int kPitch = 528;
+  uint16_t* const so = reinterpret_cast<uint16_t*>(smem);
   if constexpr (SWIGLU) {
-    // h = SiLU(gate) * up = gate / (1 + exp(-gate)) * up, in fp32, rounded
-    // once to bf16
-    const int n = n0 + wn * 32 + l32;
+    const int nl = wn * 32 + l32;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int ml = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
         const float g = yacc[mt][0][r], u = yacc[mt][1][r];
-        const float h = g / (1.f + __expf(-g)) * u;
-        if (m < M && n < NI) Y[(int64_t)m * NI + n] = (uint16_t)cvt_bf16x2(h, 0.f);
+        so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(g / (1.f + __expf(-g)) * u, 0.f);
       }
   } else {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int n = n0 + wn * 64 + nt * 32 + l32;
+        const int nl = wn * 64 + nt * 32 + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (m < M && n < N) Y[(int64_t)m * N + n] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
+          const int ml = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
         }
       }
+  }
+  __syncthreads();
+  constexpr int kChunks = (SWIGLU ? BN / 2 : BN) / 8;   // 16-byte pieces per row
+  const bool vec_ok = (NI & 7) == 0;
+#pragma unroll 4
+  for (int c = tid; c < BM * kChunks; c += kThreads) {
+    const int ml = c / kChunks, cn = c - ml * kChunks;
+    const int m = m0 + ml, n = n0 + cn * 8;
+    if (m >= M || n >= NI) continue;
+    const u32x4 o = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(so) +
+                                                    ml * kPitch + cn * 16);
+    uint16_t* py = Y + (int64_t)m * NI + n;
+    if (vec_ok && n + 7 < NI) {
+      *reinterpret_cast<u32x4*>(py) = o;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (n + j < NI) py[j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+    }
   }
 }
 
