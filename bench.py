@@ -193,9 +193,17 @@ def bench_gemms(qg, torch, dev, stream):
     from synthetic import workload_case
     out = {}
 
-    def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
+    def timed(fn, reps, warm_s=0.05):
+        # untimed warm-up of at least warm_s: after the host-side set-up
+        # between cases the clocks need some tens of milliseconds of load to
+        # come back up, and a single warm-up call leaves the first timed
+        # launches slow
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= warm_s:
+                break
         st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         st.record()
         for _ in range(reps):

@@ -13,17 +13,20 @@
 // scale, so 2^(ea + eb) is applied inside the matrix core and the epilogue
 // only rounds.
 //
-// Tiling: a 256-thread workgroup owns a 256x256 output tile and its 4 waves a
-// 128x128 quarter each (4x4 tiles of v_mfma_scale_f32_32x32x64_f8f6f4, 256
-// fp32 accumulators per lane in the AGPRs).
+// Tiling: a 512-thread workgroup owns a 256x256 output tile and its 8 waves
+// a 128 (tokens) x 64 (channels) piece each (2x4 tiles of
+// v_mfma_scale_f32_32x32x64_f8f6f4, 128 fp32 accumulators per lane), two
+// waves per SIMD so that one wave's fragment reads and barrier waits hide
+// behind the other's matrix work.
 //
 // Operand pipeline: a k-step covers 64 bytes of every operand row (64 FP8 or
 // 128 FP4 codes).  Operand tiles go from HBM straight into LDS with buffer
-// loads that write LDS (no VGPR round trip), into a ring of 4 stages, so the
-// loads of k-step k + 4 are issued three k-steps before they are needed.  One
-// barrier per k-step: it certifies that stage k + 1 has landed and that
-// every wave has finished reading stage k, which is then refilled.  During
-// k-step k the matrix cores work on fragments already in registers while the
+// loads that write LDS (no VGPR round trip), into a ring of 4 stages; the
+// loads of k-steps k + 3 and k + 4 go out together at odd k.  One barrier
+// per k-step: it certifies that stage k + 1 has landed and that every wave
+// has finished reading the stages of k - 1 and k (whose fragments are
+// already in registers), which may then be refilled.  During k-step k
+// the matrix cores work on fragments already in registers while the
 // fragments of k-step k + 1 are read from LDS.  The compiler does not track
 // the LDS writes of these loads, so the waits for them are explicit.
 // Within a 64-byte row the four 16-byte chunks are stored XOR-swizzled by
