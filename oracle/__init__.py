@@ -18,7 +18,14 @@ page title and section) as slow, direct numpy / pure-Python code:
   dynamic per-token activations).
 * ``mx``       -- OCP MXFP4: 32-element blocks, shared E8M0 exponent, E2M1 codes.
 * ``gemm``     -- fp64 reference products of the dequantized operands, the
-  relative Frobenius error metric, and a pure-Python brute-force product.
+  relative Frobenius error metric, a pure-Python brute-force product, SiLU
+  and the SwiGLU reference over the quantized gate+up concatenation.
+* ``norm``     -- LayerNorm / RMSNorm followed by per-row dynamic
+  quantization.
+* ``smooth``   -- SmoothQuant channel statistics, smoothing factors and the
+  quantization of smoothed operands.
+* ``kvcache``  -- FP8 E4M3 KV-cache quantization (per token and head, or
+  static per channel) into a paged cache through a slot mapping.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
 other than itself (values printed on the pages, a library routine, exact
@@ -26,4 +33,4 @@ rational arithmetic, closed forms, invariants or brute force); no function is
 parity-unpinned.
 """
 
-from . import formats, intquant, fp8, mx, gemm  # noqa: F401
+from . import formats, intquant, fp8, mx, gemm, norm, smooth, kvcache  # noqa: F401
