@@ -14,7 +14,10 @@
  *          max|x|/127 with clip +-127, asymmetric scale (max-min)/255 with
  *          zero point round(-min/s) and clip [0,255]; dequantization fused
  *          into the GEMM), 1.3 (group-wise INT4, group 128, W4A16 decode is
- *          HBM bound), 1.4 (FP8 E4M3 with an fp32 scale tensor).
+ *          HBM bound), 1.4 (FP8 E4M3 with an fp32 scale tensor), 1.5
+ *          (SmoothQuant factor and folding), 1.6 (FP8 KV-cache
+ *          quantization, per token or per channel), 4.4 (normalization +
+ *          quantization fusion), 4.6 (GEMM + activation fusion).
  *   [L6]   《第 6 课：量化源码走读》 section 2 (eight INT4 codes per int32;
  *          W4A16 dequantizes inside the GEMM; W8A8/FP8 quantizes activations
  *          dynamically; figure 6-2 Out = acc * scale_x * scale_w; micro-block
@@ -24,7 +27,10 @@
  *   [MX]   《大模型量化推理引擎全景大复盘》 section 2 eq. 3 (32 four-bit
  *          elements share one E8M0 exponent), section 3 code (shared scale
  *          2^ceil(log2(max|x|/6))).
- *   [CH1]  《第 1 章：推理加速全景》 section 4.1 (uniform quantization math).
+ *   [CH1]  《第 1 章：推理加速全景》 section 4.1 (uniform quantization math),
+ *          section 4.3 (SmoothQuant: X W = (X diag(s)^-1)(diag(s) W),
+ *          s_j = max|X_j|^alpha / max|W_j|^(1-alpha)).
+ *   [Q&A] also its KV-cache section (keys per channel, values per token).
  *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -34,7 +40,8 @@
  *     enqueued and a status other than QG_OK is returned.  QG_ERR_HIP reports
  *     a failed kernel launch (hipGetLastError after the launch).
  *   - Every data pointer must be 16-byte aligned (QG_ERR_ALIGN otherwise);
- *     128-bit loads and stores are used throughout.
+ *     128-bit loads and stores are used throughout.  (qg_kv_cache_store
+ *     states its own, smaller requirements for its cache-side pointers.)
  *   - round() is round-half-to-even; x/s is one IEEE fp32 division by the
  *     scale as stored; a scale that is zero (an all-zero group) is stored as 1.
  *   - Calls are stateless and re-entrant; calls on different streams may run
@@ -188,6 +195,90 @@ qg_status qg_qgemm(qg_format wfmt, qg_format afmt,
 qg_status qg_qgemm_swiglu(qg_format wfmt, qg_format afmt, const void* a, int64_t M,
                           const void* wcodes, const void* wscales, const void* wzeros,
                           int64_t N2, int64_t K, int64_t group, void* h, void* stream);
+
+/*
+ * qg_channel_absmax -- per-channel statistics for calibration ([CH1]
+ * section 4.3; [SRV] 1.5 per_channel_max): absmax[k] = max over rows of
+ * |src[r][k]|, exact.
+ *   src         [rows][K] of src_dtype (QG_BF16 or QG_F32); K % 8 == 0.
+ *   accumulate  0: absmax is overwritten; 1: absmax holds a running maximum
+ *               (non-negative floats, e.g. of earlier calibration batches)
+ *               and is raised where this batch is larger.
+ *   absmax      fp32 [K].
+ * A NaN in a column gives a NaN maximum.  Overlapping calls on one absmax
+ * race only in order, not in result (the update is an atomic max).
+ * Errors: QG_ERR_GEOMETRY, QG_ERR_FORMAT, QG_ERR_NULL, QG_ERR_ALIGN,
+ * QG_ERR_HIP.
+ */
+qg_status qg_channel_absmax(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
+                            int accumulate, float* absmax, void* stream);
+
+/*
+ * qg_smooth_scales -- SmoothQuant factors ([CH1] section 4.3; [SRV] 1.5):
+ * smooth[j] = act_absmax[j]^alpha / w_absmax[j]^(1 - alpha), evaluated in
+ * fp64 and rounded once to fp32; 1 where a statistic is zero (or NaN) or the
+ * factor is not a positive normal fp32 value.
+ *   act_absmax  fp32 [K], channel maxima of calibration activations.
+ *   w_absmax    fp32 [K], channel maxima of the weights (column maxima of
+ *               W [N][K]).
+ *   alpha       migration strength in [0, 1] (QG_ERR_GEOMETRY otherwise).
+ *   smooth      fp32 [K].
+ */
+qg_status qg_smooth_scales(const float* act_absmax, const float* w_absmax, float alpha, int64_t K,
+                           float* smooth, void* stream);
+
+/*
+ * qg_quantize_pack_smooth -- qg_quantize_pack of the smoothed operand
+ * ([CH1] section 4.3; [SRV] 1.5: W_hat = W * s offline, X_hat = X / s).
+ * Element (r, k) is first multiplied by smooth[k] (divide = 0: weights,
+ * W diag(s)) or divided by it (divide = 1: activations, X diag(s)^-1), one
+ * fp32 rounding, then quantized exactly as qg_quantize_pack does (same
+ * formats, groups, outputs and errors).  The smoothed operand is never
+ * written.  smooth: fp32 [K], positive and finite; the smoothed values must
+ * stay finite.
+ */
+qg_status qg_quantize_pack_smooth(qg_format fmt, const void* src, qg_dtype src_dtype,
+                                  int64_t rows, int64_t K, int64_t group, const float* smooth,
+                                  int divide, void* codes, void* scales, void* zeros,
+                                  void* stream);
+
+/*
+ * qg_channel_scales -- static per-channel scales from calibration maxima
+ * ([SRV] 1.6 per-channel granularity): scales[i] = absmax[i] / qmax (one
+ * fp32 division), 1 where that is zero.  For FP8 E4M3 KV channels qmax is
+ * 448.  Errors: QG_ERR_GEOMETRY (n < 1, qmax not positive and finite),
+ * QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_channel_scales(const float* absmax, int64_t n, float qmax, float* scales,
+                            void* stream);
+
+/*
+ * qg_kv_cache_store -- FP8 E4M3 quantization of new keys or values into a
+ * paged cache ([SRV] 1.6; [Q&A] KV-cache section).
+ *   x            [tokens][heads][head_dim] of x_dtype (QG_BF16 or QG_F32),
+ *                16-byte aligned; tokens may be 0 (nothing is enqueued).
+ *   head_dim     a multiple of 8 in [8, 512].
+ *   slot_mapping int64 [tokens], 8-byte aligned: token t is written to slot
+ *                slot_mapping[t]; a slot outside [0, num_slots) (negative
+ *                marks padding) is skipped.  The slots of one call must be
+ *                distinct.
+ *   channel_scales  NULL: per token and head, scale = max_d |x[t][h][d]| /
+ *                448 (1 when zero), written to cache_scales.  Otherwise fp32
+ *                [heads][head_dim] static scales (16-byte aligned, e.g. from
+ *                qg_channel_absmax and qg_channel_scales over calibration
+ *                keys); codes of values beyond the calibrated range saturate
+ *                at +-448, and cache_scales must be NULL.
+ *   cache_codes  uint8 [num_slots][heads][head_dim], 8-byte aligned; E4M3
+ *                codes of x / scale (one fp32 division), ties to even.
+ *   cache_scales fp32 [num_slots][heads], 4-byte aligned (per-token mode).
+ * Inputs must be finite.  Errors: QG_ERR_GEOMETRY, QG_ERR_FORMAT,
+ * QG_ERR_UNSUPPORTED (tokens * heads >= 2^31 - 4096), QG_ERR_NULL,
+ * QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_kv_cache_store(const void* x, qg_dtype x_dtype, int64_t tokens, int64_t heads,
+                            int64_t head_dim, const int64_t* slot_mapping, int64_t num_slots,
+                            const float* channel_scales, void* cache_codes, float* cache_scales,
+                            void* stream);
 
 /*
  * qg_mx_quant -- OCP MXFP4 quantization of [rows][K] along K ([MX]; [L6]

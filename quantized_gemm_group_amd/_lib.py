@@ -23,7 +23,9 @@ OK, ERR_GEOMETRY, ERR_ALIGN, ERR_FORMAT, ERR_NULL, ERR_HIP, ERR_UNSUPPORTED = ra
 
 EXPORTS = [
     "qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant", "qg_mx_gemm",
-    "qg_norm_quant", "qg_qgemm_swiglu", "qg_status_str", "qg_last_error", "qg_abi_version",
+    "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth", "qg_channel_absmax",
+    "qg_smooth_scales", "qg_channel_scales", "qg_kv_cache_store", "qg_status_str",
+    "qg_last_error", "qg_abi_version",
 ]
 
 _lib = None
@@ -49,8 +51,15 @@ def load() -> ctypes.CDLL:
     lib.qg_norm_quant.argtypes = [i32, i32, vp, i32, vp, vp, ctypes.c_float, i64, i64, vp, vp,
                                   vp, vp]
     lib.qg_qgemm_swiglu.argtypes = [i32, i32, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
+    lib.qg_quantize_pack_smooth.argtypes = [i32, vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, vp]
+    lib.qg_channel_absmax.argtypes = [vp, i32, i64, i64, i32, vp, vp]
+    lib.qg_smooth_scales.argtypes = [vp, vp, ctypes.c_float, i64, vp, vp]
+    lib.qg_channel_scales.argtypes = [vp, i64, ctypes.c_float, vp, vp]
+    lib.qg_kv_cache_store.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
-                 "qg_mx_gemm", "qg_norm_quant", "qg_qgemm_swiglu"]:
+                 "qg_mx_gemm", "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth",
+                 "qg_channel_absmax", "qg_smooth_scales", "qg_channel_scales",
+                 "qg_kv_cache_store"]:
         getattr(lib, name).restype = i32
     lib.qg_status_str.argtypes = [i32]
     lib.qg_status_str.restype = ctypes.c_char_p

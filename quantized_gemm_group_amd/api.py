@@ -1,4 +1,4 @@
-"""Python binding of the C ABI: same six operations, torch tensors in and out.
+"""Python binding of the C ABI: the same operations, torch tensors in and out.
 
 Marshalling only: every function checks tensor placement and dtypes,
 allocates its outputs with torch on the input's device, and makes ONE call
@@ -205,3 +205,99 @@ def mx_gemm(a_codes: torch.Tensor, a_e8m0: torch.Tensor, b_codes: torch.Tensor,
     _lib.check(lib.qg_mx_gemm(_ptr(a_codes), _ptr(a_e8m0), m, _ptr(b_codes), _ptr(b_e8m0), n,
                               2 * kh, _ptr(y), _stream(dev)))
     return y
+
+
+def _f32_vec(t: torch.Tensor, dev: torch.device, n: int, what: str):
+    if t.dtype != torch.float32 or _dev(t) != dev or t.numel() != n:
+        raise ValueError(f"{what} must be an fp32 tensor of {n} values on the input's device")
+
+
+def quantize_pack_smooth(x: torch.Tensor, smooth: torch.Tensor, fmt: str,
+                         group: int | None = None, divide: bool = False):
+    """quantize_pack of x [rows][K] with column k multiplied by smooth[k]
+    (divide False: weights, W diag(s)) or divided by it (divide True:
+    activations, X diag(s)^-1) first; smooth fp32 [K].  Same outputs as
+    quantize_pack."""
+    lib = _lib.load()
+    dev = _dev(x)
+    rows, k = x.shape
+    _f32_vec(smooth, dev, k, "smooth")
+    group = default_group(fmt, k) if group is None else group
+    if group <= 0 or k % group:
+        raise ValueError("invalid quantization geometry: group must divide K")
+    cshape, cdt, sdt = _code_shapes(fmt, rows, k, group)
+    codes = torch.empty(cshape, dtype=cdt, device=dev)
+    scales = torch.empty((rows, k // group), dtype=sdt, device=dev)
+    zeros = torch.empty_like(scales) if fmt in _ASYM else None
+    _lib.check(lib.qg_quantize_pack_smooth(FORMATS[fmt], _ptr(x), _src_dtype(x), rows, k, group,
+                                           _ptr(smooth), 1 if divide else 0, _ptr(codes),
+                                           _ptr(scales), _ptr(zeros), _stream(dev)))
+    return codes, scales, zeros
+
+
+def channel_absmax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-column max |x| over the rows of x [rows][K] (bf16 or fp32), fp32
+    [K].  With ``out`` given it holds a running maximum (earlier calibration
+    batches) that is raised in place."""
+    lib = _lib.load()
+    dev = _dev(x)
+    rows, k = x.shape
+    acc = out is not None
+    if acc:
+        _f32_vec(out, dev, k, "out")
+    else:
+        out = torch.empty((k,), dtype=torch.float32, device=dev)
+    _lib.check(lib.qg_channel_absmax(_ptr(x), _src_dtype(x), rows, k, 1 if acc else 0, _ptr(out),
+                                     _stream(dev)))
+    return out
+
+
+def smooth_scales(act_absmax: torch.Tensor, w_absmax: torch.Tensor, alpha: float = 0.5):
+    """SmoothQuant factors s = act_absmax^alpha / w_absmax^(1 - alpha), fp32 [K]."""
+    lib = _lib.load()
+    dev = _dev(act_absmax)
+    k = act_absmax.numel()
+    _f32_vec(act_absmax, dev, k, "act_absmax")
+    _f32_vec(w_absmax, dev, k, "w_absmax")
+    s = torch.empty((k,), dtype=torch.float32, device=dev)
+    _lib.check(lib.qg_smooth_scales(_ptr(act_absmax), _ptr(w_absmax), ctypes.c_float(alpha), k,
+                                    _ptr(s), _stream(dev)))
+    return s
+
+
+def channel_scales(absmax: torch.Tensor, qmax: float = 448.0) -> torch.Tensor:
+    """Static per-channel scales absmax / qmax (1 where zero), same shape."""
+    lib = _lib.load()
+    dev = _dev(absmax)
+    if absmax.dtype != torch.float32:
+        raise ValueError("absmax must be fp32")
+    s = torch.empty_like(absmax)
+    _lib.check(lib.qg_channel_scales(_ptr(absmax), absmax.numel(), ctypes.c_float(qmax), _ptr(s),
+                                     _stream(dev)))
+    return s
+
+
+def kv_cache_store(x: torch.Tensor, slot_mapping: torch.Tensor, cache_codes: torch.Tensor,
+                   cache_scales: torch.Tensor | None = None,
+                   channel_scales: torch.Tensor | None = None) -> None:
+    """FP8 E4M3 quantization of x [tokens][heads][head_dim] (bf16 or fp32)
+    into the paged cache in place: token t goes to slot slot_mapping[t]
+    (int64; slots outside the cache are skipped).  Per token and head with
+    cache_scales fp32 [slots][heads], or with static channel_scales fp32
+    [heads][head_dim]; cache_codes uint8 [slots][heads][head_dim]."""
+    lib = _lib.load()
+    dev = _dev(x)
+    t, h, d = x.shape
+    if slot_mapping.dtype != torch.int64 or _dev(slot_mapping) != dev or slot_mapping.numel() != t:
+        raise ValueError("slot_mapping must be an int64 tensor of one slot per token")
+    if (cache_codes.dtype != torch.uint8 or _dev(cache_codes) != dev or cache_codes.dim() != 3
+            or tuple(cache_codes.shape[1:]) != (h, d)):
+        raise ValueError("cache_codes must be uint8 [slots][heads][head_dim] on the device")
+    slots = cache_codes.shape[0]
+    if cache_scales is not None:
+        _f32_vec(cache_scales, dev, slots * h, "cache_scales")
+    if channel_scales is not None:
+        _f32_vec(channel_scales, dev, h * d, "channel_scales")
+    _lib.check(lib.qg_kv_cache_store(_ptr(x), _src_dtype(x), t, h, d, _ptr(slot_mapping), slots,
+                                     _ptr(channel_scales), _ptr(cache_codes), _ptr(cache_scales),
+                                     _stream(dev)))

@@ -4,6 +4,7 @@
 // call, so an invalid call enqueues nothing and touches no device state.  The
 // library allocates nothing and never synchronizes.
 
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 
@@ -30,6 +31,8 @@ qg_status from_hip(hipError_t e) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool is_quant_fmt(qg_format f) {
   return f == QG_INT4_SYM || f == QG_INT4_ASYM || f == QG_INT8_SYM || f == QG_INT8_ASYM ||
@@ -95,7 +98,100 @@ qg_status qg_quantize_pack(qg_format fmt, const void* src, qg_dtype src_dtype, i
   if (!src) return fail(QG_ERR_NULL, "quantize_pack: src is NULL");
   if (!aligned16(src)) return fail(QG_ERR_ALIGN, "quantize_pack: src must be 16-byte aligned");
   return from_hip(qg::launch_quantize(fmt, src, src_dtype, rows, K, group, codes, scales, zeros,
-                                      (hipStream_t)stream));
+                                      nullptr, false, (hipStream_t)stream));
+}
+
+qg_status qg_quantize_pack_smooth(qg_format fmt, const void* src, qg_dtype src_dtype,
+                                  int64_t rows, int64_t K, int64_t group, const float* smooth,
+                                  int divide, void* codes, void* scales, void* zeros,
+                                  void* stream) {
+  if (!is_quant_fmt(fmt)) return fail(QG_ERR_FORMAT, "quantize_pack_smooth: unknown format");
+  if (src_dtype != QG_BF16 && src_dtype != QG_F32)
+    return fail(QG_ERR_FORMAT, "quantize_pack_smooth: source dtype must be bf16 or f32");
+  if (divide != 0 && divide != 1)
+    return fail(QG_ERR_GEOMETRY, "quantize_pack_smooth: divide must be 0 or 1");
+  qg_status st = check_quant_operand(fmt, rows, K, group, codes, scales, zeros);
+  if (st != QG_OK) return st;
+  if (K % 8 != 0) return fail(QG_ERR_GEOMETRY, "quantize_pack_smooth: K must be a multiple of 8");
+  if (K / 8 > 0x7fffff00LL) return fail(QG_ERR_UNSUPPORTED, "quantize_pack_smooth: K too large");
+  if (!src || !smooth) return fail(QG_ERR_NULL, "quantize_pack_smooth: src and smooth are required");
+  if (!aligned16(src) || !aligned16(smooth))
+    return fail(QG_ERR_ALIGN, "quantize_pack_smooth: src and smooth must be 16-byte aligned");
+  return from_hip(qg::launch_quantize(fmt, src, src_dtype, rows, K, group, codes, scales, zeros,
+                                      smooth, divide == 1, (hipStream_t)stream));
+}
+
+qg_status qg_channel_absmax(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
+                            int accumulate, float* absmax, void* stream) {
+  if (src_dtype != QG_BF16 && src_dtype != QG_F32)
+    return fail(QG_ERR_FORMAT, "channel_absmax: source dtype must be bf16 or f32");
+  if (rows < 1 || K < 8 || K % 8 != 0)
+    return fail(QG_ERR_GEOMETRY, "channel_absmax: rows >= 1 and K a positive multiple of 8");
+  if (accumulate != 0 && accumulate != 1)
+    return fail(QG_ERR_GEOMETRY, "channel_absmax: accumulate must be 0 or 1");
+  if (K / 8 > 64LL * 0x7fffffffLL)
+    return fail(QG_ERR_UNSUPPORTED, "channel_absmax: K too large");
+  if (!src || !absmax) return fail(QG_ERR_NULL, "channel_absmax: src and absmax are required");
+  if (!aligned16(src) || !aligned16(absmax))
+    return fail(QG_ERR_ALIGN, "channel_absmax: pointers must be 16-byte aligned");
+  return from_hip(qg::launch_channel_absmax(src, src_dtype, rows, K, accumulate == 1, absmax,
+                                            (hipStream_t)stream));
+}
+
+qg_status qg_smooth_scales(const float* act_absmax, const float* w_absmax, float alpha, int64_t K,
+                           float* smooth, void* stream) {
+  if (K < 1) return fail(QG_ERR_GEOMETRY, "smooth_scales: K must be positive");
+  if (!(alpha >= 0.f && alpha <= 1.f))
+    return fail(QG_ERR_GEOMETRY, "smooth_scales: alpha must lie in [0, 1]");
+  if (!act_absmax || !w_absmax || !smooth)
+    return fail(QG_ERR_NULL, "smooth_scales: act_absmax, w_absmax and smooth are required");
+  if (!aligned16(act_absmax) || !aligned16(w_absmax) || !aligned16(smooth))
+    return fail(QG_ERR_ALIGN, "smooth_scales: pointers must be 16-byte aligned");
+  return from_hip(qg::launch_smooth_scales(act_absmax, w_absmax, alpha, K, smooth,
+                                           (hipStream_t)stream));
+}
+
+qg_status qg_channel_scales(const float* absmax, int64_t n, float qmax, float* scales,
+                            void* stream) {
+  if (n < 1) return fail(QG_ERR_GEOMETRY, "channel_scales: n must be positive");
+  if (!(qmax > 0.f && qmax <= 3.4e38f))
+    return fail(QG_ERR_GEOMETRY, "channel_scales: qmax must be positive and finite");
+  if (!absmax || !scales) return fail(QG_ERR_NULL, "channel_scales: absmax and scales are required");
+  if (!aligned16(absmax) || !aligned16(scales))
+    return fail(QG_ERR_ALIGN, "channel_scales: pointers must be 16-byte aligned");
+  return from_hip(qg::launch_channel_scales(absmax, n, qmax, scales, (hipStream_t)stream));
+}
+
+qg_status qg_kv_cache_store(const void* x, qg_dtype x_dtype, int64_t tokens, int64_t heads,
+                            int64_t head_dim, const int64_t* slot_mapping, int64_t num_slots,
+                            const float* channel_scales, void* cache_codes, float* cache_scales,
+                            void* stream) {
+  if (x_dtype != QG_BF16 && x_dtype != QG_F32)
+    return fail(QG_ERR_FORMAT, "kv_cache_store: source dtype must be bf16 or f32");
+  if (tokens < 0 || heads < 1 || num_slots < 1)
+    return fail(QG_ERR_GEOMETRY, "kv_cache_store: tokens >= 0, heads >= 1 and num_slots >= 1");
+  if (head_dim < 8 || head_dim > 512 || head_dim % 8 != 0)
+    return fail(QG_ERR_GEOMETRY, "kv_cache_store: head_dim a multiple of 8 in [8, 512]");
+  if (tokens * heads > 0x7fffffffLL - 4096 || heads > 0x7fffffffLL / head_dim)
+    return fail(QG_ERR_UNSUPPORTED, "kv_cache_store: tokens * heads must stay below 2^31");
+  if (num_slots > INT64_MAX / (heads * head_dim))
+    return fail(QG_ERR_UNSUPPORTED, "kv_cache_store: cache too large");
+  if (!cache_codes) return fail(QG_ERR_NULL, "kv_cache_store: cache_codes is required");
+  if (tokens > 0 && !slot_mapping) return fail(QG_ERR_NULL, "kv_cache_store: slot_mapping is NULL");
+  if (!channel_scales && !cache_scales)
+    return fail(QG_ERR_NULL, "kv_cache_store: per-token mode needs cache_scales");
+  if (channel_scales && cache_scales)
+    return fail(QG_ERR_NULL, "kv_cache_store: cache_scales must be NULL with channel_scales");
+  if (tokens > 0 && !x) return fail(QG_ERR_NULL, "kv_cache_store: x is NULL");
+  if ((x && !aligned16(x)) || (channel_scales && !aligned16(channel_scales)) ||
+      !aligned_to(cache_codes, 8) || (slot_mapping && !aligned_to(slot_mapping, 8)) ||
+      (cache_scales && !aligned_to(cache_scales, 4)))
+    return fail(QG_ERR_ALIGN, "kv_cache_store: x and channel_scales 16-byte, cache_codes and "
+                              "slot_mapping 8-byte, cache_scales 4-byte aligned");
+  if (tokens == 0) return ok();
+  return from_hip(qg::launch_kv_cache_store(x, x_dtype, tokens, heads, head_dim, slot_mapping,
+                                            num_slots, channel_scales, cache_codes, cache_scales,
+                                            (hipStream_t)stream));
 }
 
 qg_status qg_norm_quant(qg_norm norm, qg_format fmt, const void* src, qg_dtype src_dtype,

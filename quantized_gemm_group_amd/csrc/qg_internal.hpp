@@ -11,9 +11,25 @@
 
 namespace qg {
 
+// smooth: per-column factors [K] folded into the operand before the group
+// statistics (x * s_j, or x / s_j when divide), or null.
 hipError_t launch_quantize(qg_format fmt, const void* src, qg_dtype src_dtype, int64_t rows,
                            int64_t K, int64_t group, void* codes, void* scales, void* zeros,
-                           hipStream_t stream);
+                           const float* smooth, bool divide, hipStream_t stream);
+
+hipError_t launch_channel_absmax(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
+                                 bool accumulate, float* out, hipStream_t stream);
+
+hipError_t launch_smooth_scales(const float* act_absmax, const float* w_absmax, float alpha,
+                                int64_t K, float* smooth, hipStream_t stream);
+
+hipError_t launch_channel_scales(const float* absmax, int64_t n, float qmax, float* scales,
+                                 hipStream_t stream);
+
+hipError_t launch_kv_cache_store(const void* x, qg_dtype x_dtype, int64_t tokens, int64_t heads,
+                                 int64_t head_dim, const int64_t* slot_mapping, int64_t num_slots,
+                                 const float* channel_scales, void* cache_codes,
+                                 float* cache_scales, hipStream_t stream);
 
 hipError_t launch_dequant(qg_format fmt, const void* codes, const void* scales,
                           const void* zeros, int64_t rows, int64_t K, int64_t group, void* dst,

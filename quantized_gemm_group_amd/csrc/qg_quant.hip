@@ -54,6 +54,31 @@ __device__ __forceinline__ void load_vec(const void* src, int64_t vec, float (&v
   }
 }
 
+// SmoothQuant folding (《第 1 章：推理加速全景》 section 4.3; 《推理优化与量化算子深度
+// 技术调研》 section 1.5): column j of the operand is multiplied (weights,
+// W diag(s)) or divided (activations, X diag(s)^-1) by s_j before the group
+// statistics, one fp32 rounding per element.  A null factor pointer leaves
+// the operand as it is.
+struct Smooth {
+  const float* s;    // factors [K], 16-byte aligned, or null
+  int64_t kvecs;     // vecs per row (K / 8)
+  int div;           // 1: x / s_j, 0: x * s_j
+};
+
+// Fold the factors of column vec c (elements 8c .. 8c + 7) into v.
+__device__ __forceinline__ void apply_smooth(float (&v)[8], const Smooth& sm, uint32_t c) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(sm.s) + 2 * (size_t)c;
+  const f32x4 a = p[0], b = p[1];
+  const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  if (sm.div) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] / f[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * f[i];
+  }
+}
+
 struct Stats {
   float amax, lo, hi;
 };
@@ -173,7 +198,8 @@ __global__ __launch_bounds__(kThreads) void quant_wave_kernel(const void* __rest
                                                               int64_t total_vecs, int t_log2,
                                                               void* __restrict__ codes,
                                                               void* __restrict__ scales,
-                                                              void* __restrict__ zeros) {
+                                                              void* __restrict__ zeros,
+                                                              Smooth sm) {
   const int lane = threadIdx.x & 63;
   const int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * 64 * kVpl;
   float v[kVpl][8];
@@ -185,6 +211,16 @@ __global__ __launch_bounds__(kThreads) void quant_wave_kernel(const void* __rest
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    }
+  }
+  if (sm.s) {
+    // column of the wave's first vec once, then 32-bit arithmetic
+    const uint32_t c0 = (uint32_t)(base % sm.kvecs), kv = (uint32_t)sm.kvecs;
+#pragma unroll
+    for (int i = 0; i < kVpl; ++i) {
+      uint32_t c = c0 + 64 * i + lane;
+      if (c >= kv) c %= kv;
+      if (base + 64 * i + lane < total_vecs) apply_smooth(v[i], sm, c);
     }
   }
   const int seg = 1 << t_log2;
@@ -214,7 +250,8 @@ __global__ __launch_bounds__(kThreads) void quant_rowwave_kernel(const void* __r
                                                                  int64_t groups,
                                                                  void* __restrict__ codes,
                                                                  void* __restrict__ scales,
-                                                                 void* __restrict__ zeros) {
+                                                                 void* __restrict__ zeros,
+                                                                 Smooth sm) {
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (g >= groups) return;
@@ -222,6 +259,12 @@ __global__ __launch_bounds__(kThreads) void quant_rowwave_kernel(const void* __r
   float v[VPL][8];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) load_vec<BF16>(src, v0 + 64 * i + lane, v[i]);
+  if (sm.s) {
+    // a group never crosses a row
+    const uint32_t c0 = (uint32_t)(v0 % sm.kvecs);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) apply_smooth(v[i], sm, c0 + 64 * i + lane);
+  }
   Stats st{0.f, __builtin_inff(), -__builtin_inff()};
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
@@ -246,14 +289,17 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const void* __res
                                                                int64_t t_vecs,
                                                                void* __restrict__ codes,
                                                                void* __restrict__ scales,
-                                                               void* __restrict__ zeros) {
+                                                               void* __restrict__ zeros,
+                                                               Smooth sm) {
   __shared__ float red[3][kThreads / 64];
   const int64_t g = blockIdx.x;
   const int64_t v0 = g * t_vecs;
+  const uint32_t c0 = sm.s ? (uint32_t)(v0 % sm.kvecs) : 0u;   // a group never crosses a row
   Stats st{0.f, __builtin_inff(), -__builtin_inff()};
   for (int64_t i = threadIdx.x; i < t_vecs; i += kThreads) {
     float v[8];
     load_vec<BF16>(src, v0 + i, v);
+    if (sm.s) apply_smooth(v, sm, c0 + (uint32_t)i);
     const Stats s = stats_of(v);
     st.amax = __builtin_fmaxf(st.amax, s.amax);
     st.lo = __builtin_fminf(st.lo, s.lo);
@@ -281,6 +327,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const void* __res
   for (int64_t i = threadIdx.x; i < t_vecs; i += kThreads) {
     float v[8];
     load_vec<BF16>(src, v0 + i, v);
+    if (sm.s) apply_smooth(v, sm, c0 + (uint32_t)i);
     quantize_store<K>(v, p, codes, v0 + i);
   }
   if (threadIdx.x == 0) store_params<K>(p, scales, zeros, g);
@@ -398,14 +445,14 @@ inline unsigned blocks_for_vpl(int64_t n) {
 
 template <int K, bool BF16>
 void launch_quant_t(const void* src, int64_t rows, int64_t Kdim, int64_t group, void* codes,
-                    void* scales, void* zeros, hipStream_t stream) {
+                    void* scales, void* zeros, const Smooth& sm, hipStream_t stream) {
   const int64_t t_vecs = group / 8;
   const int64_t total = rows * Kdim / 8;
   if (t_vecs <= 64 && (t_vecs & (t_vecs - 1)) == 0) {
     int t_log2 = 0;
     while ((1LL << t_log2) < t_vecs) ++t_log2;
     hipLaunchKernelGGL((quant_wave_kernel<K, BF16>), dim3(blocks_for_vpl(total)), dim3(kThreads),
-                       0, stream, src, total, t_log2, codes, scales, zeros);
+                       0, stream, src, total, t_log2, codes, scales, zeros, sm);
   } else if (t_vecs % 64 == 0 && t_vecs <= 64 * 16) {
     // groups of 512, 1024, 2048, 4096 or 8192 elements: one wave per group
     // (other multiples of 512 take the workgroup kernel below)
@@ -414,50 +461,51 @@ void launch_quant_t(const void* src, int64_t rows, int64_t Kdim, int64_t group, 
     switch (t_vecs / 64) {
       case 1:
         hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 1>), dim3(blocks), dim3(kThreads), 0,
-                           stream, src, groups, codes, scales, zeros);
+                           stream, src, groups, codes, scales, zeros, sm);
         break;
       case 2:
         hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 2>), dim3(blocks), dim3(kThreads), 0,
-                           stream, src, groups, codes, scales, zeros);
+                           stream, src, groups, codes, scales, zeros, sm);
         break;
       case 4:
         hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 4>), dim3(blocks), dim3(kThreads), 0,
-                           stream, src, groups, codes, scales, zeros);
+                           stream, src, groups, codes, scales, zeros, sm);
         break;
       case 8:
         hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 8>), dim3(blocks), dim3(kThreads), 0,
-                           stream, src, groups, codes, scales, zeros);
+                           stream, src, groups, codes, scales, zeros, sm);
         break;
       case 16:
         hipLaunchKernelGGL((quant_rowwave_kernel<K, BF16, 16>), dim3(blocks), dim3(kThreads), 0,
-                           stream, src, groups, codes, scales, zeros);
+                           stream, src, groups, codes, scales, zeros, sm);
         break;
       default:
         hipLaunchKernelGGL((quant_block_kernel<K, BF16>), dim3((unsigned)groups), dim3(kThreads),
-                           0, stream, src, t_vecs, codes, scales, zeros);
+                           0, stream, src, t_vecs, codes, scales, zeros, sm);
         break;
     }
   } else {
     const int64_t groups = rows * (Kdim / group);
     hipLaunchKernelGGL((quant_block_kernel<K, BF16>), dim3((unsigned)groups), dim3(kThreads), 0,
-                       stream, src, t_vecs, codes, scales, zeros);
+                       stream, src, t_vecs, codes, scales, zeros, sm);
   }
 }
 
 template <bool BF16>
 void launch_quant_fmt(qg_format fmt, const void* src, int64_t rows, int64_t Kdim, int64_t group,
-                      void* codes, void* scales, void* zeros, hipStream_t stream) {
+                      void* codes, void* scales, void* zeros, const Smooth& sm,
+                      hipStream_t stream) {
   switch (fmt) {
     case QG_INT4_SYM:
-      return launch_quant_t<K_INT4_SYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+      return launch_quant_t<K_INT4_SYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, sm, stream);
     case QG_INT4_ASYM:
-      return launch_quant_t<K_INT4_ASYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+      return launch_quant_t<K_INT4_ASYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, sm, stream);
     case QG_INT8_SYM:
-      return launch_quant_t<K_INT8_SYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+      return launch_quant_t<K_INT8_SYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, sm, stream);
     case QG_INT8_ASYM:
-      return launch_quant_t<K_INT8_ASYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+      return launch_quant_t<K_INT8_ASYM, BF16>(src, rows, Kdim, group, codes, scales, zeros, sm, stream);
     default:
-      return launch_quant_t<K_FP8, BF16>(src, rows, Kdim, group, codes, scales, zeros, stream);
+      return launch_quant_t<K_FP8, BF16>(src, rows, Kdim, group, codes, scales, zeros, sm, stream);
   }
 }
 
@@ -666,11 +714,12 @@ namespace {
 
 hipError_t launch_quantize(qg_format fmt, const void* src, qg_dtype src_dtype, int64_t rows,
                            int64_t K, int64_t group, void* codes, void* scales, void* zeros,
-                           hipStream_t stream) {
+                           const float* smooth, bool divide, hipStream_t stream) {
+  const Smooth sm{smooth, K / 8, divide ? 1 : 0};
   if (src_dtype == QG_BF16)
-    launch_quant_fmt<true>(fmt, src, rows, K, group, codes, scales, zeros, stream);
+    launch_quant_fmt<true>(fmt, src, rows, K, group, codes, scales, zeros, sm, stream);
   else
-    launch_quant_fmt<false>(fmt, src, rows, K, group, codes, scales, zeros, stream);
+    launch_quant_fmt<false>(fmt, src, rows, K, group, codes, scales, zeros, sm, stream);
   return hipGetLastError();
 }
 

@@ -18,6 +18,13 @@ Workloads (shapes from the Llama-3-8B and Qwen2.5-72B tables of
 * ``fp8_8192``        M=N=K=8192; 0.1 % of the entries of X scaled x100; seed 4.
 * ``mxfp4_4096x8192`` M=4096, N=K=8192; 1 % of the input channels of W scaled
   x50; seed 5.
+
+Two further generators: ``smoothquant_case`` (activations whose outliers
+sit in 1 % of the input channels, x10, the 5-15x range that
+《第 1 章：推理加速全景》 section 4.3 describes) and ``kv_case`` (keys and
+values of new tokens for a paged cache: keys with outlier channels, as
+《量化与加速》 describes them; a slot mapping through a shuffled block table
+with padding entries).
 """
 
 from __future__ import annotations
@@ -30,7 +37,7 @@ import torch
 __all__ = [
     "rng_for", "normal_weights", "normal_activations", "to_bf16", "bf16_as_f32",
     "scale_input_channels", "scale_random_entries", "Projection", "WORKLOADS",
-    "workload_case", "small_case", "norm_weights",
+    "workload_case", "small_case", "norm_weights", "smoothquant_case", "kv_case",
 ]
 
 
@@ -155,3 +162,41 @@ def small_case(m: int, k: int, n: int, seed: int, w_outlier=(0.0, 1.0), x_outlie
     if x_outlier[0] > 0:
         scale_random_entries(rng, x, *x_outlier)
     return dict(w=w, x=to_bf16(x), k=k, n=n, m=m)
+
+
+def smoothquant_case(m: int, k: int, n: int, seed: int, frac: float = 0.01, mult: float = 10.0):
+    """W fp32 [N][K] ~ N(0, 0.02^2) and X [M][K] ~ N(0, 1) with round(frac*K)
+    input channels of X multiplied by mult, rounded to bf16.  Returns
+    dict(w, x (bf16 torch), outlier_channels)."""
+    rng = rng_for(seed)
+    w = normal_weights(rng, n, k)
+    x = normal_activations(rng, m, k)
+    cnt = int(round(frac * k))
+    idx = np.sort(rng.choice(k, size=cnt, replace=False))
+    x[:, idx] *= np.float32(mult)
+    return dict(w=w, x=to_bf16(x), k=k, n=n, m=m, outlier_channels=idx)
+
+
+def kv_case(tokens: int, heads: int, head_dim: int, num_slots: int, seed: int,
+            block: int = 16, key_outlier=(2, 10.0), padding: int = 0):
+    """Keys and values of `tokens` new tokens, bf16 [tokens][heads][head_dim]
+    ~ N(0, 1), with key_outlier[0] channels of every key head multiplied by
+    key_outlier[1]; and a slot mapping: the tokens fill blocks of `block`
+    slots taken in a shuffled order from the num_slots / block blocks of the
+    cache (distinct slots), then `padding` entries become -1.  Returns
+    dict(k, v (bf16 torch), slots (int64 numpy), key_channels)."""
+    rng = rng_for(seed)
+    kx = rng.standard_normal((tokens, heads, head_dim), dtype=np.float32)
+    vx = rng.standard_normal((tokens, heads, head_dim), dtype=np.float32)
+    ch = np.sort(rng.choice(head_dim, size=key_outlier[0], replace=False))
+    kx[:, :, ch] *= np.float32(key_outlier[1])
+    nblocks = num_slots // block
+    need = -(-tokens // block)
+    if need > nblocks:
+        raise ValueError("cache too small for the tokens")
+    order = rng.permutation(nblocks)[:need]
+    slots = (order[:, None] * block + np.arange(block)[None, :]).reshape(-1)[:tokens]
+    slots = slots.astype(np.int64)
+    if padding:
+        slots[rng.choice(tokens, size=padding, replace=False)] = -1
+    return dict(k=to_bf16(kx), v=to_bf16(vx), slots=slots, key_channels=ch)

@@ -158,3 +158,60 @@ def test_operands_past_32_bit_offsets_are_rejected(lib):
     assert lib.qg_mx_gemm(A16, A16b, 8, A16c, A16d, big * 2, 8192, A16e, None) == _lib.ERR_UNSUPPORTED
     assert lib.qg_qgemv(i4, A16, 1, A16b, A16c, None, 1 << 20, 8192, 128, A16e,
                         None) == _lib.ERR_UNSUPPORTED
+
+
+def test_quantize_pack_smooth_validation(lib):
+    q = lib.qg_quantize_pack_smooth
+    ok = (_lib.INT4_SYM, A16, _lib.F32, 4, 256, 128, A16e, 0, A16b, A16c, None, None)
+    assert q(*ok[:6], None, *ok[7:]) == _lib.ERR_NULL                   # no factors
+    assert q(*ok[:6], MIS, *ok[7:]) == _lib.ERR_ALIGN                   # misaligned factors
+    assert q(*ok[:7], 2, *ok[8:]) == _lib.ERR_GEOMETRY                  # divide not 0/1
+    assert q(_lib.INT4_SYM, A16, _lib.F32, 4, 256, 100, A16e, 0, A16b, A16c, None,
+             None) == _lib.ERR_GEOMETRY
+    assert q(_lib.MXFP4, *ok[1:]) == _lib.ERR_FORMAT
+    assert q(_lib.INT8_ASYM, *ok[1:]) == _lib.ERR_NULL                  # asym needs zeros
+
+
+def test_channel_statistics_validation(lib):
+    a = lib.qg_channel_absmax
+    assert a(A16, _lib.BF16, 0, 256, 0, A16b, None) == _lib.ERR_GEOMETRY
+    assert a(A16, _lib.BF16, 4, 12, 0, A16b, None) == _lib.ERR_GEOMETRY
+    assert a(A16, _lib.BF16, 4, 256, 2, A16b, None) == _lib.ERR_GEOMETRY
+    assert a(A16, 5, 4, 256, 0, A16b, None) == _lib.ERR_FORMAT
+    assert a(None, _lib.BF16, 4, 256, 0, A16b, None) == _lib.ERR_NULL
+    assert a(A16, _lib.BF16, 4, 256, 0, MIS, None) == _lib.ERR_ALIGN
+    s = lib.qg_smooth_scales
+    assert s(A16, A16b, ctypes.c_float(1.5), 64, A16c, None) == _lib.ERR_GEOMETRY
+    assert s(A16, A16b, ctypes.c_float(-0.1), 64, A16c, None) == _lib.ERR_GEOMETRY
+    assert s(A16, A16b, ctypes.c_float(float("nan")), 64, A16c, None) == _lib.ERR_GEOMETRY
+    assert s(A16, A16b, ctypes.c_float(0.5), 0, A16c, None) == _lib.ERR_GEOMETRY
+    assert s(A16, None, ctypes.c_float(0.5), 64, A16c, None) == _lib.ERR_NULL
+    c = lib.qg_channel_scales
+    assert c(A16, 64, ctypes.c_float(0.0), A16b, None) == _lib.ERR_GEOMETRY
+    assert c(A16, 64, ctypes.c_float(float("inf")), A16b, None) == _lib.ERR_GEOMETRY
+    assert c(A16, 0, ctypes.c_float(448.0), A16b, None) == _lib.ERR_GEOMETRY
+    assert c(MIS, 64, ctypes.c_float(448.0), A16b, None) == _lib.ERR_ALIGN
+
+
+def test_kv_cache_store_validation(lib):
+    k = lib.qg_kv_cache_store
+    # x, dtype, tokens, heads, head_dim, slots, num_slots, channel_scales, codes, scales
+    tok = (A16, _lib.BF16, 4, 8, 128, A16b, 64, None, A16c, A16d, None)
+    ch = (A16, _lib.BF16, 4, 8, 128, A16b, 64, A16e, A16c, None, None)
+    assert k(*tok[:4], 100, *tok[5:]) == _lib.ERR_GEOMETRY             # head_dim % 8
+    assert k(*tok[:4], 1024, *tok[5:]) == _lib.ERR_GEOMETRY            # head_dim > 512
+    assert k(*tok[:3], 0, *tok[4:]) == _lib.ERR_GEOMETRY               # heads
+    assert k(*tok[:6], 0, *tok[7:]) == _lib.ERR_GEOMETRY               # num_slots
+    assert k(*tok[:2], -1, *tok[3:]) == _lib.ERR_GEOMETRY              # tokens
+    assert k(*tok[:9], None, None) == _lib.ERR_NULL                     # per token needs scales
+    assert k(*ch[:9], A16d, None) == _lib.ERR_NULL                      # both scale kinds
+    assert k(*tok[:5], None, *tok[6:]) == _lib.ERR_NULL                 # no slot mapping
+    assert k(*tok[:2], 1 << 28, 16, *tok[4:]) == _lib.ERR_UNSUPPORTED   # tokens * heads >= 2^31
+    assert k(*tok[:5], vp(0x2004), *tok[6:]) == _lib.ERR_ALIGN          # slots 8-byte
+    assert k(*tok[:8], vp(0x3004), *tok[9:]) == _lib.ERR_ALIGN          # codes 8-byte
+    assert k(*tok[:9], vp(0x4002), None) == _lib.ERR_ALIGN              # scales 4-byte
+    assert k(*ch[:7], vp(0x5008), *ch[8:]) == _lib.ERR_ALIGN            # channel scales 16
+    assert k(A16, 9, *tok[2:]) == _lib.ERR_FORMAT
+    # no tokens: valid, nothing is enqueued (no HIP call is made)
+    assert k(None, _lib.BF16, 0, 8, 128, A16b, 64, None, A16c, A16d, None) == _lib.OK
+    assert k(None, _lib.BF16, 0, 8, 128, None, 64, None, A16c, A16d, None) == _lib.OK
