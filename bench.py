@@ -303,6 +303,77 @@ def bench_gemv_4096(qg, torch, dev, stream):
     return dict(us=t * 1e6, gbs=b / t / 1e9, frac=b / t / 1e9 / HBM_PEAK_GBS, copies=r)
 
 
+# ------------------------------------------------ SmoothQuant and KV cache
+
+def bench_smooth_kv(qg, torch, dev, stream):
+    """HBM-bound steps of the SmoothQuant and FP8 KV-cache rows, each replayed
+    from a HIP graph over input copies totalling more than twice the
+    last-level cache (algorithmic bytes / time)."""
+    from synthetic import kv_case, smoothquant_case
+    out = {}
+
+    def rate(fn_of_copy, copies, nbytes, name, **extra):
+        def f():
+            for i in range(copies):
+                fn_of_copy(i)
+        g = graph_of(f, stream)
+        time_graph(g, stream)
+        t = time_graph(g, stream, reps=3) / (3 * copies)
+        out[name] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, frac=nbytes / t / 1e9 / HBM_PEAK_GBS,
+                         **extra)
+        del g
+
+    # 8192 x 8192 activations with 1 % outlier channels (bf16), weights fp32
+    c = smoothquant_case(8192, 8192, 8192, seed=6)
+    k = 8192
+    xs = [c["x"].to(dev)]
+    xs += [xs[0].clone() for _ in range(-(-2 * MALL_BYTES // xs[0].nbytes) - 1)]
+    ws = [torch.from_numpy(c["w"]).to(dev)]
+    ws += [ws[0].clone() for _ in range(-(-2 * MALL_BYTES // ws[0].nbytes) - 1)]
+    del c
+    stat_x = torch.empty(k, dtype=torch.float32, device=dev)
+    stat_w = torch.empty(k, dtype=torch.float32, device=dev)
+    rate(lambda i: qg.channel_absmax(xs[i], out=stat_x), len(xs), xs[0].nbytes + 4 * k,
+         "smoothquant_channel_absmax_x_8192_bf16")
+    rate(lambda i: qg.channel_absmax(ws[i], out=stat_w), len(ws), ws[0].nbytes + 4 * k,
+         "smoothquant_channel_absmax_w_8192_f32")
+    s = qg.smooth_scales(qg.channel_absmax(xs[0]), qg.channel_absmax(ws[0]), 0.5)
+    xbytes = xs[0].nbytes + 8192 * k + 4 * 8192 + 4 * k
+    rate(lambda i: qg.quantize_pack_smooth(xs[i], s, "int8_sym", divide=True), len(xs), xbytes,
+         "smoothquant_int8_token_quant_x_8192")
+    rate(lambda i: qg.quantize_pack(xs[i], "int8_sym"), len(xs), xbytes - 4 * k,
+         "int8_token_quant_x_8192_unsmoothed")
+    del xs
+    rate(lambda i: qg.quantize_pack_smooth(ws[i], s, "int8_sym"), len(ws),
+         ws[0].nbytes + 8192 * k + 4 * 8192 + 4 * k, "smoothquant_int8_channel_quant_w_8192")
+    del ws, s
+    torch.cuda.empty_cache()
+
+    # FP8 KV cache: a Llama-3-8B prefill chunk (8192 tokens, 8 KV heads x 128)
+    # into a 16-token paged cache of 32768 slots, values per token, keys
+    # with static per-channel scales; and one decode step of 256 tokens
+    t, h, d, slots = 8192, 8, 128, 32768
+    c = kv_case(t, h, d, slots, seed=13)
+    ks = [c["k"].to(dev)]
+    ks += [ks[0].clone() for _ in range(-(-2 * MALL_BYTES // ks[0].nbytes) - 1)]
+    vs = [c["v"].to(dev)] + [c["v"].to(dev) for _ in range(len(ks) - 1)]
+    sl = torch.from_numpy(c["slots"]).to(dev)
+    cache = torch.zeros((slots, h, d), dtype=torch.uint8, device=dev)
+    cscale = torch.zeros(slots * h, dtype=torch.float32, device=dev)
+    chs = qg.channel_scales(qg.channel_absmax(ks[0].reshape(t, h * d)), 448.0).reshape(h, d)
+    nb = ks[0].nbytes + t * h * d + sl.nbytes
+    rate(lambda i: qg.kv_cache_store(vs[i], sl, cache, cscale), len(vs), nb + 4 * t * h,
+         "kv_cache_store_per_token_llama3_8b_8192tok", tokens=t)
+    rate(lambda i: qg.kv_cache_store(ks[i], sl, cache, None, chs), len(ks), nb + 4 * h * d,
+         "kv_cache_store_per_channel_llama3_8b_8192tok", tokens=t)
+    kd, sd = ks[0][:256].contiguous(), sl[:256].contiguous()
+    rate(lambda i: qg.kv_cache_store(kd, sd, cache, cscale), 64, kd.nbytes + 256 * h * d + 2048
+         + 4 * 256 * h, "kv_cache_store_per_token_decode_256tok", tokens=256)
+    del ks, vs, sl, cache, cscale, chs, kd, sd
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(layer, min_seconds=10.0, max_passes=12):
@@ -472,6 +543,8 @@ def main():
         detail["gemv_4096"] = bench_gemv_4096(qg, torch, dev, stream)
         log("GEMMs ...")
         detail.update(bench_gemms(qg, torch, dev, stream))
+        log("SmoothQuant and KV cache ...")
+        detail.update(bench_smooth_kv(qg, torch, dev, stream))
 
     cpu = None
     if not args.no_cpu_baseline:
