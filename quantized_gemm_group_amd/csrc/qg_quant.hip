@@ -99,13 +99,27 @@ struct Params {
   float z;          // stored zero point, as fp32 (0 for symmetric kinds)
   uint32_t s_bits;  // fp16 bits (INT4) -- unused for fp32 storage
   uint32_t z_bits;
+  double r;         // 1 / s, correctly rounded fp64
 };
+
+// fl32(x / s) for the group's stored scale s, without the fp32 division
+// sequence per element: r = 1/s in fp64 (one correctly rounded fp64
+// division per group), then x * r in fp64, rounded once to fp32.  The
+// quotient of two 24-bit significands lies at least 2^-49 (relative) away
+// from every fp32 rounding midpoint, and the fp64 product is within 2^-52 of
+// the quotient, so for a normal fp32 quotient the result is the correctly
+// rounded x / s.  A quotient in the fp32 subnormal range may differ in its
+// last bit, which no code decision sees (such values quantize to zero in
+// every format, sign kept).
+__device__ __forceinline__ float quot(float x, const Params& p) {
+  return (float)((double)x * p.r);
+}
 
 // Scale (and zero point) of one group, rounded to the storage dtype first;
 // a stored scale of 0 becomes 1.
 template <int K>
 __device__ __forceinline__ Params make_params(const Stats& st) {
-  Params p{1.f, 0.f, 0x3C00u, 0u};
+  Params p{1.f, 0.f, 0x3C00u, 0u, 1.0};
   if constexpr (K == K_INT4_SYM) {
     uint16_t b;
     float s = f32_to_f16_sat(st.amax / 7.0f, &b);
@@ -129,6 +143,7 @@ __device__ __forceinline__ Params make_params(const Stats& st) {
     float s = st.amax / 448.0f;
     p.s = (s == 0.f) ? 1.f : s;
   }
+  p.r = 1.0 / (double)p.s;
   return p;
 }
 
@@ -154,7 +169,7 @@ __device__ __forceinline__ void quantize_store(const float (&v)[8], const Params
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float q = __builtin_rintf(v[i] / p.s) + p.z;       // round, then add z
+      float q = __builtin_rintf(quot(v[i], p)) + p.z;    // round, then add z
       q = __builtin_fminf(__builtin_fmaxf(q, lo), hi);    // then clip
       word |= ((uint32_t)(int)q & 0xFu) << (4 * i);
     }
@@ -164,10 +179,10 @@ __device__ __forceinline__ void quantize_store(const float (&v)[8], const Params
     // 448 (1 + 2^-23) by construction of s, which rounds to 448, so the
     // saturating and the plain conversion agree
     uint2 out;
-    out.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] / p.s, v[1] / p.s, 0u, false);
-    out.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] / p.s, v[3] / p.s, out.x, true);
-    out.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] / p.s, v[5] / p.s, 0u, false);
-    out.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] / p.s, v[7] / p.s, out.y, true);
+    out.x = __builtin_amdgcn_cvt_pk_fp8_f32(quot(v[0], p), quot(v[1], p), 0u, false);
+    out.x = __builtin_amdgcn_cvt_pk_fp8_f32(quot(v[2], p), quot(v[3], p), out.x, true);
+    out.y = __builtin_amdgcn_cvt_pk_fp8_f32(quot(v[4], p), quot(v[5], p), 0u, false);
+    out.y = __builtin_amdgcn_cvt_pk_fp8_f32(quot(v[6], p), quot(v[7], p), out.y, true);
     reinterpret_cast<uint2*>(codes)[vec] = out;
   } else {
     uint32_t b[8];
@@ -176,7 +191,7 @@ __device__ __forceinline__ void quantize_store(const float (&v)[8], const Params
       {
         constexpr float lo = (K == K_INT8_SYM) ? -127.f : 0.f;
         constexpr float hi = (K == K_INT8_SYM) ? 127.f : 255.f;
-        float q = __builtin_rintf(v[i] / p.s) + p.z;
+        float q = __builtin_rintf(quot(v[i], p)) + p.z;
         q = __builtin_fminf(__builtin_fmaxf(q, lo), hi);
         b[i] = (uint32_t)(int)q & 0xFFu;
       }

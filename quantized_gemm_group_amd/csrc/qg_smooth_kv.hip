@@ -195,8 +195,13 @@ __global__ __launch_bounds__(256) void kv_store_kernel(const void* __restrict__ 
     am = wave_max_seg(am, 1 << p_log2);
     s = am / 448.0f;
     if (s == 0.f) s = 1.f;
+    // fl32(x / s) as fl32(x * (1/s)_fp64): exact for a normal fp32 quotient
+    // (a quotient of 24-bit significands keeps 2^-49 of relative distance
+    // from every fp32 rounding midpoint, the fp64 product errs by < 2^-52);
+    // subnormal quotients encode to zero either way
+    const double r = 1.0 / (double)s;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = v[i] / s;
+    for (int i = 0; i < 8; ++i) v[i] = (float)((double)v[i] * r);
   } else if (active) {
     const f32x4* p = reinterpret_cast<const f32x4*>(cscale) + 2 * ((int64_t)h * dvecs + j);
     const f32x4 a = p[0], b = p[1];
