@@ -105,3 +105,19 @@ def test_llama3_8b_prefill_chunk_into_paged_cache():
     k_ref, v_ref = bf16_as_f32(c["k"]), bf16_as_f32(c["v"])
     check_store(to_dev(c["v"], dev), v_ref, c["slots"], 32768, False, dev)
     check_store(to_dev(c["k"], dev), k_ref, c["slots"], 32768, True, dev)
+
+
+def test_per_token_cache_reads_back_through_dequant():
+    # the per-token layout is FP8 rows of heads * head_dim with one scale
+    # per head: qg_dequant with group = head_dim decodes it
+    dev = device()
+    t, h, d, slots = 24, 4, 128, 32
+    c = kv_case(t, h, d, slots, seed=21, block=8)
+    codes, scales = fresh_cache(slots, h, d, dev)
+    qg.kv_cache_store(to_dev(c["v"], dev), to_dev(c["slots"], dev), codes, scales)
+    got = host(qg.dequant(codes.reshape(slots, h * d), scales.reshape(slots, h), None,
+                          "fp8_e4m3", h * d, group=d))
+    rc, rs = okv.quantize_tokens(bf16_as_f32(c["v"]))
+    from oracle import formats as F
+    ref = (F.decode(rc, "e4m3") * rs[:, :, None].astype(np.float64)).astype(np.float32)
+    assert (bits32(got[c["slots"]].reshape(t, h, d)) == bits32(ref)).all()
