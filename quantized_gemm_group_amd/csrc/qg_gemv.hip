@@ -390,6 +390,10 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
 // so lane (l % 16, l / 16) accumulates D[m = 4 (l / 16) + r][n = l % 16]: its
 // outputs, scale and zero point all belong to weight row n0 + l % 16, and a
 // second MFMA against 1.0 gives the group sums of x in the same layout.
+// With one row of x (MM = 1) every output lane needs the same group sums:
+// each lane's 16-byte piece of x lies in one group, so 16-lane shuffles give
+// the sums and a lane read puts each in a scalar register, which drops the
+// second MFMA (half of the matrix work) and its registers.
 // LDS: [x slices: KS * MM * NG * 256 bytes][partials: KS * 1 KiB].
 template <bool ASYM, int NG, int MM>
 __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __restrict__ x, int M,
@@ -464,6 +468,26 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
       reinterpret_cast<u32x4*>(xw)[m * NG * 16 + q * 64 + lane] =
           pair_activations(xr[m * kXLoads + q]);
 
+  // group sums of x for one row: lane l of load q holds elements
+  // 512 q + 8 l .. + 7 of the slice, i.e. 8 values of group 4 q + l / 16
+  float gsum[MM == 1 ? kXLoads : 1];
+  if constexpr (MM == 1) {
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part += __uint_as_float(xr[q][e] << 16);
+        part += __uint_as_float(xr[q][e] & 0xffff0000u);
+      }
+      part += shfl_xor(part, 1);
+      part += shfl_xor(part, 2);
+      part += shfl_xor(part, 4);
+      part += shfl_xor(part, 8);
+      gsum[q] = part;
+    }
+  }
+
   // ---- 3. groups.  Rows m >= M of the first operand repeat row 0: their
   //      results are never stored.
   const int mrow = li < M ? li : 0;
@@ -483,7 +507,14 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], cw, acc1, 0, 0, 0);
       else
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], cw, acc0, 0, 0, 0);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], as_bf16x8(ones), sacc, 0, 0, 0);
+      if constexpr (MM != 1)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[i], as_bf16x8(ones), sacc, 0, 0, 0);
+    }
+    if constexpr (MM == 1) {
+      const float sx = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gsum[j >> 2]), 16 * (j & 3)));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[r] = sx;
     }
     const uint32_t sb = (sv[j >> 1] >> (16 * (j & 1))) & 0xffffu;
     const float sc = f16_bits_to_f32(sb);
