@@ -123,3 +123,24 @@ def test_swiglu_reference_is_gate_then_up():
     # channel selection picks the same columns
     assert np.allclose(gemm.swiglu_reference(x, packed, s, None, 128, channels=[2, 0]),
                        expect[:, [2, 0]], rtol=1e-12, atol=1e-12)
+
+
+def test_parity_bound_rejects_a_missing_cross_term():
+    # 《第 6 课：量化源码走读》 section 3: an asymmetric product that leaves out the
+    # zero-point cross term is wrong.  Planted on the oracle side: at the
+    # Llama-3-8B decode distributions (asymmetric INT4 g128, 1 % of the input
+    # channels x20) the product without the term, or with every zero point
+    # off by one, lies far outside the 2e-3 parity bound, while the exact
+    # dequantized product rounded to bf16 stays inside it
+    from synthetic import bf16_as_f32, small_case
+    c = small_case(4, 1024, 96, seed=31, w_outlier=(0.01, 20.0))
+    x = bf16_as_f32(c["x"]).astype(np.float64)
+    q, s, z = IQ.quantize_asym(c["w"], 128)
+    ref = x @ IQ.dequantize(q, s, z, 128).T
+    no_cross = x @ IQ.dequantize(q, s, np.zeros_like(z), 128).T
+    off_by_one = x @ IQ.dequantize(q, s, z + 1, 128).T
+    import torch
+    rounded = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    assert gemm.rel_fro(rounded, ref) <= 2e-3
+    assert gemm.rel_fro(no_cross, ref) > 100 * 2e-3
+    assert gemm.rel_fro(off_by_one, ref) > 2e-3
