@@ -24,8 +24,11 @@
 //
 // Tiling: 512-thread workgroup (two waves per SIMD, so one wave's unpacking
 // and scaling overlaps the other's matrix instructions), 128 (tokens) x 256
-// (channels) output tile, 8 waves of 64 x 64 (2 x 2 tiles of 32x32); one
-// k-step = one group.  The operands travel HBM -> LDS with buffer loads that
+// (channels) output tile; one k-step = one group.  The plain GEMM gives each
+// of the 8 waves 128 x 32 (4 x 1 tiles of 32x32): a wave unpacks only its own
+// 32 channels' codes and uses each unpacked code for four MFMAs.  The SwiGLU
+// variant keeps waves of 64 x 64 (2 x 2 tiles) so that a wave holds the gate
+// and the up tile of the same channels.  The operands travel HBM -> LDS with buffer loads that
 // write LDS directly, into a ring of 3 stages: X (128 rows x 256 bytes,
 // 16-byte chunks XOR-swizzled by row bits 0..3), the codes (256 rows x 64
 // bytes, swizzled by row bits 2..3) and the group's fp16 scales and zero
@@ -119,6 +122,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int l32 = lane & 31, lh = lane >> 5;
+  // Wave tile.  Plain GEMM: 128 tokens x 32 channels (4 x 1 tiles of 32x32),
+  // so every wave unpacks codes no other wave unpacks and uses each unpacked
+  // code for four MFMAs.  SWIGLU: 64 x 64 (2 x 2 tiles), the gate and up
+  // tiles of the same channels in one wave.
+  constexpr int MT = SWIGLU ? 2 : 4, NT = SWIGLU ? 2 : 1;
+  const int mrow0 = SWIGLU ? 64 * wm : 0;          // first X row of the wave tile
+  const int nrow0 = SWIGLU ? 64 * wn : 32 * wave;  // first LDS code row
 
   // SWIGLU: N = 2 I weight rows, 128 intermediate channels per tile
   const int NI = SWIGLU ? N / 2 : N;                 // output columns
@@ -186,13 +196,17 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
 
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                          0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  f32x16 yacc[2][2];
+  f32x16 yacc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) yacc[mt][nt] = zero16;
-  // s_g * c_g of this lane's two channels for the last two groups, by parity
-  float scp[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    for (int nt = 0; nt < NT; ++nt) yacc[mt][nt] = zero16;
+  // s_g * c_g of this lane's channels for the last two groups, by parity
+  float scp[2][NT];
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) scp[p2][nt] = 0.f;
   const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 
   // Cross term of groups g0 (even) and g0 + 1: lane half h supplies group
@@ -200,19 +214,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   // channel as the second); without `pair` group g0 + 1 does not exist.
   auto cross = [&](int g0, bool pair) {
     const uint8_t* sb = sums + ((g0 + lh) % kSumBufs) * kSumBytes;
-    float sx[2];
+    float sx[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const u32x4 p = *reinterpret_cast<const u32x4*>(sb + (64 * wm + 32 * mt + l32) * 16);
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 p = *reinterpret_cast<const u32x4*>(sb + (mrow0 + 32 * mt + l32) * 16);
       sx[mt] = (__uint_as_float(p[0]) + __uint_as_float(p[1])) +
                (__uint_as_float(p[2]) + __uint_as_float(p[3]));
       if (!pair && lh) sx[mt] = 0.f;
     }
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const float b = -(lh ? scp[1][nt] : scp[0][nt]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
         yacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x2f32(sx[mt], b, yacc[mt][nt], 0, 0, 0);
     }
   };
@@ -227,15 +241,18 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     const uint8_t* st = smem + (g % kStages) * kStageBytes;
     if (P == 0 && g >= 2) cross(g - 2, true);
 
-    // this wave's share of the row sums of group g: the rows of m-tile
-    // wn % 2, k = 64 h + 32 (wn / 2) .. + 31
+    // this wave's share of the row sums of group g, as one of four partial
+    // sums of 32 k per row.  SWIGLU: the rows of m-tile wn % 2, k = 64 h +
+    // 32 (wn / 2) .. + 31; plain: rows 16 w .. 16 w + 15, four lanes a row.
     {
       const int mt = wn & 1, jq = wn >> 1;
-      const int r = 64 * wm + 32 * mt + l32;
+      const int r = SWIGLU ? 64 * wm + 32 * mt + l32 : 16 * wave + (lane >> 2);
+      const int part = SWIGLU ? 2 * jq + lh : (lane & 3);
+      const int c0 = SWIGLU ? 8 * lh + 4 * jq : 4 * (lane & 3);
       float ps = 0.f;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + x_off(r, 8 * lh + 4 * jq + h));
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + x_off(r, c0 + h));
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           // (a bit cast of a vector element itself would read element 0)
@@ -243,41 +260,41 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
           ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e), ones2, ps, false);
         }
       }
-      *reinterpret_cast<float*>(sums + (g % kSumBufs) * kSumBytes + r * 16 + (2 * jq + lh) * 4) = ps;
+      *reinterpret_cast<float*>(sums + (g % kSumBufs) * kSumBytes + r * 16 + part * 4) = ps;
     }
 
     // codes: 32 contiguous bytes of the lane's row (words 8 lh .. 8 lh + 7)
-    u32x4 cw[2][2];
+    u32x4 cw[NT][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = wn * 64 + nt * 32 + l32;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = nrow0 + nt * 32 + l32;
       cw[nt][0] = *reinterpret_cast<const u32x4*>(st + w_off(r, 2 * lh));
       cw[nt][1] = *reinterpret_cast<const u32x4*>(st + w_off(r, 2 * lh + 1));
     }
-    float sv[2];
+    float sv[NT];
     const uint32_t* sl = reinterpret_cast<const uint32_t*>(st + kXBytes + kWBytes);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = wn * 64 + nt * 32 + l32;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = nrow0 + nt * 32 + l32;
       sv[nt] = f16_bits_to_f32((uint16_t)sl[r]);
       const float c = ASYM ? 128.f + f16_bits_to_f32((uint16_t)sl[BN + r]) : 136.f;
       scp[P][nt] = sv[nt] * c;
     }
 
-    f32x16 gacc[2][2];
+    f32x16 gacc[MT][NT];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      bf16x8 a[2];
+      bf16x8 a[MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int r = wm * 64 + mt * 32 + l32;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = mrow0 + mt * 32 + l32;
         a[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(st + x_off(r, 8 * lh + j)));
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const bf16x8 b = as_bf16x8(unpack_word(cw[nt][j >> 2][j & 3], mask, cmag));
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
           gacc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt], b, j ? gacc[mt][nt] : zero16,
                                                                  0, 0, 0);
       }
@@ -285,9 +302,9 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     // y += s * acc: lane (l32, lh) register r holds m = 8 (r / 4) + 4 lh + r % 4
     // of its m-tile and n = l32 of its n-tile
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           yacc[mt][nt][r] = __builtin_fmaf(sv[nt], gacc[mt][nt][r], yacc[mt][nt][r]);
@@ -332,13 +349,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
       }
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int nl = wn * 64 + nt * 32 + l32;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int nl = nrow0 + nt * 32 + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ml = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int ml = mrow0 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
           so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
         }
       }
