@@ -24,11 +24,9 @@
 //
 // Tiling: 512-thread workgroup (two waves per SIMD, so one wave's unpacking
 // and scaling overlaps the other's matrix instructions), 128 (tokens) x 256
-// (channels) output tile; one k-step = one group.  The plain GEMM gives each
-// of the 8 waves 128 x 32 (4 x 1 tiles of 32x32): a wave unpacks only its own
-// 32 channels' codes and uses each unpacked code for four MFMAs.  The SwiGLU
-// variant keeps waves of 64 x 64 (2 x 2 tiles) so that a wave holds the gate
-// and the up tile of the same channels.  The operands travel HBM -> LDS with buffer loads that
+// (channels) output tile; one k-step = one group.  Each of the 8 waves owns
+// 128 x 32 (4 x 1 tiles of 32x32): a wave unpacks only its own 32 weight
+// rows' codes and uses each unpacked code for four MFMAs.  The operands travel HBM -> LDS with buffer loads that
 // write LDS directly, into a ring of 3 stages: X (128 rows x 256 bytes,
 // 16-byte chunks XOR-swizzled by row bits 0..3), the codes (256 rows x 64
 // bytes, swizzled by row bits 2..3) and the group's fp16 scales and zero
@@ -42,10 +40,10 @@
 // up projections as one GEMM over [W_gate; W_up], SiLU(gate) * up formed in
 // registers and written once): the weight rows are the 2I rows of the
 // concatenation and the output is H[M][I].  A workgroup covers 128
-// intermediate channels: wave column wn takes gate rows n0 + 32 wn .. + 31 as
-// its first 32x32 channel tile and the up rows I + n0 + 32 wn .. + 31 as its
-// second, so each lane holds gate[n] and up[n] of the same channel n in the
-// same registers and the epilogue needs no exchange.
+// intermediate channels: wave w's 32 weight rows are gate rows n0 + 16 w ..
+// + 15 and the up rows I + n0 + 16 w .. + 15, so lane l32 < 16 and lane
+// l32 + 16 hold gate[n] and up[n] of the same channel and token rows, and one
+// lane exchange per value pairs them in the epilogue.
 
 #include "qg_gemm_common.hpp"
 #include "qg_internal.hpp"
@@ -120,15 +118,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
   const int l32 = lane & 31, lh = lane >> 5;
-  // Wave tile.  Plain GEMM: 128 tokens x 32 channels (4 x 1 tiles of 32x32),
-  // so every wave unpacks codes no other wave unpacks and uses each unpacked
-  // code for four MFMAs.  SWIGLU: 64 x 64 (2 x 2 tiles), the gate and up
-  // tiles of the same channels in one wave.
-  constexpr int MT = SWIGLU ? 2 : 4, NT = SWIGLU ? 2 : 1;
-  const int mrow0 = SWIGLU ? 64 * wm : 0;          // first X row of the wave tile
-  const int nrow0 = SWIGLU ? 64 * wn : 32 * wave;  // first LDS code row
+  // Wave tile: 128 tokens x 32 weight rows (4 x 1 tiles of 32x32), so every
+  // wave unpacks codes no other wave unpacks and uses each unpacked code for
+  // four MFMAs.  SWIGLU: the 32 rows are 16 gate and the same 16 up channels.
+  constexpr int MT = 4, NT = 1;
+  const int mrow0 = 0;                             // first X row of the wave tile
+  const int nrow0 = 32 * wave;                     // first LDS code row
 
   // SWIGLU: N = 2 I weight rows, 128 intermediate channels per tile
   const int NI = SWIGLU ? N / 2 : N;                 // output columns
@@ -137,9 +133,10 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, 8, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * TN;
-  // weight row of LDS tile row r (0..255)
+  // weight row of LDS tile row r (0..255); SWIGLU: rows 32 w .. 32 w + 15
+  // are gate channels n0 + 16 w .., rows 32 w + 16 .. their up channels
   auto wrow = [&](int r) {
-    return SWIGLU ? ((r >> 5) & 1) * NI + n0 + 32 * (r >> 6) + (r & 31) : n0 + r;
+    return SWIGLU ? ((r >> 4) & 1) * NI + n0 + 16 * (r >> 5) + (r & 15) : n0 + r;
   };
   const int G = K / BK;
 
@@ -241,14 +238,12 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     const uint8_t* st = smem + (g % kStages) * kStageBytes;
     if (P == 0 && g >= 2) cross(g - 2, true);
 
-    // this wave's share of the row sums of group g, as one of four partial
-    // sums of 32 k per row.  SWIGLU: the rows of m-tile wn % 2, k = 64 h +
-    // 32 (wn / 2) .. + 31; plain: rows 16 w .. 16 w + 15, four lanes a row.
+    // this wave's share of the row sums of group g: rows 16 w .. 16 w + 15,
+    // four lanes a row, each one of four partial sums of 32 k
     {
-      const int mt = wn & 1, jq = wn >> 1;
-      const int r = SWIGLU ? 64 * wm + 32 * mt + l32 : 16 * wave + (lane >> 2);
-      const int part = SWIGLU ? 2 * jq + lh : (lane & 3);
-      const int c0 = SWIGLU ? 8 * lh + 4 * jq : 4 * (lane & 3);
+      const int r = 16 * wave + (lane >> 2);
+      const int part = lane & 3;
+      const int c0 = 4 * part;
       float ps = 0.f;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -338,14 +333,18 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   constexpr int kPitch = 528;
   uint16_t* const so = reinterpret_cast<uint16_t*>(smem);
   if constexpr (SWIGLU) {
-    const int nl = wn * 32 + l32;
+    // lane l32 < 16 holds gate channel n0 + 16 w + l32 and lane l32 + 16 the
+    // same channel's up value for the same token rows
+    const int nl = 16 * wave + (l32 & 15);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ml = wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const float g = yacc[mt][0][r], u = yacc[mt][1][r];
-        so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(g / (1.f + __expf(-g)) * u, 0.f);
+        const int ml = mrow0 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const float g = yacc[mt][0][r];
+        const float u = __shfl_xor(g, 16, 64);
+        if (l32 < 16)
+          so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(g / (1.f + __expf(-g)) * u, 0.f);
       }
   } else {
 #pragma unroll
