@@ -85,8 +85,12 @@ def test_fp8_gemm_8192_sampled():
 
 # ---------------------------------------------------------------------- MXFP4
 
+# K a multiple of 128 (one aligned exponent dword per row and k-step of 128
+# codes) with 1 to 6, 11 and 32 k-steps, odd and even step counts included;
+# K = 32 and 1056 load each k-step's exponents byte by byte
 @pytest.mark.parametrize("m,k,n", [(64, 256, 64), (130, 512, 200), (33, 1056, 129), (1, 32, 16),
-                                   (256, 4096, 260)])
+                                   (256, 4096, 260), (96, 128, 72), (70, 384, 300),
+                                   (257, 640, 64), (128, 768, 520), (40, 1408, 96)])
 def test_mx_gemm_small(m, k, n):
     dev = device()
     c = small_case(m, k, n, seed=3 * m + n, w_outlier=(0.01, 50.0))
