@@ -67,8 +67,8 @@ __device__ __forceinline__ void xcd_tile(int bid, int tiles_m, int tiles_n, int*
   tile_coords(lin, tiles_m, tiles_n, 4, tm, tn);
 }
 
-// Byte offset of 16-byte chunk c of row r in a stage operand tile.
-__device__ __forceinline__ int sw_off(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 4); }
+// In a stage operand tile, 16-byte chunk c of row r sits at byte
+// r * BK + ((c ^ ((r >> 2) & 3)) << 4).
 
 template <bool MX, bool SALIGN> struct Frags;
 template <bool SALIGN> struct Frags<false, SALIGN> {
@@ -88,7 +88,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // SALIGN (MX only): every row's exponents of a k-step are one aligned dword
 // (K a multiple of 128); otherwise its 4 bytes are loaded one by one.
-template <bool MX, bool SALIGN>
+// KFULL: K fills whole k-steps, so no load needs a K-tail check (loads past
+// the last k-step fill stages that are never read).
+template <bool MX, bool SALIGN, bool KFULL>
 __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
                                                              const void* __restrict__ a_aux, int M,
                                                              const uint8_t* __restrict__ W,
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     uint8_t* sA = smem + st * kStageBytes;
     if (d < 4) {
       const int j = d >> 1;
-      const bool kin = k * BK + dchunk * 16 < kbytes;   // K tail: whole chunks
+      const bool kin = KFULL || k * BK + dchunk * 16 < kbytes;   // K tail: whole chunks
       const int blk = 2 * wave + j;
       if (d & 1)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sA + kOpBytes + blk * 1024), 16,
@@ -172,6 +174,20 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     }
   };
 
+  // LDS read offsets within a stage: the lane's row in the first 32-row tile
+  // of its A rows (wm) and W rows (wn), fragment half c (FP8: chunk 2 lh + c,
+  // MX: chunk 2 c + lh).  The other tiles lie 32 rows (2 KiB) further, and
+  // the row swizzle (r >> 2) & 3 depends only on l32 because every tile
+  // starts at a multiple of 32 rows; so each read is one of these offsets
+  // plus a constant.
+  int offA[2], offW[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = (MX ? 2 * c + lh : 2 * lh + c) ^ ((l32 >> 2) & 3);
+    offA[c] = (wm * 128 + l32) * BK + (ch << 4);
+    offW[c] = kOpBytes + (wn * 64 + l32) * BK + (ch << 4);
+  }
+
   typedef Frags<MX, SALIGN> frags_t;
   // Fragment reads of k-step k, in the order the MFMAs consume them: entry
   // e of kOrd is A tile e (e < 4) or W tile e - 4.
@@ -180,14 +196,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   auto read_piece = [&](int k, frags_t& f, int p) {
     const int st = k & (kStages - 1);
     const uint8_t* sA = smem + st * kStageBytes;
-    const uint8_t* sW = sA + kOpBytes;
     if constexpr (!MX) {
       // the lane holds bytes 32 * lh .. +32 of the k-step's 64 for its row
       // (half h = 16 of them); both operands use the same byte -> k map
       const int e = kOrd[p >> 1], h = p & 1;
       const bool isw = e >= 4;
-      const int r = isw ? wn * 64 + (e - 4) * 32 + l32 : wm * 128 + e * 32 + l32;
-      const u32x4 v = *reinterpret_cast<const u32x4*>((isw ? sW : sA) + sw_off(r, 2 * lh + h));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          sA + (isw ? offW[h] + (e - 4) * 32 * BK : offA[h] + e * 32 * BK));
       i32x8& dst = isw ? f.w[e - 4] : f.a[e];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[4 * h + i] = (int)v[i];
@@ -211,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
         const int q = p - 6 * kSWords;
         const int sub = q / 6, e = kOrd[q % 6];
         const bool isw = e >= 4;
-        const int r = isw ? wn * 64 + (e - 4) * 32 + l32 : wm * 128 + e * 32 + l32;
-        const i32x4 v = *reinterpret_cast<const i32x4*>((isw ? sW : sA) + sw_off(r, 2 * sub + lh));
+        const i32x4 v = *reinterpret_cast<const i32x4*>(
+            sA + (isw ? offW[sub] + (e - 4) * 32 * BK : offA[sub] + e * 32 * BK));
         if (isw)
           f.w[sub][e - 4] = v;
         else
@@ -375,11 +390,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   }
 }
 
-template <bool MX, bool SALIGN>
+template <bool MX, bool SALIGN, bool KFULL>
 hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, const void* w_aux,
                   int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN>), dim3(tiles), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN, KFULL>), dim3(tiles), dim3(kThreads), 0, stream,
                      (const uint8_t*)a, a_aux, (int)M, (const uint8_t*)w, w_aux, (int)N, (int)K,
                      (uint16_t*)y);
   return hipGetLastError();
@@ -390,15 +405,18 @@ hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, co
 hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const void* w,
                            const void* w_scales, int64_t N, int64_t K, void* y,
                            hipStream_t stream) {
-  return launch<false, true>(a, a_scales, M, w, w_scales, N, K, y, stream);
+  if (K % BK == 0) return launch<false, true, true>(a, a_scales, M, w, w_scales, N, K, y, stream);
+  return launch<false, true, false>(a, a_scales, M, w, w_scales, N, K, y, stream);
 }
 
 hipError_t launch_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
                           const void* b_codes, const void* b_e8m0, int64_t N, int64_t K, void* y,
                           hipStream_t stream) {
-  // one aligned exponent dword per row and k-step when K is a multiple of 128
-  if (K % 128 == 0) return launch<true, true>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
-  return launch<true, false>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
+  // one aligned exponent dword per row and k-step, and whole k-steps of 128
+  // codes, when K is a multiple of 128
+  if (K % 128 == 0)
+    return launch<true, true, true>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
+  return launch<true, false, false>(a_codes, a_e8m0, M, b_codes, b_e8m0, N, K, y, stream);
 }
 
 }  // namespace qg
