@@ -380,7 +380,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     if (m < M) {
       uint16_t* py = Y + (int64_t)m * N + nbase;
       if (full_n) {
-        *reinterpret_cast<u32x4*>(py) = o;
+        // nontemporal: the output is not read again by this kernel
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(py));
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)

@@ -371,7 +371,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
                                                     ml * kPitch + cn * 16);
     uint16_t* py = Y + (int64_t)m * NI + n;
     if (vec_ok && n + 7 < NI) {
-      *reinterpret_cast<u32x4*>(py) = o;
+      // nontemporal: the output is not read again by this kernel
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(py));
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
