@@ -47,8 +47,10 @@ def fp8_case(m, k, n, seed):
     return c["w"], c["x"]
 
 
+# K a multiple of 64 (whole k-steps) and K = 48, 176, 1040 (a last k-step of
+# 3, 3 and 1 of its four 16-byte chunks)
 @pytest.mark.parametrize("m,k,n", [(64, 256, 80), (130, 512, 200), (257, 1040, 129), (1, 128, 16),
-                                   (300, 2048, 384)])
+                                   (300, 2048, 384), (40, 48, 72), (100, 176, 96)])
 def test_fp8_gemm_small(m, k, n):
     dev = device()
     w, x = fp8_case(m, k, n, seed=m + n + k)
