@@ -187,23 +187,111 @@ def bench_dominant(qg, torch, copies, stream, reps=40):
     return t / reps, proj_bytes(p0, 1)
 
 
+# ---------------------------------------------------- clocks and power
+
+def _card_dir(torch, dev):
+    """sysfs device directory of the amdgpu card behind dev, or None."""
+    import glob
+    cards = [c for c in sorted(glob.glob("/sys/class/drm/card*/device"))
+             if os.path.exists(os.path.join(c, "pp_dpm_sclk"))]
+    try:
+        pr = torch.cuda.get_device_properties(dev)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}."
+        hit = [c for c in cards if os.path.basename(os.path.realpath(c)).startswith(bdf)]
+        if len(hit) == 1:
+            return hit[0]
+    except Exception:
+        pass
+    return cards[0] if len(cards) == 1 else None
+
+
+class HwSampler:
+    """Engine clock, memory clock and board power sampled from sysfs (the
+    current pp_dpm_sclk / pp_dpm_mclk level, hwmon power1_input in
+    microwatts) by a background thread while a kernel runs back to back;
+    medians of the samples, None where a file cannot be read."""
+
+    def __init__(self, card, period_s=0.004):
+        import threading
+        self.card, self.period = card, period_s
+        self.samples = {"sclk_mhz": [], "mclk_mhz": [], "power_w": []}
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _level(path):
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().lower().split("mhz")[0])
+        return None
+
+    def _power(self):
+        import glob
+        with open(glob.glob(os.path.join(self.card, "hwmon", "hwmon*", "power1_input"))[0]) as f:
+            return int(f.read()) * 1e-6
+
+    def _read(self):
+        c = self.card
+        for key, fn in (("sclk_mhz", lambda: self._level(os.path.join(c, "pp_dpm_sclk"))),
+                        ("mclk_mhz", lambda: self._level(os.path.join(c, "pp_dpm_mclk"))),
+                        ("power_w", self._power)):
+            try:
+                v = fn()
+                if v is not None:
+                    self.samples[key].append(v)
+            except (OSError, ValueError, IndexError):
+                pass
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            self._read()
+
+    def __enter__(self):
+        if self.card:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        import statistics
+        out = {k: (round(statistics.median(v), 1) if v else None) for k, v in self.samples.items()}
+        out["samples"] = len(self.samples["sclk_mhz"])
+        return out
+
+
 # --------------------------------------------------------------- GEMMs
 
 def bench_gemms(qg, torch, dev, stream):
     from synthetic import workload_case
     out = {}
+    card = _card_dir(torch, dev)
+    hw = {}
 
     def timed(fn, reps, warm_s=0.05):
         # untimed warm-up of at least warm_s: after the host-side set-up
         # between cases the clocks need some tens of milliseconds of load to
         # come back up, and a single warm-up call leaves the first timed
-        # launches slow
+        # launches slow.  Clocks and power are sampled over its second half
+        # (the same kernel back to back) into hw["last"].
         t0 = time.perf_counter()
         while True:
             fn()
             torch.cuda.synchronize()
-            if time.perf_counter() - t0 >= warm_s:
+            if time.perf_counter() - t0 >= warm_s / 2:
                 break
+        with HwSampler(card) as smp:
+            t0 = time.perf_counter()
+            while True:
+                fn()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t0 >= warm_s / 2:
+                    break
+        hw["last"] = smp.summary()
         st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         st.record()
         for _ in range(reps):
@@ -218,14 +306,16 @@ def bench_gemms(qg, torch, dev, stream):
     wq, sw, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "fp8_e4m3")
     xq, sx, _ = qg.quantize_pack(x, "fp8_e4m3")
     y = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
-    t = timed(lambda: qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx, out=y), 10)
+    t = timed(lambda: qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx, out=y), 10,
+              0.1)
+    hw_gemm = hw["last"]
     tq = timed(lambda: qg.quantize_pack(x, "fp8_e4m3"), 10)
     fl = 2 * 8192 ** 3
     out["fp8_gemm_8192"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
                                 frac=fl / t / 1e12 / PEAK_TFLOPS["fp8"],
                                 act_quant_us=tq * 1e6,
                                 act_quant_gbs=(8192 * 8192 * 3 + 8192 * 4) / tq / 1e9,
-                                end_to_end_tflops=fl / (t + tq) / 1e12)
+                                end_to_end_tflops=fl / (t + tq) / 1e12, clocks_power=hw_gemm)
     # fused RMSNorm / LayerNorm + per-token FP8 quantization of the same
     # activations (one read of x, one write of codes and scales), against
     # the unfused path: torch's layer norm writing bf16, then the quantizer
@@ -249,13 +339,15 @@ def bench_gemms(qg, torch, dev, stream):
     bc, be = qg.mx_quant(torch.from_numpy(c["w"]).to(dev))
     ac, ae = qg.mx_quant(x)
     y = torch.empty((4096, 8192), dtype=torch.bfloat16, device=dev)
-    t = timed(lambda: qg.mx_gemm(ac, ae, bc, be, out=y), 10)
+    t = timed(lambda: qg.mx_gemm(ac, ae, bc, be, out=y), 10, 0.1)
+    hw_gemm = hw["last"]
     tq = timed(lambda: qg.mx_quant(x), 10)
     fl = 2 * 4096 * 8192 * 8192
     out["mxfp4_gemm_4096x8192"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
                                        frac=fl / t / 1e12 / PEAK_TFLOPS["fp4"],
                                        act_quant_us=tq * 1e6,
-                                       end_to_end_tflops=fl / (t + tq) / 1e12)
+                                       end_to_end_tflops=fl / (t + tq) / 1e12,
+                                       clocks_power=hw_gemm)
     del x, bc, be, ac, ae, y, c
     # W4A16 prefill, Qwen2.5-72B FFN shapes
     for i, name in enumerate(["ffn_up", "ffn_down"]):
@@ -263,20 +355,22 @@ def bench_gemms(qg, torch, dev, stream):
         x = c["x"].to(dev)
         codes, s, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_sym", 128)
         y = torch.empty((2048, c["n"]), dtype=torch.bfloat16, device=dev)
-        t = timed(lambda: qg.qgemm(x, codes, s, None, "int4_sym", "bf16", out=y), 5)
+        t = timed(lambda: qg.qgemm(x, codes, s, None, "int4_sym", "bf16", out=y), 5, 0.1)
         fl = 2 * 2048 * c["k"] * c["n"]
         out[f"w4a16_prefill_{name}"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
-                                            frac=fl / t / 1e12 / PEAK_TFLOPS["bf16"])
+                                            frac=fl / t / 1e12 / PEAK_TFLOPS["bf16"],
+                                            clocks_power=hw["last"])
         if name == "ffn_up":
             # the up shape is a fused gate+up (29568 = 2 x 14784 rows): the
             # SwiGLU epilogue variant writes SiLU(gate) * up, [2048][14784]
             h = torch.empty((2048, c["n"] // 2), dtype=torch.bfloat16, device=dev)
-            th = timed(lambda: qg.qgemm_swiglu(x, codes, s, None, "int4_sym", out=h), 5)
+            th = timed(lambda: qg.qgemm_swiglu(x, codes, s, None, "int4_sym", out=h), 5, 0.1)
+            hw_gemm = hw["last"]
             tm = timed(lambda: torch.mul(torch.nn.functional.silu(y[:, :c["n"] // 2]),
                                          y[:, c["n"] // 2:], out=h), 5)
             out["w4a16_prefill_ffn_gate_up_swiglu"] = dict(
                 us=th * 1e6, tflops=fl / th / 1e12, frac=fl / th / 1e12 / PEAK_TFLOPS["bf16"],
-                unfused_us=(t + tm) * 1e6)
+                unfused_us=(t + tm) * 1e6, clocks_power=hw_gemm)
             del h
         del x, codes, s, y, c
     torch.cuda.empty_cache()
