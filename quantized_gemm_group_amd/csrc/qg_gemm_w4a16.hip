@@ -173,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   // Loads of group g into stage g % 3.  Past the last group the last group is
   // loaded again (into a stage nobody reads), so every k-step issues the same
   // number of loads and the wait counts stay uniform.
-  auto issue = [&](int g) {
-    uint8_t* st = smem + (g % kStages) * kStageBytes;
+  auto issue = [&](int g, int stage) {
+    uint8_t* st = smem + stage * kStageBytes;
     const int gl = g < G ? g : G - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -228,14 +228,18 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     }
   };
 
-  // One k-step over group g (P = g % 2).
-  auto step = [&](int g, auto parity) {
+  // One k-step over group g (P = g % 2).  SC = g % 3 when known at compile
+  // time (the main loop is unrolled by 6), else -1: with a constant stage
+  // every LDS address is a per-lane offset plus an immediate.
+  auto step = [&](int g, auto parity, auto stage_c) {
     constexpr int P = decltype(parity)::value;
+    constexpr int SC = decltype(stage_c)::value;
+    const int sg = SC >= 0 ? SC : g % kStages;        // stage of g (also its row-sum buffer)
     // group g has landed for every wave; stage (g - 1) % 3 is free and the
     // row sums of the groups before g are in LDS
     wait_vm_barrier<kGroupLoads>();
-    issue(g + 2);
-    const uint8_t* st = smem + (g % kStages) * kStageBytes;
+    issue(g + 2, SC >= 0 ? (SC + 2) % kStages : (g + 2) % kStages);
+    const uint8_t* st = smem + sg * kStageBytes;
     if (P == 0 && g >= 2) cross(g - 2, true);
 
     // this wave's share of the row sums of group g: rows 16 w .. 16 w + 15,
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
           ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e), ones2, ps, false);
         }
       }
-      *reinterpret_cast<float*>(sums + (g % kSumBufs) * kSumBytes + r * 16 + part * 4) = ps;
+      *reinterpret_cast<float*>(sums + sg * kSumBytes + r * 16 + part * 4) = ps;
     }
 
     // codes: 32 contiguous bytes of the lane's row (words 8 lh .. 8 lh + 7)
@@ -305,14 +309,23 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
           yacc[mt][nt][r] = __builtin_fmaf(sv[nt], gacc[mt][nt][r], yacc[mt][nt][r]);
   };
 
-  issue(0);
-  issue(1);
+  static_assert(kSumBufs == kStages, "row-sum buffers rotate with the stages");
+  issue(0, 0);
+  issue(1, 1);
   int g = 0;
-  for (; g + 1 < G; g += 2) {
-    step(g, Parity<0>{});
-    step(g + 1, Parity<1>{});
+  for (; g + 5 < G; g += 6) {
+    step(g, Parity<0>{}, Parity<0>{});
+    step(g + 1, Parity<1>{}, Parity<1>{});
+    step(g + 2, Parity<0>{}, Parity<2>{});
+    step(g + 3, Parity<1>{}, Parity<0>{});
+    step(g + 4, Parity<0>{}, Parity<1>{});
+    step(g + 5, Parity<1>{}, Parity<2>{});
   }
-  if (g < G) step(g, Parity<0>{});
+  for (; g + 1 < G; g += 2) {
+    step(g, Parity<0>{}, Parity<-1>{});
+    step(g + 1, Parity<1>{}, Parity<-1>{});
+  }
+  if (g < G) step(g, Parity<0>{}, Parity<-1>{});
   // Every wave's trailing loads (a repeat of the last group) have landed and
   // every wave is past its last k-step: the row sums of the last groups are
   // in LDS and the operand stages are free for the epilogue.
