@@ -601,7 +601,12 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __rest
       if (tid + (int64_t)kThreads * i >= kvecs) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double d = (double)v[i][e] - mean64;
+        // converted again here: reusing the first pass's fp64 values would
+        // keep all of them live (two registers per element) across the
+        // reduction, halving the waves that fit on a SIMD
+        float f = v[i][e];
+        asm volatile("" : "+v"(f));
+        const double d = (double)f - mean64;
         acc2 += d * d;
       }
     }
