@@ -272,33 +272,34 @@ def bench_gemms(qg, torch, dev, stream):
     card = _card_dir(torch, dev)
     hw = {}
 
-    def timed(fn, reps, warm_s=0.05):
+    def timed(fn, reps, warm_s=0.05, sample_s=0.0):
         # untimed warm-up of at least warm_s: after the host-side set-up
         # between cases the clocks need some tens of milliseconds of load to
         # come back up, and a single warm-up call leaves the first timed
-        # launches slow.  Clocks and power are sampled over its second half
-        # (the same kernel back to back) into hw["last"].
+        # launches slow.  With sample_s, clocks and power are sampled after
+        # the timed launches, over sample_s of the same kernel back to back,
+        # into hw["last"] (the sysfs reads stay out of the timed region).
         t0 = time.perf_counter()
         while True:
             fn()
             torch.cuda.synchronize()
-            if time.perf_counter() - t0 >= warm_s / 2:
+            if time.perf_counter() - t0 >= warm_s:
                 break
-        with HwSampler(card) as smp:
-            t0 = time.perf_counter()
-            while True:
-                fn()
-                torch.cuda.synchronize()
-                if time.perf_counter() - t0 >= warm_s / 2:
-                    break
-        hw["last"] = smp.summary()
         st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         st.record()
         for _ in range(reps):
             fn()
         en.record()
         en.synchronize()
-        return st.elapsed_time(en) * 1e-3 / reps
+        t = st.elapsed_time(en) * 1e-3 / reps
+        if sample_s > 0:
+            with HwSampler(card) as smp:
+                t0 = time.perf_counter()
+                while time.perf_counter() - t0 < sample_s:
+                    fn()
+                    torch.cuda.synchronize()
+            hw["last"] = smp.summary()
+        return t
 
     # FP8 W8A8, M=N=K=8192
     c = workload_case("fp8_8192")
@@ -307,7 +308,7 @@ def bench_gemms(qg, torch, dev, stream):
     xq, sx, _ = qg.quantize_pack(x, "fp8_e4m3")
     y = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
     t = timed(lambda: qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx, out=y), 10,
-              0.1)
+              0.05, 0.05)
     hw_gemm = hw["last"]
     tq = timed(lambda: qg.quantize_pack(x, "fp8_e4m3"), 10)
     fl = 2 * 8192 ** 3
@@ -339,7 +340,7 @@ def bench_gemms(qg, torch, dev, stream):
     bc, be = qg.mx_quant(torch.from_numpy(c["w"]).to(dev))
     ac, ae = qg.mx_quant(x)
     y = torch.empty((4096, 8192), dtype=torch.bfloat16, device=dev)
-    t = timed(lambda: qg.mx_gemm(ac, ae, bc, be, out=y), 10, 0.1)
+    t = timed(lambda: qg.mx_gemm(ac, ae, bc, be, out=y), 10, 0.05, 0.05)
     hw_gemm = hw["last"]
     tq = timed(lambda: qg.mx_quant(x), 10)
     fl = 2 * 4096 * 8192 * 8192
@@ -355,7 +356,7 @@ def bench_gemms(qg, torch, dev, stream):
         x = c["x"].to(dev)
         codes, s, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_sym", 128)
         y = torch.empty((2048, c["n"]), dtype=torch.bfloat16, device=dev)
-        t = timed(lambda: qg.qgemm(x, codes, s, None, "int4_sym", "bf16", out=y), 5, 0.1)
+        t = timed(lambda: qg.qgemm(x, codes, s, None, "int4_sym", "bf16", out=y), 5, 0.05, 0.05)
         fl = 2 * 2048 * c["k"] * c["n"]
         out[f"w4a16_prefill_{name}"] = dict(us=t * 1e6, tflops=fl / t / 1e12,
                                             frac=fl / t / 1e12 / PEAK_TFLOPS["bf16"],
@@ -364,7 +365,7 @@ def bench_gemms(qg, torch, dev, stream):
             # the up shape is a fused gate+up (29568 = 2 x 14784 rows): the
             # SwiGLU epilogue variant writes SiLU(gate) * up, [2048][14784]
             h = torch.empty((2048, c["n"] // 2), dtype=torch.bfloat16, device=dev)
-            th = timed(lambda: qg.qgemm_swiglu(x, codes, s, None, "int4_sym", out=h), 5, 0.1)
+            th = timed(lambda: qg.qgemm_swiglu(x, codes, s, None, "int4_sym", out=h), 5, 0.05, 0.05)
             hw_gemm = hw["last"]
             tm = timed(lambda: torch.mul(torch.nn.functional.silu(y[:, :c["n"] // 2]),
                                          y[:, c["n"] // 2:], out=h), 5)
