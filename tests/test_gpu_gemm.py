@@ -175,9 +175,12 @@ def test_int8_gemm_4096_sampled():
 
 # --------------------------------------------------------------- W4A16 prefill
 
+# groups of 128 per row G = 1, 2, 3, 5, 7, 8, 11, 12, 16: the k-loop runs in
+# unrolled blocks of 6 groups, then pairs, then a single group
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("m,k,n", [(64, 256, 80), (200, 1024, 136), (1, 128, 16), (300, 2048, 520),
-                                   (130, 384, 300), (70, 640, 260)])
+                                   (130, 384, 300), (70, 640, 260), (96, 896, 72),
+                                   (33, 1408, 264), (140, 1536, 128)])
 def test_w4a16_gemm_small(m, k, n, asym):
     dev = device()
     c = small_case(m, k, n, seed=m + 11 * n, w_outlier=(0.01, 20.0))

@@ -29,7 +29,7 @@ def check(h, ref, what):
 
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("m,k,i", [(64, 256, 40), (200, 1024, 136), (1, 128, 8), (130, 384, 300),
-                                   (300, 2048, 520)])
+                                   (300, 2048, 520), (96, 896, 72), (40, 1408, 136)])
 def test_swiglu_small(m, k, i, asym):
     dev = device()
     fmt = "int4_asym" if asym else "int4_sym"
