@@ -96,13 +96,19 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
                                                              const uint8_t* __restrict__ W,
                                                              const void* __restrict__ w_aux, int N,
                                                              int K, uint16_t* __restrict__ Y) {
-  // exponent staging per row and k-step: one dword (SALIGN) or its 4 bytes
-  // loaded one by one, each landing zero-extended in a dword of its own
-  constexpr int kSWords = MX ? (SALIGN ? 1 : 4) : 0;
+  // Exponent staging.  Grouped (SALIGN): the dwords of 4 k-steps (a group)
+  // of all 512 tile rows in one of 3 slots, see issue_exp.  Otherwise per
+  // row and k-step 4 bytes loaded one by one beside the operands, each
+  // landing zero-extended in a dword of its own, in every ring stage.
+  constexpr bool kGrouped = MX && SALIGN;
+  constexpr int kSWords = (MX && !SALIGN) ? 4 : 0;
   constexpr int kScaleStage = (BM + BN) * 4 * kSWords;
-  constexpr int kRing = kStages * (kStageBytes + kScaleStage);
+  constexpr int kChunk = 320;                   // 16 rows x 4 k-steps + 64 bytes of skew
+  constexpr int kExpSlot = kGrouped ? (BM + BN) / 16 * kChunk : 0;
+  constexpr int kRing = kStages * (kStageBytes + kScaleStage) + 3 * kExpSlot;
   constexpr int kLds = kRing > kEpiBytes ? kRing : kEpiBytes;
-  // loads per wave per k-step: 4 operand blocks of 1 KiB + exponent loads
+  // loads per wave per k-step beside the grouped exponent loads: 4 operand
+  // blocks of 1 KiB + per-k-step exponent loads
   constexpr int kGroup = 4 + kSWords;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   uint8_t* const sscale = smem + kStages * kStageBytes;
@@ -136,15 +142,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     voa[j] = (uint32_t)(m0 + r) * kbytes + dchunk * 16;
     vow[j] = (uint32_t)(n0 + r) * kbytes + dchunk * 16;
   }
-  // Exponent loads (MX): wave w brings the dwords of tile rows 64 w .. +63
-  // (rows 0..255 of A, then 256..511 of W), one load per k-step and byte.
+  // Exponent loads (MX): wave w brings the exponents of tile rows 64 w .. +63
+  // (rows 0..255 of A, then 256..511 of W).  Grouped: lane l reads dword
+  // l / 16 (k-step) of row l % 16 of a 16-row chunk, so one load touches 16
+  // rows' cache lines instead of 64; otherwise one load per k-step and byte
+  // with lane l on row l.
   __amdgpu_buffer_rsrc_t rsx = make_rsrc(a_aux, 0);
   uint32_t vos = 0;
   if constexpr (MX) {
     const bool wop = wave >= 4;
     rsx = make_rsrc(wop ? w_aux : a_aux, (int64_t)(wop ? N : M) * kblocks);
-    const int grow = (wop ? n0 : m0) + 64 * (wave & 3) + lane;
-    vos = (uint32_t)grow * kblocks;
+    const int grow = (wop ? n0 : m0) + 64 * (wave & 3) + (kGrouped ? (lane & 15) : lane);
+    vos = (uint32_t)grow * kblocks + (kGrouped ? 4 * (lane >> 4) : 0);
   }
 
   // One load of the k-step group: d < 4 -> operand block 2 w + d / 2 of A
@@ -162,17 +171,33 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + blk * 1024), 16,
                                                  kin ? voa[j] : kOutOfRange, k * BK, 0, 0);
-    } else if constexpr (MX) {
+    } else if constexpr (MX && !SALIGN) {
       const int j = d - 4;
       uint8_t* ss = sscale + st * kScaleStage;
       lds_void* dst = (lds_void*)(ss + (j * 512 + 64 * wave) * 4);
       const uint32_t vo = k * 4 + j < kblocks ? vos + j : kOutOfRange;
-      if constexpr (SALIGN)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 4, vo, k * 4, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 1, vo, k * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 1, vo, k * 4, 0, 0);
     }
   };
+
+  // Grouped exponents of k-steps 4 G .. 4 G + 3 go to slot G % 3 as 32 chunks
+  // of 16 rows, chunk q at q * kChunk: dword 16 j + r' of a chunk holds k-step
+  // j of row 16 q + r', so one k-step of 32 consecutive rows spans 32 banks
+  // (the 64-byte skew per chunk shifts the second 16 rows by 16 banks).
+  // Piece p (0..3) of a group is chunk 4 w + p of wave w.  The pieces of
+  // group g + 2 go out two per odd step at steps 4 g + 1 and 4 g + 3; its slot
+  // last held group g - 1, whose reads ended before the barrier of step
+  // 4 g - 1.  They are waited for by the barrier of step 4 g + 5 at the
+  // latest, before the reads of k-step 4 g + 8.
+  auto issue_exp = [&](int G, int p) {
+    if constexpr (kGrouped) {
+      uint8_t* dst = sscale + (G % 3) * kExpSlot + (4 * wave + p) * kChunk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)dst, 4, vos,
+                                               p * 16 * kblocks + G * 16, 0, 0);
+    }
+  };
+  // lane's offset within a group slot for rows r0 + l32 (r0 a multiple of 32)
+  const int eoff = (l32 >> 4) * kChunk + (l32 & 15) * 4;
 
   // LDS read offsets within a stage: the lane's row in the first 32-row tile
   // of its A rows (wm) and W rows (wn), fragment half c (FP8: chunk 2 lh + c,
@@ -192,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // Fragment reads of k-step k, in the order the MFMAs consume them: entry
   // e of kOrd is A tile e (e < 4) or W tile e - 4.
   constexpr int kOrd[6] = {4, 0, 1, 2, 3, 5};
-  constexpr int kReads = MX ? 12 + 6 * kSWords : 12;
+  constexpr int kEWords = kGrouped ? 1 : kSWords;   // exponent reads per row and k-step
+  constexpr int kReads = MX ? 12 + 6 * kEWords : 12;
   auto read_piece = [&](int k, frags_t& f, int p) {
     const int st = k & (kStages - 1);
     const uint8_t* sA = smem + st * kStageBytes;
@@ -207,23 +233,29 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[4 * h + i] = (int)v[i];
     } else {
-      const uint32_t* ss = reinterpret_cast<const uint32_t*>(sscale + st * kScaleStage);
-      if (p < 6 * kSWords) {
-        // exponents first: row entry p / kSWords (A rows 0..3, W rows 4..5)
-        const int e = p / kSWords, j = p % kSWords;
+      if (p < 6 * kEWords) {
+        // exponents first: row entry p / kEWords (A rows 0..3, W rows 4..5)
+        const int e = p / kEWords, j = p % kEWords;
         const bool isw = e >= 4;
-        const int r = isw ? 256 + wn * 64 + (e - 4) * 32 + l32 : wm * 128 + e * 32 + l32;
+        const int r0 = isw ? 256 + wn * 64 + (e - 4) * 32 : wm * 128 + e * 32;
         uint32_t& dst = isw ? f.ws[e - 4] : f.as[e];
-        const uint32_t v = ss[j * 512 + r];
+        uint32_t v;
+        if constexpr (kGrouped) {
+          const uint8_t* se = sscale + ((k >> 2) % 3) * kExpSlot + (r0 >> 4) * kChunk + (k & 3) * 64;
+          v = *reinterpret_cast<const uint32_t*>(se + eoff);
+        } else {
+          const uint32_t* ss = reinterpret_cast<const uint32_t*>(sscale + st * kScaleStage);
+          v = ss[j * 512 + r0 + l32];
+        }
         if (j == 0)
           dst = v;
         else
           dst |= v << (8 * j);
         // the lane's block in sub-step s is byte 2 s + lh: shifted to byte 2 s
-        if (j == kSWords - 1) dst >>= 8 * lh;
+        if (j == kEWords - 1) dst >>= 8 * lh;
       } else {
         // sub-step s: the lane holds block 2 s + lh of the k-step (16 bytes)
-        const int q = p - 6 * kSWords;
+        const int q = p - 6 * kEWords;
         const int sub = q / 6, e = kOrd[q % 6];
         const bool isw = e >= 4;
         const i32x4 v = *reinterpret_cast<const i32x4*>(
@@ -279,11 +311,14 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // Loads past the last k-step read zeros and keep the wait counts uniform.
   // At the barrier of an even step the pair (k + 2, k + 3) may still be in
   // flight; at an odd step the pair holding k + 1 is waited for entirely.
+  // Grouped exponents: every odd step also issues two exponent pieces after
+  // its operand loads, so an even step lets those 10 loads stay in flight.
+  constexpr int kExpPer = kGrouped ? 2 : 0;
   constexpr int kReadsPer = (kReads + (3 * kMfma / 4) - 1) / (3 * kMfma / 4);
-  constexpr int kLoadsPer = (2 * kGroup + kMfma - 1) / kMfma;
+  constexpr int kLoadsPer = (2 * kGroup + kExpPer + kMfma - 1) / kMfma;
   auto step = [&](int k, frags_t& cur, frags_t& nxt, auto odd_t) {
     constexpr bool odd = decltype(odd_t)::value;
-    wait_vm_barrier<odd ? 0 : 2 * kGroup>();
+    wait_vm_barrier<odd ? 0 : 2 * kGroup + kExpPer>();
 #pragma unroll
     for (int i = 0; i < kMfma; ++i) {
       mma_piece(cur, k, i);
@@ -294,20 +329,32 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
 #pragma unroll
         for (int r = 0; r < kLoadsPer; ++r) {
           const int x = i * kLoadsPer + r;     // x / 2 = piece, x % 2 = which k-step
-          if (x < 2 * kGroup) issue_piece(k + 3 + (x & 1), x >> 1);
+          if (x < 2 * kGroup)
+            issue_piece(k + 3 + (x & 1), x >> 1);
+          else if (x < 2 * kGroup + kExpPer)   // group (k - 1) / 4 + 2, pieces 2 ((k >> 1) & 1) + 0, 1
+            issue_exp(((k - 1) >> 2) + 2, 2 * ((k >> 1) & 1) + (x - 2 * kGroup));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // prologue: k-steps 0..3 in two interleaved pairs; stage 0 (all of the
-  // first pair) must land before its fragments are read
+  // prologue: k-steps 0..3 in two interleaved pairs (grouped exponents:
+  // group 0 before them, group 1 after); stage 0 (all of the first pair)
+  // must land before its fragments are read
+  if constexpr (kGrouped) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue_exp(0, p);
+  }
 #pragma unroll
   for (int k0 = 0; k0 < 4; k0 += 2)
 #pragma unroll
     for (int x = 0; x < 2 * kGroup; ++x) issue_piece(k0 + (x & 1), x >> 1);
-  wait_vm_barrier<2 * kGroup>();
+  if constexpr (kGrouped) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue_exp(1, p);
+  }
+  wait_vm_barrier<2 * kGroup + (kGrouped ? 4 : 0)>();
   frags_t f0, f1;
 #pragma unroll
   for (int p = 0; p < kReads; ++p) read_piece(0, f0, p);
