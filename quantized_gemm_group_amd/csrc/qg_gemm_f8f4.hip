@@ -21,16 +21,18 @@
 //
 // Operand pipeline: a k-step covers 64 bytes of every operand row (64 FP8 or
 // 128 FP4 codes).  Operand tiles go from HBM straight into LDS with buffer
-// loads that write LDS (no VGPR round trip), into a ring of 4 stages; the
-// loads of k-steps k + 3 and k + 4 go out together at odd k.  One barrier
+// loads that write LDS (no VGPR round trip), into a ring of 4 stages kept
+// as 2 double stages: the pair of k-steps (2 p, 2 p + 1) is one 128-byte
+// row per operand row, so every load covers 8 rows' whole cache lines.  The
+// loads of the pair (k + 3, k + 4) go out together at odd k.  One barrier
 // per k-step: it certifies that stage k + 1 has landed and that every wave
 // has finished reading the stages of k - 1 and k (whose fragments are
 // already in registers), which may then be refilled.  During k-step k
 // the matrix cores work on fragments already in registers while the
 // fragments of k-step k + 1 are read from LDS.  The compiler does not track
 // the LDS writes of these loads, so the waits for them are explicit.
-// Within a 64-byte row the four 16-byte chunks are stored XOR-swizzled by
-// bits 2..3 of the row, so the 16 rows read by 16 lanes cover all banks.
+// Within a 128-byte row the eight 16-byte chunks are stored XOR-swizzled by
+// bits 1..3 of the row, so the 16 rows read by 16 lanes cover all banks.
 // Workgroups are dispatched round-robin over the 8 XCDs; each XCD is given a
 // contiguous range of tiles walked in column groups, so concurrently running
 // workgroups of one XCD share operand panels in its L2.
@@ -52,6 +54,12 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kOpBytes = BM * BK;   // one operand, one stage: 16 KiB
 constexpr int kStageBytes = 2 * kOpBytes;
+// The ring holds pairs of k-steps (even, odd) as double stages: each operand
+// row's 128 bytes of the pair form one row of 8 16-byte chunks, chunk c of
+// row r stored at position c ^ ((r >> 1) & 7).
+constexpr int kPRow = 2 * BK;             // 128 bytes per row and pair
+constexpr int kDOpBytes = BM * kPRow;     // one operand, one pair: 32 KiB
+constexpr int kDStageBytes = 2 * kDOpBytes;
 // epilogue: each wave's 128 (m) x 64 (n) bf16 piece with a 144-byte row pitch
 // (8-byte LDS writes of 32 rows spread over the banks, 16-byte aligned reads)
 constexpr int kEpiPitch = 144;
@@ -67,8 +75,6 @@ __device__ __forceinline__ void xcd_tile(int bid, int tiles_m, int tiles_n, int*
   tile_coords(lin, tiles_m, tiles_n, 4, tm, tn);
 }
 
-// In a stage operand tile, 16-byte chunk c of row r sits at byte
-// r * BK + ((c ^ ((r >> 2) & 3)) << 4).
 
 template <bool MX, bool SALIGN> struct Frags;
 template <bool SALIGN> struct Frags<false, SALIGN> {
@@ -131,16 +137,20 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (int64_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (int64_t)N * kbytes);
 
-  // Operand loads: wave w fills 1 KiB blocks 2w, 2w+1 (16 rows each) of both
-  // operand tiles; lane i brings row 16 b + i / 4, chunk (i & 3) ^
-  // ((i >> 4) & 3), which lands at LDS position i of the block.
-  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  // Operand loads, one pair of k-steps at a time: wave w brings rows 32 w ..
+  // 32 w + 31 of both operand tiles in 4 loads each (piece j: rows 32 w + 8 j
+  // .. + 7, whole 128-byte lines); lane i brings row 32 w + 8 j + i / 8,
+  // chunk (i & 7) ^ ((row >> 1) & 7) = (i & 7) ^ (4 (j & 1) + (i >> 4)),
+  // which lands at LDS position i of the piece.  Piece j's row offset goes
+  // into the scalar offset, so two voffsets per operand (by j & 1) suffice.
+  int pchunk[2];
   uint32_t voa[2], vow[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 16 * (2 * wave + j) + (lane >> 2);
-    voa[j] = (uint32_t)(m0 + r) * kbytes + dchunk * 16;
-    vow[j] = (uint32_t)(n0 + r) * kbytes + dchunk * 16;
+  for (int jp = 0; jp < 2; ++jp) {
+    pchunk[jp] = (lane & 7) ^ (4 * jp + (lane >> 4));
+    const int r = 32 * wave + (lane >> 3);
+    voa[jp] = (uint32_t)(m0 + r) * kbytes + pchunk[jp] * 16;
+    vow[jp] = (uint32_t)(n0 + r) * kbytes + pchunk[jp] * 16;
   }
   // Exponent loads (MX): wave w brings the exponents of tile rows 64 w .. +63
   // (rows 0..255 of A, then 256..511 of W).  Grouped: lane l reads dword
@@ -156,22 +166,27 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     vos = (uint32_t)grow * kblocks + (kGrouped ? 4 * (lane >> 4) : 0);
   }
 
-  // One load of the k-step group: d < 4 -> operand block 2 w + d / 2 of A
-  // (d even) or W (d odd); then exponent loads (MX).
+  // One load of the pair group (the pair holding k-step k): d < 4 -> operand
+  // piece j = 2 (d >> 1) + (k & 1) of A (d even) or W (d odd), so the 8
+  // operand loads of the two k-steps cover both operands' 4 pieces; then the
+  // per-k-step exponent loads (MX, K not a multiple of 128).
   auto issue_piece = [&](int k, int d) {
-    const int st = k & (kStages - 1);
-    uint8_t* sA = smem + st * kStageBytes;
     if (d < 4) {
-      const int j = d >> 1;
-      const bool kin = KFULL || k * BK + dchunk * 16 < kbytes;   // K tail: whole chunks
-      const int blk = 2 * wave + j;
+      const int pk = k >> 1;
+      uint8_t* sD = smem + (pk & 1) * kDStageBytes + (d & 1) * kDOpBytes;
+      const int j = 2 * (d >> 1) + (k & 1);
+      const int jp = j & 1;
+      const bool kin = KFULL || pk * kPRow + pchunk[jp] * 16 < kbytes;   // K tail: whole chunks
+      const int soff = pk * kPRow + 8 * j * kbytes;
+      lds_void* dst = (lds_void*)(sD + (32 * wave + 8 * j) * kPRow);
       if (d & 1)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(sA + kOpBytes + blk * 1024), 16,
-                                                 kin ? vow[j] : kOutOfRange, k * BK, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, kin ? vow[jp] : kOutOfRange, soff, 0,
+                                                 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + blk * 1024), 16,
-                                                 kin ? voa[j] : kOutOfRange, k * BK, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, kin ? voa[jp] : kOutOfRange, soff, 0,
+                                                 0);
     } else if constexpr (MX && !SALIGN) {
+      const int st = k & (kStages - 1);
       const int j = d - 4;
       uint8_t* ss = sscale + st * kScaleStage;
       lds_void* dst = (lds_void*)(ss + (j * 512 + 64 * wave) * 4);
@@ -199,19 +214,21 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // lane's offset within a group slot for rows r0 + l32 (r0 a multiple of 32)
   const int eoff = (l32 >> 4) * kChunk + (l32 & 15) * 4;
 
-  // LDS read offsets within a stage: the lane's row in the first 32-row tile
-  // of its A rows (wm) and W rows (wn), fragment half c (FP8: chunk 2 lh + c,
-  // MX: chunk 2 c + lh).  The other tiles lie 32 rows (2 KiB) further, and
-  // the row swizzle (r >> 2) & 3 depends only on l32 because every tile
-  // starts at a multiple of 32 rows; so each read is one of these offsets
-  // plus a constant.
-  int offA[2], offW[2];
+  // LDS read offsets within a double stage: the lane's row in the first
+  // 32-row tile of its A rows (wm) and W rows (wn), for k-step parity h and
+  // fragment half c (FP8: chunk 4 h + 2 lh + c, MX: chunk 4 h + 2 c + lh).
+  // The other tiles lie 32 rows (4 KiB) further, and the row swizzle
+  // (r >> 1) & 7 depends only on l32 because every tile starts at a multiple
+  // of 32 rows; so each read is one of these offsets plus a constant.
+  int offA[2][2], offW[2][2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch = (MX ? 2 * c + lh : 2 * lh + c) ^ ((l32 >> 2) & 3);
-    offA[c] = (wm * 128 + l32) * BK + (ch << 4);
-    offW[c] = kOpBytes + (wn * 64 + l32) * BK + (ch << 4);
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = (4 * h + (MX ? 2 * c + lh : 2 * lh + c)) ^ ((l32 >> 1) & 7);
+      offA[h][c] = (wm * 128 + l32) * kPRow + (ch << 4);
+      offW[h][c] = kDOpBytes + (wn * 64 + l32) * kPRow + (ch << 4);
+    }
 
   typedef Frags<MX, SALIGN> frags_t;
   // Fragment reads of k-step k, in the order the MFMAs consume them: entry
@@ -219,16 +236,17 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   constexpr int kOrd[6] = {4, 0, 1, 2, 3, 5};
   constexpr int kEWords = kGrouped ? 1 : kSWords;   // exponent reads per row and k-step
   constexpr int kReads = MX ? 12 + 6 * kEWords : 12;
-  auto read_piece = [&](int k, frags_t& f, int p) {
+  auto read_piece = [&](int k, frags_t& f, int p, auto hpar) {
+    constexpr int H = decltype(hpar)::value;   // k & 1
     const int st = k & (kStages - 1);
-    const uint8_t* sA = smem + st * kStageBytes;
+    const uint8_t* sA = smem + ((k >> 1) & 1) * kDStageBytes;
     if constexpr (!MX) {
       // the lane holds bytes 32 * lh .. +32 of the k-step's 64 for its row
       // (half h = 16 of them); both operands use the same byte -> k map
       const int e = kOrd[p >> 1], h = p & 1;
       const bool isw = e >= 4;
       const u32x4 v = *reinterpret_cast<const u32x4*>(
-          sA + (isw ? offW[h] + (e - 4) * 32 * BK : offA[h] + e * 32 * BK));
+          sA + (isw ? offW[H][h] + (e - 4) * 32 * kPRow : offA[H][h] + e * 32 * kPRow));
       i32x8& dst = isw ? f.w[e - 4] : f.a[e];
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[4 * h + i] = (int)v[i];
@@ -259,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
         const int sub = q / 6, e = kOrd[q % 6];
         const bool isw = e >= 4;
         const i32x4 v = *reinterpret_cast<const i32x4*>(
-            sA + (isw ? offW[sub] + (e - 4) * 32 * BK : offA[sub] + e * 32 * BK));
+            sA + (isw ? offW[H][sub] + (e - 4) * 32 * kPRow : offA[H][sub] + e * 32 * kPRow));
         if (isw)
           f.w[sub][e - 4] = v;
         else
@@ -324,7 +342,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
       mma_piece(cur, k, i);
 #pragma unroll
       for (int r = 0; r < kReadsPer; ++r)
-        if (i * kReadsPer + r < kReads) read_piece(k + 1, nxt, i * kReadsPer + r);
+        if (i * kReadsPer + r < kReads)
+          read_piece(k + 1, nxt, i * kReadsPer + r, std::integral_constant<int, odd ? 0 : 1>{});
       if constexpr (odd) {
 #pragma unroll
         for (int r = 0; r < kLoadsPer; ++r) {
@@ -357,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   wait_vm_barrier<2 * kGroup + (kGrouped ? 4 : 0)>();
   frags_t f0, f1;
 #pragma unroll
-  for (int p = 0; p < kReads; ++p) read_piece(0, f0, p);
+  for (int p = 0; p < kReads; ++p) read_piece(0, f0, p, std::integral_constant<int, 0>{});
   int k = 0;
   for (; k + 1 < nk; k += 2) {
     step(k, f0, f1, std::false_type{});
