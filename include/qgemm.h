@@ -165,6 +165,8 @@ qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
  *       (group == K): a_scales fp32 [M], wscales fp32 [N].
  *   W INT8_SYM|INT8_ASYM, A INT8_SYM|INT8_ASYM : INT8 W8A8 ([SRV] 1.2;
  *       [L6] section 3 cross terms); per-row scales/zeros (group == K).
+ *       The integer sums are exact for every accepted K (int32 runs of
+ *       at most 65536 elements folded into fp64).
  *   y          bf16 [M][N].
  * Errors: QG_ERR_GEOMETRY (M, N, K < 1; K % 128 for W4A16; K % 16 for the
  * 8-bit formats; group), QG_ERR_FORMAT, QG_ERR_UNSUPPORTED (also when an

@@ -1,8 +1,10 @@
 """Python binding of the C ABI: the same operations, torch tensors in and out.
 
-Marshalling only: every function checks tensor placement and dtypes,
-allocates its outputs with torch on the input's device, and makes ONE call
-into libqgemm.so on the current HIP stream.  No arithmetic of the method
+Marshalling only: every function checks tensor placement, dtypes and
+shapes (the C ABI takes raw pointers and sizes, so a mis-shaped operand or
+output cannot be detected past this layer), allocates its outputs with torch
+on the input's device, and makes ONE call into libqgemm.so on the current
+HIP stream.  No arithmetic of the method
 happens here.
 """
 
@@ -48,6 +50,49 @@ def _src_dtype(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return _lib.F32
     raise ValueError("source must be bf16 or fp32")
+
+
+def _expect(t, shape, dtype, what: str, dev=None):
+    """Raise ValueError unless t is a contiguous tensor of exactly this shape
+    and dtype (on dev when given).  The C ABI takes raw pointers and sizes,
+    so a mis-shaped operand cannot be detected past this point."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what} must be a tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be {dtype} of shape {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{what} must be on {dev}, got {t.device}")
+
+
+def _expect_rows(t, rows: int, what: str, dev=None):
+    """A per-row fp32 vector of `rows` values: shape [rows] or [rows][1]."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or \
+            tuple(t.shape) not in ((rows,), (rows, 1)):
+        raise ValueError(f"{what} must be fp32 of shape [{rows}] or [{rows}][1]")
+    _expect(t, t.shape, torch.float32, what, dev)
+
+
+def _expect_none(t, what: str):
+    if t is not None:
+        raise ValueError(f"{what} must be None for this format")
+
+
+def _weights(fmt: str, codes, scales, zeros, n: int, k: int, group: int, dev):
+    """The stored operand of quantize_pack: codes, scales (+ zeros)."""
+    if fmt not in FORMATS or fmt in ("bf16", "mxfp4"):
+        raise ValueError(f"unknown weight format {fmt}")
+    if group <= 0 or k % group:
+        raise ValueError("invalid quantization geometry: group must divide K")
+    cshape, cdt, sdt = _code_shapes(fmt, n, k, group)
+    _expect(codes, cshape, cdt, "weight codes", dev)
+    _expect(scales, (n, k // group), sdt, "weight scales", dev)
+    if fmt in _ASYM:
+        _expect(zeros, (n, k // group), sdt, "weight zeros", dev)
+    else:
+        _expect_none(zeros, "weight zeros")
 
 
 def _code_shapes(fmt: str, rows: int, k: int, group: int):
@@ -98,10 +143,10 @@ def norm_quant(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None =
         raise ValueError(f"unknown normalization {norm}")
     if fmt not in ("fp8_e4m3", "int8_sym", "int8_asym"):
         raise ValueError(f"norm_quant: unsupported format {fmt}")
-    for t in (gamma, beta):
-        if t is not None and (t.dtype != torch.float32 or _dev(t) != dev):
-            raise ValueError("gamma and beta must be fp32 tensors on the input's device")
     rows, k = x.shape
+    for t, what in ((gamma, "gamma"), (beta, "beta")):
+        if t is not None:
+            _f32_vec(t, dev, k, what)
     cshape, cdt, sdt = _code_shapes(fmt, rows, k, k)
     codes = torch.empty(cshape, dtype=cdt, device=dev)
     scales = torch.empty((rows, 1), dtype=sdt, device=dev)
@@ -115,14 +160,23 @@ def norm_quant(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None =
 def dequant(codes: torch.Tensor, scales: torch.Tensor, zeros, fmt: str, k: int,
             group: int | None = None, out_dtype=torch.float32) -> torch.Tensor:
     """x_hat = s * (q - z) (or 2^e * e2m1 for "mxfp4") as [rows][K]."""
-    lib = _lib.load()
-    dev = _dev(codes)
+    dev = codes.device        # checked for the GPU below, after the shapes
     rows = codes.shape[0]
     group = (32 if fmt == "mxfp4" else default_group(fmt, k)) if group is None else group
-    out = torch.empty((rows, k), dtype=out_dtype, device=dev)
-    dt = _lib.BF16 if out_dtype == torch.bfloat16 else _lib.F32
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out_dtype must be bf16 or fp32")
+    if fmt == "mxfp4":
+        if group != 32 or k % 32:
+            raise ValueError("invalid quantization geometry: MX blocks are 32 elements")
+        _expect(codes, (rows, k // 2), torch.uint8, "codes", dev)
+        _expect(scales, (rows, k // 32), torch.uint8, "e8m0 scales", dev)
+        _expect_none(zeros, "zeros")
+    else:
+        _weights(fmt, codes, scales, zeros, rows, k, group, dev)
+    _dev(codes)
+    lib = _lib.load()
+    out = torch.empty((rows, k), dtype=out_dtype, device=dev)
+    dt = _lib.BF16 if out_dtype == torch.bfloat16 else _lib.F32
     _lib.check(lib.qg_dequant(FORMATS[fmt], _ptr(codes), _ptr(scales), _ptr(zeros), rows, k,
                               group, _ptr(out), dt, _stream(dev)))
     return out
@@ -131,12 +185,18 @@ def dequant(codes: torch.Tensor, scales: torch.Tensor, zeros, fmt: str, k: int,
 def qgemv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, zeros, fmt: str,
           group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
     """W4A16 decode product y = x * dequant(W)^T for 1 <= M <= 16; x bf16 [M][K]."""
-    lib = _lib.load()
-    dev = _dev(x)
-    if x.dtype != torch.bfloat16:
-        raise ValueError("x must be bf16")
+    dev = x.device        # checked for the GPU below, after the shapes
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be bf16 [M][K]")
+    if not fmt.startswith("int4"):
+        raise ValueError("qgemv: weights must be int4_sym or int4_asym")
     m, k = x.shape
     n = codes.shape[0]
+    _weights(fmt, codes, scales, zeros, n, k, group, dev)
+    if out is not None:
+        _expect(out, (m, n), torch.bfloat16, "out", dev)
+    _dev(x)
+    lib = _lib.load()
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
     _lib.check(lib.qg_qgemv(FORMATS[fmt], _ptr(x), m, _ptr(codes), _ptr(scales), _ptr(zeros),
                             n, k, group, _ptr(y), _stream(dev)))
@@ -148,12 +208,38 @@ def qgemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_zero
           group: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """Quantized GEMM y = dequant(a) * dequant(W)^T with bf16 output.
     Pairs: (int4_*, "bf16"), ("fp8_e4m3", "fp8_e4m3"), (int8_*, int8_*)."""
-    lib = _lib.load()
-    dev = _dev(a)
+    dev = a.device        # checked for the GPU below, after the shapes
+    if a.dim() != 2:
+        raise ValueError("a must be [M][K]")
     m = a.shape[0]
-    k = a.shape[1] if k is None else k
+    if k is not None and k != a.shape[1]:
+        raise ValueError("k must equal a.shape[1]")
+    k = a.shape[1]
     n = w_codes.shape[0]
     group = default_group(wfmt, k) if group is None else group
+    pair = ((wfmt in ("int4_sym", "int4_asym") and afmt == "bf16")
+            or (wfmt == "fp8_e4m3" and afmt == "fp8_e4m3")
+            or (wfmt in ("int8_sym", "int8_asym") and afmt in ("int8_sym", "int8_asym")))
+    if not pair:
+        pass                      # the library reports the unsupported pair (QG_ERR_FORMAT)
+    elif afmt == "bf16":
+        _weights(wfmt, w_codes, w_scales, w_zeros, n, k, group, dev)
+        if a.dtype != torch.bfloat16:
+            raise ValueError("a must be bf16 for bf16 activations")
+        _expect_none(a_scales, "a_scales")
+        _expect_none(a_zeros, "a_zeros")
+    else:
+        _weights(wfmt, w_codes, w_scales, w_zeros, n, k, group, dev)
+        _expect(a, (m, k), _code_shapes(afmt, m, k, k)[1], "a (activation codes)", dev)
+        _expect_rows(a_scales, m, "a_scales", dev)
+        if afmt in _ASYM:
+            _expect_rows(a_zeros, m, "a_zeros", dev)
+        else:
+            _expect_none(a_zeros, "a_zeros")
+    if out is not None:
+        _expect(out, (m, n), torch.bfloat16, "out", dev)
+    _dev(a)
+    lib = _lib.load()
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
     _lib.check(lib.qg_qgemm(FORMATS[wfmt], FORMATS[afmt], _ptr(a), _ptr(a_scales), _ptr(a_zeros),
                             m, _ptr(w_codes), _ptr(w_scales), _ptr(w_zeros), n, k, group,
@@ -166,12 +252,20 @@ def qgemm_swiglu(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     """Fused SwiGLU projection h = SiLU(a W_gate^T) * (a W_up^T) with bf16 a
     [M][K] and INT4 weights quantized as the [2I][K] concatenation
     [W_gate; W_up].  Returns h bf16 [M][I]."""
-    lib = _lib.load()
-    dev = _dev(a)
-    if a.dtype != torch.bfloat16:
-        raise ValueError("a must be bf16")
+    dev = a.device        # checked for the GPU below, after the shapes
+    if a.dtype != torch.bfloat16 or a.dim() != 2:
+        raise ValueError("a must be bf16 [M][K]")
+    if not wfmt.startswith("int4"):
+        raise ValueError("qgemm_swiglu: weights must be int4_sym or int4_asym")
     m, k = a.shape
     n2 = w_codes.shape[0]
+    if n2 % 2:
+        raise ValueError("invalid quantization geometry: [W_gate; W_up] needs an even row count")
+    _weights(wfmt, w_codes, w_scales, w_zeros, n2, k, group, dev)
+    if out is not None:
+        _expect(out, (m, n2 // 2), torch.bfloat16, "out", dev)
+    _dev(a)
+    lib = _lib.load()
     h = torch.empty((m, n2 // 2), dtype=torch.bfloat16, device=dev) if out is None else out
     _lib.check(lib.qg_qgemm_swiglu(FORMATS[wfmt], FORMATS["bf16"], _ptr(a), m, _ptr(w_codes),
                                    _ptr(w_scales), _ptr(w_zeros), n2, k, group, _ptr(h),
@@ -197,10 +291,21 @@ def mx_quant(x: torch.Tensor):
 def mx_gemm(a_codes: torch.Tensor, a_e8m0: torch.Tensor, b_codes: torch.Tensor,
             b_e8m0: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Block-scaled MXFP4 product y = A * B^T (both [rows][K] in MX form), bf16."""
-    lib = _lib.load()
-    dev = _dev(a_codes)
+    dev = a_codes.device        # checked for the GPU below, after the shapes
+    if a_codes.dim() != 2 or b_codes.dim() != 2:
+        raise ValueError("MX codes must be [rows][K/2]")
     m, kh = a_codes.shape
     n = b_codes.shape[0]
+    if (2 * kh) % 32:
+        raise ValueError("invalid quantization geometry: K must be a multiple of 32")
+    _expect(a_codes, (m, kh), torch.uint8, "a_codes", dev)
+    _expect(a_e8m0, (m, 2 * kh // 32), torch.uint8, "a_e8m0", dev)
+    _expect(b_codes, (n, kh), torch.uint8, "b_codes", dev)
+    _expect(b_e8m0, (n, 2 * kh // 32), torch.uint8, "b_e8m0", dev)
+    if out is not None:
+        _expect(out, (m, n), torch.bfloat16, "out", dev)
+    _dev(a_codes)
+    lib = _lib.load()
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
     _lib.check(lib.qg_mx_gemm(_ptr(a_codes), _ptr(a_e8m0), m, _ptr(b_codes), _ptr(b_e8m0), n,
                               2 * kh, _ptr(y), _stream(dev)))

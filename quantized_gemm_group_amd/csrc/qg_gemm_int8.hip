@@ -10,6 +10,12 @@
 // staging (q - 128), which shifts the zero point to z - 128; the row sums of
 // the codes come from extra MFMAs against an all-ones operand.  The integer
 // combination is formed in fp64 (exact for the integer terms) and scaled once.
+//
+// Exactness of the int32 sums: one 128-element k-block adds at most
+// 128 * 128^2 = 2^21 in magnitude to a product sum and 2^14 to a row sum, so
+// 512 blocks (K = 65536) stay below 2^30.  Longer K (LONGK) folds the int32
+// sums into fp64 accumulators every 512 blocks and restarts them at zero;
+// fp64 holds every such integer sum exactly (|sum| < 2^53 for K < 2^39).
 
 #include "qg_gemm_common.hpp"
 #include "qg_internal.hpp"
@@ -18,8 +24,9 @@ namespace qg {
 namespace {
 
 constexpr int BM = 128, BN = 128, BKB = 128;
+constexpr int kFoldBlocks = 512;           // k-blocks per exact int32 run
 
-template <bool AASYM, bool WASYM>
+template <bool AASYM, bool WASYM, bool LONGK>
 __global__ __launch_bounds__(256) void gemm_i8_kernel(const uint8_t* __restrict__ A,
                                                       const float* __restrict__ sa,
                                                       const float* __restrict__ za, int M,
@@ -88,6 +95,36 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const uint8_t* __restrict_
     for (int b = 0; b < 4; ++b) acc[a][b] = i32x4{0, 0, 0, 0};
   }
   const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  // fp64 totals of the folded int32 runs (LONGK only)
+  double dacc[4][4][4], dsum_a[4], dsum_w[4][4];
+  if constexpr (LONGK) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      dsum_a[a] = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dsum_w[a][r] = 0.0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dacc[a][b][r] = 0.0;
+    }
+  }
+  auto fold = [&]() {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      dsum_a[a] += (double)rsum_a[a][0];
+      rsum_a[a] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dsum_w[a][r] += (double)rsum_w[a][r];
+      rsum_w[a] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dacc[a][b][r] += (double)acc[a][b][r];
+        acc[a][b] = i32x4{0, 0, 0, 0};
+      }
+    }
+  };
 
   gload(0);
   lstore();
@@ -115,6 +152,9 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const uint8_t* __restrict_
       }
     }
     __syncthreads();
+    if constexpr (LONGK) {
+      if (kb % kFoldBlocks == kFoldBlocks - 1 || kb == nk - 1) fold();
+    }
     if (kb + 1 < nk) {
       lstore();
       __syncthreads();
@@ -127,7 +167,8 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const uint8_t* __restrict_
     const bool mok = m < M;
     const double sam = mok ? (double)sa[m] : 0.0;
     const double zam = (AASYM && mok) ? (double)za[m] - 128.0 : 0.0;
-    const double sum_a = (double)rsum_a[t][0];          // sum_k qa[m][k] (all rows equal)
+    // sum_k qa[m][k] (all rows of the MFMA result are equal)
+    const double sum_a = LONGK ? dsum_a[t] : (double)rsum_a[t][0];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int n = n0 + wn * 64 + u * 16 + 4 * lg;
@@ -137,8 +178,9 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const uint8_t* __restrict_
         const bool nok = n + r < N;
         const double swn = nok ? (double)sw[n + r] : 0.0;
         const double zwn = (WASYM && nok) ? (double)zw[n + r] - 128.0 : 0.0;
-        const double sum_w = (double)rsum_w[u][r];      // sum_k qw[n+r][k]
-        const double val = (double)acc[u][t][r] - zwn * sum_a - zam * sum_w + (double)K * zam * zwn;
+        const double sum_w = LONGK ? dsum_w[u][r] : (double)rsum_w[u][r];   // sum_k qw[n+r][k]
+        const double dot = LONGK ? dacc[u][t][r] : (double)acc[u][t][r];
+        const double val = dot - zwn * sum_a - zam * sum_w + (double)K * zam * zwn;
         v[r] = (float)(val * sam * swn);
       }
       store_out4(Y, M, N, m, n, v[0], v[1], v[2], v[3]);
@@ -150,9 +192,16 @@ template <bool AA, bool WA>
 void launch_t(const void* a, const void* sa, const void* za, int64_t M, const void* w,
               const void* sw, const void* zw, int64_t N, int64_t K, void* y, hipStream_t s) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_i8_kernel<AA, WA>), dim3(tiles), dim3(256), 0, s, (const uint8_t*)a,
-                     (const float*)sa, (const float*)za, (int)M, (const uint8_t*)w,
-                     (const float*)sw, (const float*)zw, (int)N, (int)K, (uint16_t*)y);
+  if (K > (int64_t)kFoldBlocks * BKB)
+    hipLaunchKernelGGL((gemm_i8_kernel<AA, WA, true>), dim3(tiles), dim3(256), 0, s,
+                       (const uint8_t*)a, (const float*)sa, (const float*)za, (int)M,
+                       (const uint8_t*)w, (const float*)sw, (const float*)zw, (int)N, (int)K,
+                       (uint16_t*)y);
+  else
+    hipLaunchKernelGGL((gemm_i8_kernel<AA, WA, false>), dim3(tiles), dim3(256), 0, s,
+                       (const uint8_t*)a, (const float*)sa, (const float*)za, (int)M,
+                       (const uint8_t*)w, (const float*)sw, (const float*)zw, (int)N, (int)K,
+                       (uint16_t*)y);
 }
 
 }  // namespace

@@ -215,3 +215,61 @@ def test_kv_cache_store_validation(lib):
     # no tokens: valid, nothing is enqueued (no HIP call is made)
     assert k(None, _lib.BF16, 0, 8, 128, A16b, 64, None, A16c, A16d, None) == _lib.OK
     assert k(None, _lib.BF16, 0, 8, 128, None, 64, None, A16c, A16d, None) == _lib.OK
+
+
+def test_binding_rejects_mismatched_operands_before_any_call():
+    # the binding checks shapes, dtypes and outputs before it touches the
+    # library (the C ABI cannot see tensor extents); CPU tensors suffice
+    # because the device check comes after the shapes
+    import torch
+    import quantized_gemm_group_amd as qg
+    m, k, n = 2, 256, 16
+    x = torch.zeros((m, k), dtype=torch.bfloat16)
+    codes = torch.zeros((n, k // 8), dtype=torch.int32)
+    s = torch.zeros((n, k // 128), dtype=torch.float16)
+    z = torch.zeros((n, k // 128), dtype=torch.float16)
+    y = torch.zeros((m, n), dtype=torch.bfloat16)
+
+    def bad(match, fn, *a, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    # well formed: only the device check is left
+    bad("must live on the GPU", qg.qgemv, x, codes, s, z, "int4_asym", out=y)
+    bad("out must be", qg.qgemv, x, codes, s, z, "int4_asym", out=y[:, :8])
+    bad("out must be", qg.qgemv, x, codes, s, z, "int4_asym", out=y.float())
+    bad("weight codes", qg.qgemv, x, codes[:, :16], s, z, "int4_asym")
+    bad("weight codes", qg.qgemv, torch.zeros((m, 2 * k), dtype=torch.bfloat16), codes, s, z,
+        "int4_asym")
+    bad("weight scales", qg.qgemv, x, codes, s[:, :1], z, "int4_asym")
+    bad("weight scales", qg.qgemv, x, codes, s.float(), z, "int4_asym")
+    bad("weight zeros", qg.qgemv, x, codes, s, None, "int4_asym")
+    bad("weight zeros must be None", qg.qgemv, x, codes, s, z, "int4_sym")
+    bad("x must be bf16", qg.qgemv, x.float(), codes, s, z, "int4_asym")
+    bad("weight scales", qg.qgemm, x, codes[:8], s, z, "int4_asym", "bf16")
+    bad("a_scales must be None", qg.qgemm, x, codes, s, z, "int4_asym", "bf16",
+        a_scales=torch.ones(m))
+    bad("must live on the GPU", qg.qgemm, x, codes, s, z, "int4_asym", "bf16", out=y)
+    # FP8 W8A8: per-row scales of both operands
+    a8 = torch.zeros((m, k), dtype=torch.uint8)
+    w8 = torch.zeros((n, k), dtype=torch.uint8)
+    ws, as_ = torch.ones((n, 1)), torch.ones((m, 1))
+    bad("must live on the GPU", qg.qgemm, a8, w8, ws, None, "fp8_e4m3", "fp8_e4m3", a_scales=as_)
+    bad("a_scales", qg.qgemm, a8, w8, ws, None, "fp8_e4m3", "fp8_e4m3", a_scales=as_[:1])
+    bad("a_scales", qg.qgemm, a8, w8, ws, None, "fp8_e4m3", "fp8_e4m3", a_scales=None)
+    bad("weight scales", qg.qgemm, a8, w8, ws[:4], None, "fp8_e4m3", "fp8_e4m3", a_scales=as_)
+    bad("weight codes", qg.qgemm, a8, w8[:, :128], ws, None, "fp8_e4m3", "fp8_e4m3", a_scales=as_)
+    bad("activation codes", qg.qgemm, a8.to(torch.int8), w8, ws, None, "fp8_e4m3", "fp8_e4m3",
+        a_scales=as_)
+    bad("a_zeros", qg.qgemm, a8, w8.to(torch.int8), ws, None, "int8_sym", "int8_asym",
+        a_scales=as_)
+    # SwiGLU and MXFP4
+    bad("out must be", qg.qgemm_swiglu, x, codes, s, None, "int4_sym", out=y)
+    bad("even row count", qg.qgemm_swiglu, x, codes[:15], s[:15], None, "int4_sym")
+    mc, me = torch.zeros((m, k // 2), dtype=torch.uint8), torch.zeros((m, k // 32), dtype=torch.uint8)
+    bc, be = torch.zeros((n, k // 2), dtype=torch.uint8), torch.zeros((n, k // 32), dtype=torch.uint8)
+    bad("must live on the GPU", qg.mx_gemm, mc, me, bc, be, out=y)
+    bad("b_e8m0", qg.mx_gemm, mc, me, bc, be[:, :4])
+    bad("a_e8m0", qg.mx_gemm, mc, me[:1], bc, be)
+    bad("out must be", qg.mx_gemm, mc, me, bc, be, out=y.t())
+    bad("codes", qg.dequant, codes[:, :4], s, z, "int4_asym", k)

@@ -173,6 +173,40 @@ def test_int8_gemm_4096_sampled():
     check(y[np.ix_(rm, rn)], ref, "int8 4096")
 
 
+@pytest.mark.parametrize("fmt", ["int8_sym", "int8_asym"])
+def test_int8_gemm_long_k_stays_exact(fmt):
+    # K = 262144 with constant extreme codes: the product sums reach 2^32,
+    # past int32 (one int32 run may hold 512 k-blocks of 128; the kernel
+    # folds longer sums into fp64)
+    dev = device()
+    k = 262144
+    rng = rng_for(45)
+    if fmt == "int8_sym":
+        lo, hi, dt = -127, 127, np.int8
+        a = np.stack([np.full(k, lo), rng.integers(lo, hi + 1, k), np.full(k, hi)]).astype(dt)
+        w = np.stack([np.full(k, lo), np.full(k, hi), rng.integers(lo, hi + 1, k),
+                      np.where(np.arange(k) % 2 == 0, lo, hi)]).astype(dt)
+        az = wz = None
+    else:
+        lo, hi, dt = 0, 255, np.uint8
+        a = np.stack([np.full(k, lo), rng.integers(lo, hi + 1, k), np.full(k, hi)]).astype(dt)
+        w = np.stack([np.full(k, lo), np.full(k, hi), rng.integers(lo, hi + 1, k),
+                      np.where(np.arange(k) % 2 == 0, lo, hi)]).astype(dt)
+        az = np.array([255.0, 128.0, 0.0], dtype=np.float32)
+        wz = np.array([255.0, 0.0, 100.0, 7.0], dtype=np.float32)
+    a_s = np.array([1.0 / 127, 2.0 ** -10, 3.0e-3], dtype=np.float32)
+    w_s = np.array([2.0 ** -12, 1.0 / 255, 5.0e-4, 2.0 ** -9], dtype=np.float32)
+    print(f"int8 gemm long K={k} {fmt}", flush=True)
+    t = lambda v: to_dev(v, dev)
+    y = host(qg.qgemm(t(a), t(w), t(w_s), None if wz is None else t(wz), fmt, fmt,
+                      a_scales=t(a_s), a_zeros=None if az is None else t(az)))
+    ref = og.int8_reference(a.astype(np.int64), a_s, az, w.astype(np.int64), w_s, wz)
+    # the constant rows' exact products (e.g. 262144 * 127^2 > 2^31) are
+    # what a wrapped int32 sum would get wrong
+    assert abs(ref[0, 0]) > 1.0
+    check(y, ref, f"int8 long K {fmt}")
+
+
 # --------------------------------------------------------------- W4A16 prefill
 
 # groups of 128 per row G = 1, 2, 3, 5, 7, 8, 11, 12, 16: the k-loop runs in
