@@ -27,7 +27,9 @@
  *   [MX]   《大模型量化推理引擎全景大复盘》 section 2 eq. 3 (32 four-bit
  *          elements share one E8M0 exponent), section 3 code (shared scale
  *          2^ceil(log2(max|x|/6))).
- *   [CH1]  《第 1 章：推理加速全景》 section 4.1 (uniform quantization math),
+ *   [CH1]  《第 1 章：推理加速全景》 section 1.5 (the roofline: attainable
+ *          throughput = min(bandwidth x intensity, peak); calibration
+ *          probes), section 4.1 (uniform quantization math),
  *          section 4.3 (SmoothQuant: X W = (X diag(s)^-1)(diag(s) W),
  *          s_j = max|X_j|^alpha / max|W_j|^(1-alpha)).
  *   [Q&A] also its KV-cache section (keys per channel, values per token).
@@ -341,6 +343,43 @@ qg_status qg_norm_quant(qg_norm norm, qg_format fmt, const void* src, qg_dtype s
 qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
                      const void* b_codes, const void* b_e8m0, int64_t N, int64_t K,
                      void* y, void* stream);
+
+/*
+ * Roofline calibration (measurement only, not a step of the method): the two
+ * roofs of [CH1] section 1.5 (attainable = min(bandwidth x intensity, peak))
+ * as measured on this GPU, reported beside the published peaks.
+ *
+ * qg_calib_stream_read -- reads `bytes` of device memory once: workgroup c
+ * reads the contiguous 64 KiB chunk c with 16-byte loads, all in flight at
+ * once, and writes the XOR of the chunk's 32-bit words to sink[c].
+ *   src        device memory, 16-byte aligned, `bytes` long.
+ *   bytes      a positive multiple of 65536, at most 2^40.
+ *   sink       uint32 [bytes / 65536], 4-byte aligned (owned by the caller).
+ * Errors: QG_ERR_GEOMETRY, QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_HIP.
+ *
+ * qg_calib_mfma -- `waves` waves each issue `iters` x 8 back-to-back 32x32
+ * matrix instructions (four independent accumulators, no memory traffic in
+ * the loop) on pseudo-random finite operands whose mantissa bits change
+ * every iteration; lane l of the grid writes the sum of its accumulators to
+ * sink[l].  Work per launch: waves x iters x 8 x 2 x 32 x 32 x Kc operations
+ * with Kc = 16 (QG_CALIB_BF16), 64 (QG_CALIB_FP8, QG_CALIB_FP4 on the scaled
+ * f8f6f4 instruction with per-lane unit-range scales) or 32 (QG_CALIB_INT8).
+ *   waves      a positive multiple of 4, at most 2^20; iters 1 .. 2^24.
+ *   sink       fp32 [waves x 64], 4-byte aligned.
+ * Errors: QG_ERR_FORMAT (kind), QG_ERR_GEOMETRY, QG_ERR_NULL, QG_ERR_ALIGN,
+ * QG_ERR_HIP.
+ */
+typedef enum {
+    QG_CALIB_BF16 = 0,
+    QG_CALIB_FP8 = 1,
+    QG_CALIB_FP4 = 2,
+    QG_CALIB_INT8 = 3
+} qg_calib_kind;
+
+qg_status qg_calib_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
+qg_status qg_calib_mfma(qg_calib_kind kind, int64_t waves, int64_t iters, float* sink,
+                        void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* qg_status_str(qg_status status);

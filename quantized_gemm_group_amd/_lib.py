@@ -18,6 +18,8 @@ INT4_SYM, INT4_ASYM, INT8_SYM, INT8_ASYM, FP8_E4M3, BF16_ACT, MXFP4 = range(7)
 BF16, F32 = 0, 1
 # qg_norm
 NORM_LAYER, NORM_RMS = 0, 1
+# qg_calib_kind
+CALIB_BF16, CALIB_FP8, CALIB_FP4, CALIB_INT8 = range(4)
 # qg_status
 OK, ERR_GEOMETRY, ERR_ALIGN, ERR_FORMAT, ERR_NULL, ERR_HIP, ERR_UNSUPPORTED = range(7)
 
@@ -25,7 +27,7 @@ EXPORTS = [
     "qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant", "qg_mx_gemm",
     "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth", "qg_channel_absmax",
     "qg_smooth_scales", "qg_channel_scales", "qg_kv_cache_store", "qg_status_str",
-    "qg_last_error", "qg_abi_version",
+    "qg_last_error", "qg_abi_version", "qg_calib_stream_read", "qg_calib_mfma",
 ]
 
 _lib = None
@@ -56,10 +58,12 @@ def load() -> ctypes.CDLL:
     lib.qg_smooth_scales.argtypes = [vp, vp, ctypes.c_float, i64, vp, vp]
     lib.qg_channel_scales.argtypes = [vp, i64, ctypes.c_float, vp, vp]
     lib.qg_kv_cache_store.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+    lib.qg_calib_stream_read.argtypes = [vp, i64, vp, vp]
+    lib.qg_calib_mfma.argtypes = [i32, i64, i64, vp, vp]
     for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
                  "qg_mx_gemm", "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth",
                  "qg_channel_absmax", "qg_smooth_scales", "qg_channel_scales",
-                 "qg_kv_cache_store"]:
+                 "qg_kv_cache_store", "qg_calib_stream_read", "qg_calib_mfma"]:
         getattr(lib, name).restype = i32
     lib.qg_status_str.argtypes = [i32]
     lib.qg_status_str.restype = ctypes.c_char_p

@@ -406,3 +406,39 @@ def kv_cache_store(x: torch.Tensor, slot_mapping: torch.Tensor, cache_codes: tor
     _lib.check(lib.qg_kv_cache_store(_ptr(x), _src_dtype(x), t, h, d, _ptr(slot_mapping), slots,
                                      _ptr(channel_scales), _ptr(cache_codes), _ptr(cache_scales),
                                      _stream(dev)))
+
+
+# ------------------------------------------------ roofline calibration
+
+CALIB_KINDS = {"bf16": _lib.CALIB_BF16, "fp8": _lib.CALIB_FP8, "fp4": _lib.CALIB_FP4,
+               "int8": _lib.CALIB_INT8}
+CALIB_K = {"bf16": 16, "fp8": 64, "fp4": 64, "int8": 32}
+
+
+def calib_stream_read(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Read-only stream over src (bytes a multiple of 64 KiB): returns the XOR
+    of each 64 KiB chunk's 32-bit words, uint32 as int32 [bytes / 65536]."""
+    dev = _dev(src)
+    nbytes = src.numel() * src.element_size()
+    if nbytes < 65536 or nbytes % 65536:
+        raise ValueError("calib_stream_read: the tensor must hold a multiple of 64 KiB")
+    if out is None:
+        out = torch.empty(nbytes // 65536, dtype=torch.int32, device=dev)
+    else:
+        _expect(out, (nbytes // 65536,), torch.int32, "out", dev)
+    lib = _lib.load()
+    _lib.check(lib.qg_calib_stream_read(_ptr(src), nbytes, _ptr(out), _stream(dev)))
+    return out
+
+
+def calib_mfma(kind: str, waves: int, iters: int, out: torch.Tensor, ) -> torch.Tensor:
+    """MFMA-only loop of `kind` ("bf16", "fp8", "fp4", "int8"); out fp32
+    [waves * 64] on the GPU receives one checksum per lane.  Operations per
+    launch: waves * iters * 8 * 2 * 32 * 32 * CALIB_K[kind]."""
+    dev = _dev(out)
+    if kind not in CALIB_KINDS:
+        raise ValueError(f"unknown calibration kind {kind}")
+    _expect(out, (waves * 64,), torch.float32, "out", dev)
+    lib = _lib.load()
+    _lib.check(lib.qg_calib_mfma(CALIB_KINDS[kind], waves, iters, _ptr(out), _stream(dev)))
+    return out

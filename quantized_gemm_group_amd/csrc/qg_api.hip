@@ -349,4 +349,26 @@ qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M, const v
                                      (hipStream_t)stream));
 }
 
+qg_status qg_calib_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 65536 || bytes % 65536 != 0 || bytes > ((int64_t)1 << 40))
+    return fail(QG_ERR_GEOMETRY, "calib_stream_read: bytes a positive multiple of 65536");
+  if (!src || !sink) return fail(QG_ERR_NULL, "calib_stream_read: src and sink are required");
+  if (!aligned16(src) || !aligned_to(sink, 4))
+    return fail(QG_ERR_ALIGN, "calib_stream_read: src 16-byte, sink 4-byte aligned");
+  return from_hip(qg::launch_calib_stream_read(src, bytes, sink, (hipStream_t)stream));
+}
+
+qg_status qg_calib_mfma(qg_calib_kind kind, int64_t waves, int64_t iters, float* sink,
+                        void* stream) {
+  if (kind != QG_CALIB_BF16 && kind != QG_CALIB_FP8 && kind != QG_CALIB_FP4 &&
+      kind != QG_CALIB_INT8)
+    return fail(QG_ERR_FORMAT, "calib_mfma: unknown kind");
+  if (waves < 4 || waves % 4 != 0 || waves > ((int64_t)1 << 20) || iters < 1 ||
+      iters > ((int64_t)1 << 24))
+    return fail(QG_ERR_GEOMETRY, "calib_mfma: waves a positive multiple of 4, iters 1 .. 2^24");
+  if (!sink) return fail(QG_ERR_NULL, "calib_mfma: sink is required");
+  if (!aligned_to(sink, 4)) return fail(QG_ERR_ALIGN, "calib_mfma: sink must be 4-byte aligned");
+  return from_hip(qg::launch_calib_mfma((int)kind, waves, iters, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -68,4 +68,13 @@ hipError_t launch_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
                           const void* b_codes, const void* b_e8m0, int64_t N, int64_t K, void* y,
                           hipStream_t stream);
 
+// Roofline calibration (measurement only): a read-only stream of `bytes`
+// (a multiple of 64 KiB) and an MFMA-only loop of `waves` waves (a multiple
+// of 4) x `iters` iterations of 8 instructions.
+hipError_t launch_calib_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                                    hipStream_t stream);
+
+hipError_t launch_calib_mfma(int kind, int64_t waves, int64_t iters, float* sink,
+                             hipStream_t stream);
+
 }  // namespace qg
