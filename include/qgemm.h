@@ -158,6 +158,37 @@ qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
                    int64_t N, int64_t K, int64_t group, void* y, void* stream);
 
 /*
+ * qg_tile_gemv_weights -- the one-time relayout of INT4 codes for the decode
+ * GEMV ([L6] section 2: weights are re-laid-out for the kernel's access
+ * pattern after loading, process_weights_after_loading; [SRV] 1.3: Marlin's
+ * interleaved weight layout is the NVIDIA prior art).  Tiled layout: tile t
+ * (rows 16t .. 16t+15), group g (128 codes = 64 bytes per row) is one
+ * contiguous 1 KiB block at byte (t * K/128 + g) * 1024, holding the 16 rows'
+ * 64-byte group segments in row order, each exactly as in the canonical
+ * packing (same nibble order); rows past N in the last tile are zero.  The
+ * nibbles only move, so INT4_SYM and INT4_ASYM tile alike, and the scales
+ * and zero points keep their canonical [N][K/group] layout.
+ *   codes        int32 [N][K/8], the canonical packing of qg_quantize_pack.
+ *   tiled_codes  ceil(N/16) * 16 * K/2 bytes (caller-owned, not `codes`).
+ * Errors: QG_ERR_GEOMETRY (N < 1, K not a positive multiple of 128),
+ * QG_ERR_UNSUPPORTED (K > 65536, codes larger than 2 GiB - 4 KiB, in place),
+ * QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_tile_gemv_weights(const void* codes, int64_t N, int64_t K, void* tiled_codes,
+                               void* stream);
+
+/*
+ * qg_qgemv_tiled -- qg_qgemv on codes in the tiled layout of
+ * qg_tile_gemv_weights (same arguments, results bit-identical to qg_qgemv on
+ * the canonical codes).  Every 16-byte code load then covers whole cache
+ * lines and is issued with the non-temporal hint, which streams HBM faster
+ * than the canonical layout's half-line loads.
+ */
+qg_status qg_qgemv_tiled(qg_format wfmt, const void* x, int64_t M, const void* tiled_codes,
+                         const void* wscales, const void* wzeros, int64_t N, int64_t K,
+                         int64_t group, void* y, void* stream);
+
+/*
  * qg_qgemm -- quantized GEMM Y = dequant(A) * dequant(W)^T, fp32
  * accumulation, bf16 output (round to nearest even).  Format pairs:
  *   W INT4_SYM|INT4_ASYM, A BF16_ACT : W4A16 prefill ([SRV] 1.3; [L6] sec. 2);
@@ -350,8 +381,9 @@ qg_status qg_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,
  * as measured on this GPU, reported beside the published peaks.
  *
  * qg_calib_stream_read -- reads `bytes` of device memory once: workgroup c
- * reads the contiguous 64 KiB chunk c with 16-byte loads, all in flight at
- * once, and writes the XOR of the chunk's 32-bit words to sink[c].
+ * reads the contiguous 64 KiB chunk c with 16-byte non-temporal loads, all
+ * in flight at once, and writes the XOR of the chunk's 32-bit words to
+ * sink[c].
  *   src        device memory, 16-byte aligned, `bytes` long.
  *   bytes      a positive multiple of 65536, at most 2^40.
  *   sink       uint32 [bytes / 65536], 4-byte aligned (owned by the caller).

@@ -28,6 +28,7 @@ EXPORTS = [
     "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth", "qg_channel_absmax",
     "qg_smooth_scales", "qg_channel_scales", "qg_kv_cache_store", "qg_status_str",
     "qg_last_error", "qg_abi_version", "qg_calib_stream_read", "qg_calib_mfma",
+    "qg_tile_gemv_weights", "qg_qgemv_tiled",
 ]
 
 _lib = None
@@ -59,11 +60,14 @@ def load() -> ctypes.CDLL:
     lib.qg_channel_scales.argtypes = [vp, i64, ctypes.c_float, vp, vp]
     lib.qg_kv_cache_store.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     lib.qg_calib_stream_read.argtypes = [vp, i64, vp, vp]
+    lib.qg_tile_gemv_weights.argtypes = [vp, i64, i64, vp, vp]
+    lib.qg_qgemv_tiled.argtypes = [i32, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
     lib.qg_calib_mfma.argtypes = [i32, i64, i64, vp, vp]
     for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
                  "qg_mx_gemm", "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth",
                  "qg_channel_absmax", "qg_smooth_scales", "qg_channel_scales",
-                 "qg_kv_cache_store", "qg_calib_stream_read", "qg_calib_mfma"]:
+                 "qg_kv_cache_store", "qg_calib_stream_read", "qg_calib_mfma",
+                 "qg_tile_gemv_weights", "qg_qgemv_tiled"]:
         getattr(lib, name).restype = i32
     lib.qg_status_str.argtypes = [i32]
     lib.qg_status_str.restype = ctypes.c_char_p

@@ -88,9 +88,13 @@ def _weights(fmt: str, codes, scales, zeros, n: int, k: int, group: int, dev):
         raise ValueError("invalid quantization geometry: group must divide K")
     cshape, cdt, sdt = _code_shapes(fmt, n, k, group)
     _expect(codes, cshape, cdt, "weight codes", dev)
-    _expect(scales, (n, k // group), sdt, "weight scales", dev)
+    # one scale per row (group == K) may also come as a flat [rows] vector
+    sshape = (n, k // group)
+    if group == k and isinstance(scales, torch.Tensor) and scales.dim() == 1:
+        sshape = (n,)
+    _expect(scales, sshape, sdt, "weight scales", dev)
     if fmt in _ASYM:
-        _expect(zeros, (n, k // group), sdt, "weight zeros", dev)
+        _expect(zeros, sshape, sdt, "weight zeros", dev)
     else:
         _expect_none(zeros, "weight zeros")
 
@@ -200,6 +204,69 @@ def qgemv(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, zeros, fmt
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
     _lib.check(lib.qg_qgemv(FORMATS[fmt], _ptr(x), m, _ptr(codes), _ptr(scales), _ptr(zeros),
                             n, k, group, _ptr(y), _stream(dev)))
+    return y
+
+
+class TiledCodes:
+    """INT4 codes of an [N][K] weight in the decode GEMV's tile layout (the
+    one-time relayout of tile_gemv_weights): `data` holds ceil(N/16)*16*K/2
+    bytes; n and k are the weight's sizes."""
+
+    def __init__(self, data: torch.Tensor, n: int, k: int):
+        self.data, self.n, self.k = data, n, k
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def tile_gemv_weights(codes: torch.Tensor, k: int | None = None) -> TiledCodes:
+    """Relayout of canonical INT4 codes (int32 [N][K/8]) into the decode GEMV's
+    tile layout (1 KiB per 16 rows x one group of 128)."""
+    dev = codes.device
+    if codes.dim() != 2 or codes.dtype != torch.int32:
+        raise ValueError("codes must be int32 [N][K/8]")
+    n = codes.shape[0]
+    k = codes.shape[1] * 8 if k is None else k
+    _expect(codes, (n, k // 8), torch.int32, "codes", dev)
+    if k % 128:
+        raise ValueError("invalid quantization geometry: K must be a multiple of 128")
+    _dev(codes)
+    lib = _lib.load()
+    out = torch.empty(((n + 15) // 16 * 16 * k // 2,), dtype=torch.uint8, device=dev)
+    _lib.check(lib.qg_tile_gemv_weights(_ptr(codes), n, k, _ptr(out), _stream(dev)))
+    return TiledCodes(out, n, k)
+
+
+def qgemv_tiled(x: torch.Tensor, codes: TiledCodes, scales: torch.Tensor, zeros, fmt: str,
+                group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """qgemv on tiled codes (tile_gemv_weights); same results as qgemv."""
+    dev = x.device        # checked for the GPU below, after the shapes
+    if not isinstance(codes, TiledCodes):
+        raise ValueError("codes must come from tile_gemv_weights")
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be bf16 [M][K]")
+    if not fmt.startswith("int4"):
+        raise ValueError("qgemv: weights must be int4_sym or int4_asym")
+    m, k = x.shape
+    n = codes.n
+    if codes.k != k:
+        raise ValueError(f"tiled codes are for K={codes.k}, x has K={k}")
+    _expect(codes.data, ((n + 15) // 16 * 16 * k // 2,), torch.uint8, "tiled codes", dev)
+    if group <= 0 or k % group:
+        raise ValueError("invalid quantization geometry: group must divide K")
+    _expect(scales, (n, k // group), torch.float16, "weight scales", dev)
+    if fmt in _ASYM:
+        _expect(zeros, (n, k // group), torch.float16, "weight zeros", dev)
+    else:
+        _expect_none(zeros, "weight zeros")
+    if out is not None:
+        _expect(out, (m, n), torch.bfloat16, "out", dev)
+    _dev(x)
+    lib = _lib.load()
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_qgemv_tiled(FORMATS[fmt], _ptr(x), m, _ptr(codes.data), _ptr(scales),
+                                  _ptr(zeros), n, k, group, _ptr(y), _stream(dev)))
     return y
 
 

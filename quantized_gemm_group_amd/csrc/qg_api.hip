@@ -66,6 +66,24 @@ bool fits_offsets(int64_t rows, int64_t row_bytes) {
   return (rows + 256) * row_bytes <= 0x7ffff000LL;
 }
 
+qg_status qgemv_common(bool tiled, qg_format wfmt, const void* x, int64_t M, const void* wcodes,
+                       const void* wscales, const void* wzeros, int64_t N, int64_t K,
+                       int64_t group, void* y, void* stream) {
+  if (!is_int4(wfmt)) return fail(QG_ERR_FORMAT, "qgemv: weights must be INT4_SYM or INT4_ASYM");
+  if (M < 1 || M > 16) return fail(QG_ERR_GEOMETRY, "qgemv: M must be in 1..16");
+  if (N < 1 || N > (int64_t)1 << 30) return fail(QG_ERR_GEOMETRY, "qgemv: N out of range");
+  qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
+  if (st != QG_OK) return st;
+  if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemv: only group 128 is implemented");
+  if (K > 65536) return fail(QG_ERR_UNSUPPORTED, "qgemv: K above 65536 is not implemented");
+  if (!fits_offsets(N, K / 2) || !fits_offsets(M, K * 2))
+    return fail(QG_ERR_UNSUPPORTED, "qgemv: operand larger than 2 GiB");
+  if (!x || !y) return fail(QG_ERR_NULL, "qgemv: x and y are required");
+  if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemv: x, y must be 16-byte aligned");
+  return from_hip(qg::launch_qgemv(wfmt == QG_INT4_ASYM, tiled, x, M, wcodes, wscales, wzeros, N,
+                                   K, y, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,19 +257,27 @@ qg_status qg_dequant(qg_format fmt, const void* codes, const void* scales, const
 qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M, const void* wcodes,
                    const void* wscales, const void* wzeros, int64_t N, int64_t K, int64_t group,
                    void* y, void* stream) {
-  if (!is_int4(wfmt)) return fail(QG_ERR_FORMAT, "qgemv: weights must be INT4_SYM or INT4_ASYM");
-  if (M < 1 || M > 16) return fail(QG_ERR_GEOMETRY, "qgemv: M must be in 1..16");
-  if (N < 1 || N > (int64_t)1 << 30) return fail(QG_ERR_GEOMETRY, "qgemv: N out of range");
-  qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
-  if (st != QG_OK) return st;
-  if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemv: only group 128 is implemented");
-  if (K > 65536) return fail(QG_ERR_UNSUPPORTED, "qgemv: K above 65536 is not implemented");
-  if (!fits_offsets(N, K / 2) || !fits_offsets(M, K * 2))
-    return fail(QG_ERR_UNSUPPORTED, "qgemv: operand larger than 2 GiB");
-  if (!x || !y) return fail(QG_ERR_NULL, "qgemv: x and y are required");
-  if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemv: x, y must be 16-byte aligned");
-  return from_hip(qg::launch_qgemv(wfmt == QG_INT4_ASYM, x, M, wcodes, wscales, wzeros, N, K, y,
-                                   (hipStream_t)stream));
+  return qgemv_common(false, wfmt, x, M, wcodes, wscales, wzeros, N, K, group, y, stream);
+}
+
+qg_status qg_qgemv_tiled(qg_format wfmt, const void* x, int64_t M, const void* tiled_codes,
+                         const void* wscales, const void* wzeros, int64_t N, int64_t K,
+                         int64_t group, void* y, void* stream) {
+  return qgemv_common(true, wfmt, x, M, tiled_codes, wscales, wzeros, N, K, group, y, stream);
+}
+
+qg_status qg_tile_gemv_weights(const void* codes, int64_t N, int64_t K, void* tiled_codes,
+                               void* stream) {
+  if (N < 1 || N > (int64_t)1 << 30 || K < 128 || K % 128 != 0)
+    return fail(QG_ERR_GEOMETRY, "tile_gemv_weights: N >= 1 and K a positive multiple of 128");
+  if (K > 65536) return fail(QG_ERR_UNSUPPORTED, "tile_gemv_weights: K above 65536");
+  if (!fits_offsets(N, K / 2))
+    return fail(QG_ERR_UNSUPPORTED, "tile_gemv_weights: codes larger than 2 GiB");
+  if (!codes || !tiled_codes) return fail(QG_ERR_NULL, "tile_gemv_weights: NULL pointer");
+  if (!aligned16(codes) || !aligned16(tiled_codes))
+    return fail(QG_ERR_ALIGN, "tile_gemv_weights: pointers must be 16-byte aligned");
+  if (codes == tiled_codes) return fail(QG_ERR_UNSUPPORTED, "tile_gemv_weights: not in place");
+  return from_hip(qg::launch_tile_gemv_codes(codes, N, K, tiled_codes, (hipStream_t)stream));
 }
 
 qg_status qg_qgemm(qg_format wfmt, qg_format afmt, const void* a, const void* a_scales,

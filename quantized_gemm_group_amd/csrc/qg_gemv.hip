@@ -74,6 +74,32 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Where the packed codes of a 16-row tile live.  Canonical layout ([N][K/8]
+// int32): row n, group g at n * K/2 + 64 g; one wave-wide 16-byte load covers
+// 16 rows x 64 bytes, i.e. half of 16 cache lines.  Tiled layout (written
+// once by qg_tile_gemv_weights): tile t, group g is one contiguous 1 KiB block
+// [t][g][16 rows][64 bytes], so the same load covers 8 whole lines; those
+// loads carry the non-temporal hint (the codes are read once: they stream
+// past the caches instead of displacing the activations and scales there).
+template <bool TILED>
+struct WLayout {
+  static constexpr int kGroupStride = TILED ? 1024 : 64;   // bytes between groups of a row
+  // lane's byte offset of group 0 of its row (li) in tile `tile`
+  __device__ static uint32_t lane_off(int tile, int li, int lg, int N, int K) {
+    const int n = tile * 16 + li;
+    if (n >= N) return 0x80000000u;                       // past the end: reads zero
+    return TILED ? (uint32_t)tile * (uint32_t)(K / 128) * 1024u + (uint32_t)(li * 64 + lg * 16)
+                 : (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(lg * 16);
+  }
+  __device__ static int64_t bytes(int N, int K) {
+    return TILED ? (int64_t)((N + 15) / 16) * 16 * K / 2 : (int64_t)N * K / 2;
+  }
+  __device__ static u32x4 load(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff,
+                                                                           TILED ? 2 : 0));
+  }
+};
+
 // One group of one 16-channel tile: 4 code MFMAs, then the flush
 // y += s * (acc - c * sum_x).  sum_x comes precomputed (x staged in LDS) or
 // from 4 more MFMAs against 1.0 (x read from the cache).
@@ -143,7 +169,7 @@ __device__ __forceinline__ void stage_scales(const uint16_t* __restrict__ s16,
 //   LDS: [x: M*K bf16, pair-permuted (XLDS)] [sum_x: M*G floats (XLDS)]
 //        [sc: G * RW*16 float2]; then reused for the partial sums
 //        [RW][KS][4][64] floats.
-template <bool ASYM, bool XLDS, bool SVEC>
+template <bool ASYM, bool XLDS, bool SVEC, bool TILED>
 __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict__ x, int M,
                                                      const uint32_t* __restrict__ w,
                                                      const uint16_t* __restrict__ s16,
@@ -164,11 +190,10 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
   const int gb = (int)((int64_t)kw * G / KS);
   const int ge = (int)((int64_t)(kw + 1) * G / KS);
 
-  const int64_t wbytes = (int64_t)N * K / 2;
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)w, (short)0, (int)(wbytes > 0x7ffff000LL ? 0x7ffff000LL : wbytes), 0x00020000);
-  const int nrow = (tile0 + rw) * 16 + li;
-  const uint32_t woff = nrow < N ? (uint32_t)nrow * (uint32_t)(K / 2) + lg * 16 : 0x80000000u;
+  using WL = WLayout<TILED>;
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N, K));
+  const uint32_t woff = WL::lane_off(tile0 + rw, li, lg, N, K);
+  constexpr int kGS = WL::kGroupStride;
   float yacc[4] = {0.f, 0.f, 0.f, 0.f};
   const int xbytes = XLDS ? M * K * 2 : 0;
   const int sxbytes = XLDS ? (M * G * 4 + 15) & ~15 : 0;
@@ -220,7 +245,7 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
     u32x4 ring[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; ++j)
-      ring[j] = bload(wres, gb + j < ge ? woff : 0x80000000u, (gb + j) * 64);
+      ring[j] = WL::load(wres, gb + j < ge ? woff : 0x80000000u, (gb + j) * kGS);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. x into LDS pair-permuted, with the group sums of x (16
@@ -304,7 +329,7 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
           for (int i = 0; i < 4; ++i) bx[i] = as_bf16x8(xrow[g * 16 + lg * 4 + i]);
           group_math<ASYM, true>(ring[j], bx, sc_base + g * TR * 2, sxrow[g], mask, cmag, yacc);
         }
-        ring[j] = bload(wres, g + kRing < ge ? woff : 0x80000000u, (g + kRing) * 64);
+        ring[j] = WL::load(wres, g + kRing < ge ? woff : 0x80000000u, (g + kRing) * kGS);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -317,7 +342,7 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
     u32x4 a0, a1, b0[4], b1[4];
     auto load_group = [&](int g, u32x4& a, u32x4 (&b)[4]) {
       const bool ok = g < ge;
-      a = bload(wres, ok ? woff : 0x80000000u, g * 64);
+      a = WL::load(wres, ok ? woff : 0x80000000u, g * kGS);
 #pragma unroll
       for (int i = 0; i < 4; ++i) b[i] = bload(xres, ok ? xoff : 0x80000000u, g * 256 + i * 16);
     };
@@ -395,7 +420,7 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
 // the sums and a lane read puts each in a scalar register, which drops the
 // second MFMA (half of the matrix work) and its registers.
 // LDS: [x slices: KS * MM * NG * 256 bytes][partials: KS * 1 KiB].
-template <bool ASYM, int NG, int MM>
+template <bool ASYM, int NG, int MM, bool TILED>
 __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __restrict__ x, int M,
                                                           const uint32_t* __restrict__ w,
                                                           const uint16_t* __restrict__ s16,
@@ -451,11 +476,12 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
       }
     }
   }
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, (int64_t)N * K / 2);
-  const uint32_t woff = n < N ? (uint32_t)n * (uint32_t)(K / 2) + lg * 16 : 0x80000000u;
+  using WL = WLayout<TILED>;
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N, K));
+  const uint32_t woff = WL::lane_off(blockIdx.x, li, lg, N, K);
   u32x4 wr[NG];
 #pragma unroll
-  for (int j = 0; j < NG; ++j) wr[j] = bload(wres, woff, (gb + j) * 64);
+  for (int j = 0; j < NG; ++j) wr[j] = WL::load(wres, woff, (gb + j) * WL::kGroupStride);
   __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
 
   // ---- 2. the x slice, pair-permuted, into this wave's LDS region: row m,
@@ -589,7 +615,7 @@ __device__ __forceinline__ u32x4 transpose_rows(const u32x4& v) {
 // D[m = 4 lg + r][n = li] of each channel tile, and an MFMA against 1.0
 // gives the group sums of x in the same layout.
 // LDS: partial sums [KS][R][4][64] floats.
-template <bool ASYM, int NG, int R>
+template <bool ASYM, int NG, int R, bool TILED>
 __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restrict__ x, int M,
                                                          const uint32_t* __restrict__ w,
                                                          const uint16_t* __restrict__ s16,
@@ -611,7 +637,8 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
   // rows m >= M and channels n >= N read as zero (out of the buffer ranges)
   const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x, (int64_t)M * K * 2);
   const uint32_t xoff = li < M ? (uint32_t)(li * K + gb * kGroup + 8 * lg) * 2 : 0x80000000u;
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, (int64_t)N * K / 2);
+  using WL = WLayout<TILED>;
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N, K));
   const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * G * 2);
   const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
   uint32_t woff[R];
@@ -619,7 +646,8 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
 #pragma unroll
   for (int t = 0; t < R; ++t) {
     const int n = n0 + 16 * t + li;
-    woff[t] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(gb * 64 + lg * 16) : 0x80000000u;
+    woff[t] = WL::lane_off(blockIdx.x * R + t, li, lg, N, K);
+    if (woff[t] != 0x80000000u) woff[t] += (uint32_t)(gb * WL::kGroupStride);
     const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
     if constexpr (NG == 4) {
       const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
@@ -648,7 +676,7 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 4; ++i) xr[slot][i] = bload(xres, xoff, j * 256 + i * 64);
 #pragma unroll
-    for (int t = 0; t < R; ++t) wr[slot][t] = bload(wres, woff[t], j * 64);
+    for (int t = 0; t < R; ++t) wr[slot][t] = WL::load(wres, woff[t], j * WL::kGroupStride);
   };
 #pragma unroll
   for (int j = 0; j < D; ++j) load(j, j);
@@ -715,14 +743,14 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
   }
 }
 
-template <bool ASYM, int NG, int R>
+template <bool ASYM, int NG, int R, bool TILED>
 hipError_t launch_m16_t(const void* x, int M, const void* w, const void* s, const void* z, int N,
                         int K, void* y, hipStream_t stream) {
   const int G = K / kGroup;
   const int ks = G / NG;
   const int blocks = (N + 16 * R - 1) / (16 * R);
   const size_t lds = (size_t)ks * R * 4 * 64 * sizeof(float);
-  hipLaunchKernelGGL((qgemv_m16_kernel<ASYM, NG, R>), dim3(blocks), dim3(64 * ks), lds, stream,
+  hipLaunchKernelGGL((qgemv_m16_kernel<ASYM, NG, R, TILED>), dim3(blocks), dim3(64 * ks), lds, stream,
                      (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
                      (const uint16_t*)z, N, K, ks, (uint16_t*)y, 0x000F000Fu,
                      ASYM ? 0x43004300u : 0x43084308u);
@@ -739,22 +767,23 @@ int pick_m16_ng(int K) {
   return 0;
 }
 
+template <bool TILED>
 hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, const void* s,
                       const void* z, int N, int K, void* y, hipStream_t stream) {
   // two channel tiles per wave (4 groups each, to stay within 128 VGPRs)
   // once there are enough tiles for the chip
   const int G = K / kGroup;
   if (N >= 16384 && G % 4 == 0 && G / 4 <= 16)
-    return asym ? launch_m16_t<true, 4, 2>(x, M, w, s, z, N, K, y, stream)
-                : launch_m16_t<false, 4, 2>(x, M, w, s, z, N, K, y, stream);
+    return asym ? launch_m16_t<true, 4, 2, TILED>(x, M, w, s, z, N, K, y, stream)
+                : launch_m16_t<false, 4, 2, TILED>(x, M, w, s, z, N, K, y, stream);
   if (asym) {
-    if (ng == 4) return launch_m16_t<true, 4, 1>(x, M, w, s, z, N, K, y, stream);
-    if (ng == 16) return launch_m16_t<true, 16, 1>(x, M, w, s, z, N, K, y, stream);
-    return launch_m16_t<true, 8, 1>(x, M, w, s, z, N, K, y, stream);
+    if (ng == 4) return launch_m16_t<true, 4, 1, TILED>(x, M, w, s, z, N, K, y, stream);
+    if (ng == 16) return launch_m16_t<true, 16, 1, TILED>(x, M, w, s, z, N, K, y, stream);
+    return launch_m16_t<true, 8, 1, TILED>(x, M, w, s, z, N, K, y, stream);
   }
-  if (ng == 4) return launch_m16_t<false, 4, 1>(x, M, w, s, z, N, K, y, stream);
-  if (ng == 16) return launch_m16_t<false, 16, 1>(x, M, w, s, z, N, K, y, stream);
-  return launch_m16_t<false, 8, 1>(x, M, w, s, z, N, K, y, stream);
+  if (ng == 4) return launch_m16_t<false, 4, 1, TILED>(x, M, w, s, z, N, K, y, stream);
+  if (ng == 16) return launch_m16_t<false, 16, 1, TILED>(x, M, w, s, z, N, K, y, stream);
+  return launch_m16_t<false, 8, 1, TILED>(x, M, w, s, z, N, K, y, stream);
 }
 
 // Launch shape (measured on MI355X for the Llama-3-8B decode shapes): about
@@ -763,7 +792,7 @@ hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, co
 // 1024 tiles.  Deeper rings and more waves measured slower: the kernels are
 // bound by the latency of their prologue and epilogue, not by the bytes in
 // flight.
-template <bool ASYM, bool XLDS, bool SVEC>
+template <bool ASYM, bool XLDS, bool SVEC, bool TILED>
 hipError_t launch_t(const void* x, int M, const void* w, const void* s, const void* z, int N,
                     int K, void* y, hipStream_t stream) {
   const int G = K / kGroup;
@@ -783,21 +812,21 @@ hipError_t launch_t(const void* x, int M, const void* w, const void* s, const vo
   // keep the staged scales within 32 KiB and the workgroup within 64 KiB of LDS
   while (rw > 1 && ((size_t)G * rw * 16 * 8 > 32 * 1024 || lds_for(rw) > 64 * 1024)) --rw;
   const int blocks = (tiles + rw - 1) / rw;
-  hipLaunchKernelGGL((qgemv_kernel<ASYM, XLDS, SVEC>), dim3(blocks), dim3(64 * rw * ks), lds_for(rw),
+  hipLaunchKernelGGL((qgemv_kernel<ASYM, XLDS, SVEC, TILED>), dim3(blocks), dim3(64 * rw * ks), lds_for(rw),
                      stream, (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
                      (const uint16_t*)z, N, K, ks, rw, (uint16_t*)y, 0x000F000Fu,
                      ASYM ? 0x43004300u : 0x43084308u);
   return hipGetLastError();
 }
 
-template <bool ASYM, int NG, int MM>
+template <bool ASYM, int NG, int MM, bool TILED>
 hipError_t launch_wave_t(const void* x, int M, const void* w, const void* s, const void* z, int N,
                          int K, void* y, hipStream_t stream) {
   const int G = K / kGroup;
   const int ks = G / NG;
   const int tiles = (N + 15) / 16;
   const size_t lds = (size_t)ks * (MM * NG * 256 + 1024);
-  hipLaunchKernelGGL((qgemv_wave_kernel<ASYM, NG, MM>), dim3(tiles), dim3(64 * ks), lds, stream,
+  hipLaunchKernelGGL((qgemv_wave_kernel<ASYM, NG, MM, TILED>), dim3(tiles), dim3(64 * ks), lds, stream,
                      (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
                      (const uint16_t*)z, N, K, ks, (uint16_t*)y, 0x000F000Fu,
                      ASYM ? 0x43004300u : 0x43084308u);
@@ -806,20 +835,21 @@ hipError_t launch_wave_t(const void* x, int M, const void* w, const void* s, con
 
 // Per-wave kernel for M <= 4 when K splits into slices of NG groups with at
 // most 16 slices (G % NG == 0, G / NG <= 16) and the LDS fits.
+template <bool TILED>
 hipError_t launch_wave(bool asym, int ng, const void* x, int M, const void* w, const void* s,
                        const void* z, int N, int K, void* y, hipStream_t stream) {
   if (M == 1) {
-    if (ng == 4) return asym ? launch_wave_t<true, 4, 1>(x, M, w, s, z, N, K, y, stream)
-                             : launch_wave_t<false, 4, 1>(x, M, w, s, z, N, K, y, stream);
-    if (ng == 16) return asym ? launch_wave_t<true, 16, 1>(x, M, w, s, z, N, K, y, stream)
-                              : launch_wave_t<false, 16, 1>(x, M, w, s, z, N, K, y, stream);
-    return asym ? launch_wave_t<true, 8, 1>(x, M, w, s, z, N, K, y, stream)
-                : launch_wave_t<false, 8, 1>(x, M, w, s, z, N, K, y, stream);
+    if (ng == 4) return asym ? launch_wave_t<true, 4, 1, TILED>(x, M, w, s, z, N, K, y, stream)
+                             : launch_wave_t<false, 4, 1, TILED>(x, M, w, s, z, N, K, y, stream);
+    if (ng == 16) return asym ? launch_wave_t<true, 16, 1, TILED>(x, M, w, s, z, N, K, y, stream)
+                              : launch_wave_t<false, 16, 1, TILED>(x, M, w, s, z, N, K, y, stream);
+    return asym ? launch_wave_t<true, 8, 1, TILED>(x, M, w, s, z, N, K, y, stream)
+                : launch_wave_t<false, 8, 1, TILED>(x, M, w, s, z, N, K, y, stream);
   }
-  if (ng == 4) return asym ? launch_wave_t<true, 4, 4>(x, M, w, s, z, N, K, y, stream)
-                           : launch_wave_t<false, 4, 4>(x, M, w, s, z, N, K, y, stream);
-  return asym ? launch_wave_t<true, 8, 4>(x, M, w, s, z, N, K, y, stream)
-              : launch_wave_t<false, 8, 4>(x, M, w, s, z, N, K, y, stream);
+  if (ng == 4) return asym ? launch_wave_t<true, 4, 4, TILED>(x, M, w, s, z, N, K, y, stream)
+                           : launch_wave_t<false, 4, 4, TILED>(x, M, w, s, z, N, K, y, stream);
+  return asym ? launch_wave_t<true, 8, 4, TILED>(x, M, w, s, z, N, K, y, stream)
+              : launch_wave_t<false, 8, 4, TILED>(x, M, w, s, z, N, K, y, stream);
 }
 
 // Groups per wave for the per-wave kernel (0: not applicable).  Measured on
@@ -849,16 +879,18 @@ int pick_wave_ng(int M, int N, int K) {
 // LDS per workgroup: x (M*K*2 bytes when staged, <= 48 KiB) + (s, c) pairs
 // (G * RW * 128 bytes <= 32 KiB for RW > 1; G * 128 bytes = 64 KiB at the
 // API's K limit of 65536 with RW = 1, where x is never staged).
-hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
-                        const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
-                        hipStream_t stream) {
+namespace {
+template <bool TILED>
+hipError_t launch_qgemv_t(bool asym, const void* x, int64_t M, const void* wcodes,
+                          const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
+                          hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   const int G = k / kGroup;
   const int ng = pick_wave_ng(m, n, k);
-  if (ng) return launch_wave(asym, ng, x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  if (ng) return launch_wave<TILED>(asym, ng, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   if (m > 4) {
     const int ng16 = pick_m16_ng(k);
-    if (ng16) return launch_m16(asym, ng16, x, m, wcodes, wscales, wzeros, n, k, y, stream);
+    if (ng16) return launch_m16<TILED>(asym, ng16, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   }
   // staged x must leave room for the (s, c) pairs of one row tile in 64 KiB
   const bool xlds = M * K * 2 <= kXldsMaxBytes &&
@@ -867,13 +899,54 @@ hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
   // cache path stages scales with the generic loop
   const bool svec = (G & 7) == 0;
   if (asym) {
-    if (!xlds) return launch_t<true, false, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
-    return svec ? launch_t<true, true, true>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
-                : launch_t<true, true, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+    if (!xlds) return launch_t<true, false, false, TILED>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+    return svec ? launch_t<true, true, true, TILED>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
+                : launch_t<true, true, false, TILED>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
   }
-  if (!xlds) return launch_t<false, false, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
-  return svec ? launch_t<false, true, true>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
-              : launch_t<false, true, false>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  if (!xlds) return launch_t<false, false, false, TILED>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+  return svec ? launch_t<false, true, true, TILED>(x, m, wcodes, wscales, wzeros, n, k, y, stream)
+              : launch_t<false, true, false, TILED>(x, m, wcodes, wscales, wzeros, n, k, y, stream);
+}
+
+}  // namespace
+
+namespace {
+
+// One lane per 16-byte piece of the tiled output: piece q of tile t, group g,
+// row r, quarter b is the 16 bytes at row t*16 + r, byte 64 g + 16 b of the
+// canonical codes (zero for rows past N).  64 consecutive lanes write one
+// contiguous 1 KiB block.
+__global__ __launch_bounds__(256) void tile_codes_kernel(const u32x4* __restrict__ src, int N,
+                                                         int K, int64_t pieces,
+                                                         u32x4* __restrict__ dst) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= pieces) return;
+  const int G = K / kGroup;
+  const int b = (int)(q & 3), r = (int)((q >> 2) & 15);
+  const int64_t tg = q >> 6;
+  const int g = (int)(tg % G);
+  const int64_t t = tg / G;
+  const int64_t n = t * 16 + r;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (n < N) v = src[(n * (K / 2) + g * 64 + b * 16) / 16];
+  dst[q] = v;
+}
+
+}  // namespace
+
+hipError_t launch_tile_gemv_codes(const void* codes, int64_t N, int64_t K, void* tiled,
+                                  hipStream_t stream) {
+  const int64_t pieces = (N + 15) / 16 * 16 * (K / 2) / 16;
+  hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                     stream, (const u32x4*)codes, (int)N, (int)K, pieces, (u32x4*)tiled);
+  return hipGetLastError();
+}
+
+hipError_t launch_qgemv(bool asym, bool tiled, const void* x, int64_t M, const void* wcodes,
+                        const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
+                        hipStream_t stream) {
+  return tiled ? launch_qgemv_t<true>(asym, x, M, wcodes, wscales, wzeros, N, K, y, stream)
+               : launch_qgemv_t<false>(asym, x, M, wcodes, wscales, wzeros, N, K, y, stream);
 }
 
 }  // namespace qg

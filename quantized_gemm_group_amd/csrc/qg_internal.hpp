@@ -43,9 +43,13 @@ hipError_t launch_norm_quant(bool rms, qg_format fmt, const void* src, qg_dtype 
 hipError_t launch_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K,
                            void* codes, void* e8m0, hipStream_t stream);
 
-hipError_t launch_qgemv(bool asym, const void* x, int64_t M, const void* wcodes,
+// tiled: wcodes in the GEMV tile layout written by launch_tile_gemv_codes.
+hipError_t launch_qgemv(bool asym, bool tiled, const void* x, int64_t M, const void* wcodes,
                         const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
                         hipStream_t stream);
+
+hipError_t launch_tile_gemv_codes(const void* codes, int64_t N, int64_t K, void* tiled,
+                                  hipStream_t stream);
 
 hipError_t launch_gemm_w4a16(bool asym, const void* x, int64_t M, const void* wcodes,
                              const void* wscales, const void* wzeros, int64_t N, int64_t K,

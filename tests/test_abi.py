@@ -273,3 +273,17 @@ def test_binding_rejects_mismatched_operands_before_any_call():
     bad("a_e8m0", qg.mx_gemm, mc, me[:1], bc, be)
     bad("out must be", qg.mx_gemm, mc, me, bc, be, out=y.t())
     bad("codes", qg.dequant, codes[:, :4], s, z, "int4_asym", k)
+
+
+def test_tiled_gemv_validation(lib):
+    t = lib.qg_tile_gemv_weights
+    assert t(A16, 0, 256, A16b, None) == _lib.ERR_GEOMETRY
+    assert t(A16, 16, 200, A16b, None) == _lib.ERR_GEOMETRY
+    assert t(A16, 16, 65536 * 2, A16b, None) == _lib.ERR_UNSUPPORTED
+    assert t(A16, 16, 256, A16, None) == _lib.ERR_UNSUPPORTED           # in place
+    assert t(None, 16, 256, A16b, None) == _lib.ERR_NULL
+    assert t(MIS, 16, 256, A16b, None) == _lib.ERR_ALIGN
+    g = lib.qg_qgemv_tiled
+    assert g(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
+    assert g(_lib.INT8_SYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_FORMAT
+    assert g(_lib.INT4_ASYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_NULL

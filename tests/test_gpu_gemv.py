@@ -34,6 +34,9 @@ def run_case(m, k, n, asym, seed, outliers=(0.01, 20.0)):
     packed, s, z = oracle_weights(c["w"], asym)
     assert (host(codes) == packed).all()
     y = host(qg.qgemv(to_dev(c["x"], dev), codes, scales, zeros, fmt))
+    # the tiled-code kernels run the same arithmetic in the same order
+    yt = host(qg.qgemv_tiled(to_dev(c["x"], dev), qg.tile_gemv_weights(codes), scales, zeros, fmt))
+    assert (yt.view(np.uint32) == y.view(np.uint32)).all(), "tiled GEMV differs from canonical"
     ref = og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, 128)
     finite_checks(y)
     if y.size < 1024:      # too few outputs for the statistical bar: per-element bound
@@ -77,10 +80,29 @@ def test_qgemv_one_hot_is_bit_exact(asym):
     x = np.zeros((16, k), np.float32)
     x[np.arange(16), ks] = 1.0
     y = host(qg.qgemv(to_dev(to_bf16(x), dev), codes, scales, zeros, fmt))
+    yt = host(qg.qgemv_tiled(to_dev(to_bf16(x), dev), qg.tile_gemv_weights(codes), scales, zeros,
+                             fmt))
     q = oi.unpack_int4(packed, signed=not asym)
     w_hat = oi.dequantize(q, s, z, 128, out="f32")
     expect = of.round_to_bf16(w_hat[:, ks].T)
     assert (y.view(np.uint32) == expect.view(np.uint32)).all()
+    assert (yt.view(np.uint32) == expect.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (37, 384), (5, 1024), (1000, 4096)])
+def test_tile_gemv_weights_layout(n, k):
+    # the tiled layout of the header, written out with numpy: block (t, g) of
+    # 1 KiB holds rows 16t .. 16t+15, bytes 64g .. 64g+63 of each, zero rows
+    # past N
+    dev = device()
+    codes = rng_for(n + k).integers(-2 ** 31, 2 ** 31, size=(n, k // 8), dtype=np.int64)
+    codes = codes.astype(np.int32)
+    got = host(qg.tile_gemv_weights(to_dev(codes, dev)).data)
+    tiles, g = (n + 15) // 16, k // 128
+    rows = np.zeros((tiles * 16, k // 2), np.uint8)
+    rows[:n] = codes.view(np.uint8).reshape(n, k // 2)
+    want = rows.reshape(tiles, 16, g, 64).transpose(0, 2, 1, 3).reshape(-1)
+    assert got.shape == want.shape and (got == want).all()
 
 
 def test_qgemv_gemv_4096_full():
@@ -93,6 +115,9 @@ def test_qgemv_gemv_4096_full():
     assert (host(scales).view(np.uint16) == s.view(np.uint16)).all()
     x = c["x"][:1]
     y = host(qg.qgemv(to_dev(x, dev), codes, scales, None, "int4_sym"))
+    yt = host(qg.qgemv_tiled(to_dev(x, dev), qg.tile_gemv_weights(codes), scales, None,
+                             "int4_sym"))
+    assert (yt.view(np.uint32) == y.view(np.uint32)).all()
     ref = og.w4a16_reference(bf16_as_f32(x), packed, s, None, 128)
     finite_checks(y)
     assert og.rel_fro(y, ref) <= TOL
@@ -115,8 +140,11 @@ def test_qgemv_llama3_8b_decode_sampled(proj):
     assert (host(scales)[rows].view(np.uint16) == s.view(np.uint16)).all()
     assert (host(zeros)[rows].view(np.uint16) == z.view(np.uint16)).all()
     xs = bf16_as_f32(c["x"])
+    tiled = qg.tile_gemv_weights(codes)
     for m in WORKLOADS["llama3_8b_decode"].ms:
         y = host(qg.qgemv(to_dev(c["x"][:m], dev), codes, scales, zeros, "int4_asym"))
+        yt = host(qg.qgemv_tiled(to_dev(c["x"][:m], dev), tiled, scales, zeros, "int4_asym"))
+        assert (yt.view(np.uint32) == y.view(np.uint32)).all(), f"M={m} tiled differs"
         finite_checks(y)
         ref = og.w4a16_reference(xs[:m], packed, s, z, 128)
         err = og.rel_fro(y[:, rows], ref)
