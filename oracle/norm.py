@@ -31,15 +31,20 @@ the design notes):
   truncation is not used: it would disagree with the unfused path's
   quantizer.
 * eps is given as a float32 value and widened exactly to float64.
+* MXFP4 output (the same section's fusion applied to the block-scaled
+  format of 《大模型量化推理引擎全景大复盘》 section 2, eq. 3): the normalized
+  float32 row goes through the MX quantizer of this package unchanged, 32
+  elements along K per E8M0 exponent; there is then no per-row scale, the
+  per-block exponents take its place.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import fp8, intquant
+from . import fp8, intquant, mx
 
 KINDS = ("layer", "rms")
-FORMATS = ("fp8_e4m3", "int8_sym", "int8_asym")
+FORMATS = ("fp8_e4m3", "int8_sym", "int8_asym", "mxfp4")
 
 
 def row_stats(x, kind: str, eps: float):
@@ -81,11 +86,15 @@ def normalize(x, gamma, beta, kind: str, eps: float) -> np.ndarray:
 
 def norm_quant(x, gamma, beta, kind: str, fmt: str, eps: float):
     """Normalize, then quantize per row.  Returns (codes [rows][K], scales
-    float32 [rows], zeros float32 [rows] or None)."""
+    float32 [rows], zeros float32 [rows] or None); for "mxfp4" (codes uint8
+    [rows][K/2], E8M0 exponents uint8 [rows][K/32], None)."""
     if fmt not in FORMATS:
         raise ValueError(f"unknown format {fmt!r}")
     y = normalize(x, gamma, beta, kind, eps)
     k = y.shape[1]
+    if fmt == "mxfp4":
+        codes, e8m0 = mx.quantize(y)
+        return codes, e8m0, None
     if fmt == "fp8_e4m3":
         codes, s = fp8.quantize_rows(y)
         return codes, np.asarray(s, np.float32).reshape(-1), None

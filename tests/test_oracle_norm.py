@@ -10,6 +10,7 @@ import torch
 
 from oracle import fp8 as F8
 from oracle import intquant as IQ
+from oracle import mx as MX
 from oracle import norm as NQ
 
 
@@ -115,3 +116,74 @@ def test_invalid_geometry():
         NQ.normalize(np.zeros((2, 8), np.float32), np.ones(4, np.float32), None, "rms", 1e-6)
     with pytest.raises(ValueError):
         NQ.norm_quant(np.zeros((2, 8), np.float32), np.ones(8), None, "rms", "int4_sym", 1e-6)
+
+
+# --------------------------------------------------------------- MXFP4 output
+
+def test_mx_output_hand_worked_rms_block():
+    # RMSNorm of rows +-a (a a power of two), eps 0: u = +-1 exactly, so y =
+    # +-gamma.  gamma puts one 32-element block on the E2M1 grid times 2^-3
+    # (block max 6 * 2^-3 = 0.75, so e = -3, byte 124) and a second block
+    # that rounds (max 0.3: e = -4, byte 123, values / 2^-4 = 4.8 -> 4 and
+    # the rest of that block at 0.05 / 2^-4 = 0.8 -> 1 (code 2), 0.02 ->
+    # 0.32 -> 0.5 (code 1), -0.1 -> -1.6 -> -1.5 (code 8 | 3))
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    g0 = np.concatenate([grid, -grid, grid[::-1], -grid[::-1]]) * np.float32(2.0 ** -3)
+    g1 = np.full(32, 0.05, np.float32)
+    g1[0], g1[1], g1[2] = 0.3, 0.02, -0.1
+    gamma = np.concatenate([g0, g1]).astype(np.float32)
+    x = np.full((2, 64), 0.5, np.float32)
+    x[1] *= -1.0
+    codes, e8m0, z = NQ.norm_quant(x, gamma, None, "rms", "mxfp4", 0.0)
+    assert z is None
+    assert e8m0.tolist() == [[124, 123], [124, 123]]
+    mag = [0, 1, 2, 3, 4, 5, 6, 7]
+    b0 = mag + [8 | m for m in mag] + mag[::-1] + [8 | m for m in mag[::-1]]
+    b0[8] = 8                                  # -0 keeps its sign bit
+    b0[31] = 8
+    b1 = [2] * 32
+    b1[0], b1[1], b1[2] = 6, 1, 8 | 3          # 4.8 -> 4 (code 6), 0.32 -> 0.5, -1.6 -> -1.5
+    want = np.array(b0 + b1, np.uint8)
+    nib = np.stack([codes[0] & 15, codes[0] >> 4], axis=1).reshape(-1)
+    assert nib.tolist() == want.tolist()
+    # the negated row flips every sign bit, zeros included
+    nib1 = np.stack([codes[1] & 15, codes[1] >> 4], axis=1).reshape(-1)
+    assert (nib1 == (want ^ 8)).all()
+
+
+def test_mx_output_constant_row_is_beta():
+    # LayerNorm of a constant row is beta bit for bit, so the MX codes and
+    # exponents are those of beta itself
+    k = 96
+    _, g, b = _case(1, k, 31)
+    x = np.full((3, k), -1.25, np.float32)
+    codes, e8m0, _ = NQ.norm_quant(x, g, b, "layer", "mxfp4", 1e-5)
+    cb, eb = MX.quantize(b[None, :])
+    assert (codes == cb).all() and (e8m0 == eb).all()
+
+
+@pytest.mark.parametrize("kind", ["layer", "rms"])
+def test_mx_output_agrees_with_torch_norm(kind):
+    # torch's float64 normalization, rounded to float32, through the MX
+    # quantizer: the codes agree except where float32 rounding moves a value
+    # across an E2M1 midpoint or a block maximum across 6 * 2^e (then the two
+    # sides may differ by one code step); a dropped term or a transposed
+    # gamma would change most of them
+    k = 256
+    x, g, b = _case(64, k, 40 + len(kind))
+    tx = torch.from_numpy(x).double()
+    if kind == "layer":
+        ref = torch.nn.functional.layer_norm(tx, (k,), torch.from_numpy(g).double(),
+                                             torch.from_numpy(b).double(), eps=1e-5)
+    else:
+        ref = torch.nn.functional.rms_norm(tx, (k,), torch.from_numpy(g).double(), eps=1e-5)
+    ref = ref.numpy().astype(np.float32)
+    codes, e8m0, _ = NQ.norm_quant(x, g, b if kind == "layer" else None, kind, "mxfp4", 1e-5)
+    rc, re = MX.quantize(ref)
+    assert (e8m0 == re).mean() > 0.99
+    same = (codes == rc).mean()
+    assert same > 0.995, same
+    # dequantized, the fused output is within one MX step of torch's values
+    deq = MX.dequantize(codes, e8m0)
+    step = np.repeat(2.0 ** (e8m0.astype(np.float64) - 127), 32, axis=1)
+    assert (np.abs(deq - ref) <= 1.01 * step).all()
