@@ -412,7 +412,20 @@ def bench_gemms(qg, torch, dev, stream, cpu=None):
                                        end_to_end_tflops=fl / (t + tq) / 1e12)
     if cpu is not None:
         cpu["mxfp4_4096x8192"] = cpu_mx_sample(c, rows=1024)
-    del x, bc, be, ac, ae, y, c
+    # fused RMSNorm / LayerNorm + MXFP4 quantization of the same activations
+    # (codes and E8M0 exponents written once), against torch's layer norm
+    # writing bf16 followed by the MX quantizer
+    gamma, beta = (torch.from_numpy(a).to(dev) for a in norm_weights(8192, 5))
+    nbytes = 4096 * 8192 * 2 + 4096 * 4096 + 4096 * 256 + 2 * 8192 * 4
+    for norm in ("rms", "layer"):
+        b_ = beta if norm == "layer" else None
+        tn = timed(lambda: qg.norm_quant(x, gamma, b_, "mxfp4", norm, 1e-5))
+        out[f"{norm}_norm_mxfp4_quant_4096x8192"] = dict(us=tn * 1e6, gbs=nbytes / tn / 1e9,
+                                                         frac=nbytes / tn / 1e9 / HBM_PEAK_GBS)
+    gb, bb = gamma.to(torch.bfloat16), beta.to(torch.bfloat16)
+    tu = timed(lambda: qg.mx_quant(torch.nn.functional.layer_norm(x, (8192,), gb, bb, 1e-5)))
+    out["layer_norm_mxfp4_quant_4096x8192"]["unfused_us"] = tu * 1e6
+    del x, bc, be, ac, ae, y, c, gamma, beta, gb, bb
     # W4A16 prefill, Qwen2.5-72B FFN shapes
     for i, name in enumerate(["ffn_up", "ffn_down"]):
         c = workload_case("qwen72b_prefill", i)

@@ -336,21 +336,26 @@ typedef enum {
  * statistics, the normalization and the quantization scale in one kernel,
  * codes and scale written once; RMSNorm + quantization as the same kind of
  * fusion).  The result equals the normalized rows passed to
- * qg_quantize_pack with group == K.
+ * qg_quantize_pack with group == K, or for QG_MXFP4 to qg_mx_quant (the
+ * same fusion with the block-scaled format of [MX] section 2 eq. 3: one
+ * E8M0 exponent per 32 elements instead of a row scale).
  *   norm       QG_NORM_LAYER or QG_NORM_RMS.
- *   fmt        QG_FP8_E4M3 | QG_INT8_SYM | QG_INT8_ASYM.
+ *   fmt        QG_FP8_E4M3 | QG_INT8_SYM | QG_INT8_ASYM | QG_MXFP4.
  *   src        [rows][K] of src_dtype (QG_BF16 or QG_F32), row-major.
  *   gamma      fp32 [K]; beta fp32 [K] for QG_NORM_LAYER, NULL for
  *              QG_NORM_RMS.
  *   eps        >= 0 and finite.
  *   codes      [rows][K] (int8 / uint8 / E4M3 bytes); scales fp32 [rows];
  *              zeros fp32 [rows] for QG_INT8_ASYM, NULL otherwise.
+ *              QG_MXFP4: codes uint8 [rows][K/2], scales = E8M0 uint8
+ *              [rows][K/32] (the layout of qg_mx_quant), zeros NULL, K a
+ *              multiple of 32.
  * Arithmetic (bit-exact reference): the row sums (of x and of (x - mean)^2,
  * or of x^2) are accumulated in fp64 and the variance is the biased one
  * (divide by K); mean and r = 1 / sqrt(var + eps) are rounded once to fp32;
  * then t = x - mean, u = t * r, y = u * gamma, y = y + beta, each one fp32
  * operation rounded to nearest even (no fused multiply-add); y is quantized
- * as by qg_quantize_pack.
+ * as by qg_quantize_pack (qg_mx_quant for QG_MXFP4).
  * Limits: K a multiple of 8, 8 <= K <= 16384 (QG_ERR_GEOMETRY when not a
  * multiple of 8, QG_ERR_UNSUPPORTED above 16384); rows <= 2^31 - 1.
  * Errors: QG_ERR_GEOMETRY, QG_ERR_FORMAT, QG_ERR_NULL, QG_ERR_ALIGN,

@@ -139,22 +139,31 @@ def norm_quant(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None =
                fmt: str = "fp8_e4m3", norm: str = "layer", eps: float = 1e-5):
     """Fused LayerNorm ("layer", needs beta) or RMSNorm ("rms", beta None) of
     each row of x [rows][K] (bf16 or fp32) followed by its per-row dynamic
-    quantization ("fp8_e4m3", "int8_sym", "int8_asym").  gamma, beta: fp32
-    [K].  Returns (codes [rows][K], scales fp32 [rows][1], zeros or None)."""
+    quantization ("fp8_e4m3", "int8_sym", "int8_asym"), or its MXFP4
+    quantization ("mxfp4").  gamma, beta: fp32 [K].  Returns (codes
+    [rows][K], scales fp32 [rows][1], zeros or None); for "mxfp4" (codes
+    uint8 [rows][K/2], E8M0 exponents uint8 [rows][K/32], None)."""
     lib = _lib.load()
     dev = _dev(x)
     if norm not in NORMS:
         raise ValueError(f"unknown normalization {norm}")
-    if fmt not in ("fp8_e4m3", "int8_sym", "int8_asym"):
+    if fmt not in ("fp8_e4m3", "int8_sym", "int8_asym", "mxfp4"):
         raise ValueError(f"norm_quant: unsupported format {fmt}")
     rows, k = x.shape
     for t, what in ((gamma, "gamma"), (beta, "beta")):
         if t is not None:
             _f32_vec(t, dev, k, what)
-    cshape, cdt, sdt = _code_shapes(fmt, rows, k, k)
-    codes = torch.empty(cshape, dtype=cdt, device=dev)
-    scales = torch.empty((rows, 1), dtype=sdt, device=dev)
-    zeros = torch.empty_like(scales) if fmt in _ASYM else None
+    if fmt == "mxfp4":
+        if k % 32:
+            raise ValueError("invalid quantization geometry: K must be a multiple of 32")
+        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, k // 32), dtype=torch.uint8, device=dev)
+        zeros = None
+    else:
+        cshape, cdt, sdt = _code_shapes(fmt, rows, k, k)
+        codes = torch.empty(cshape, dtype=cdt, device=dev)
+        scales = torch.empty((rows, 1), dtype=sdt, device=dev)
+        zeros = torch.empty_like(scales) if fmt in _ASYM else None
     _lib.check(lib.qg_norm_quant(NORMS[norm], FORMATS[fmt], _ptr(x), _src_dtype(x), _ptr(gamma),
                                  _ptr(beta), ctypes.c_float(eps), rows, k, _ptr(codes),
                                  _ptr(scales), _ptr(zeros), _stream(dev)))

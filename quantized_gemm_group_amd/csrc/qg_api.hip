@@ -217,15 +217,18 @@ qg_status qg_norm_quant(qg_norm norm, qg_format fmt, const void* src, qg_dtype s
                         int64_t K, void* codes, void* scales, void* zeros, void* stream) {
   if (norm != QG_NORM_LAYER && norm != QG_NORM_RMS)
     return fail(QG_ERR_FORMAT, "norm_quant: unknown normalization");
-  if (fmt != QG_FP8_E4M3 && fmt != QG_INT8_SYM && fmt != QG_INT8_ASYM)
-    return fail(QG_ERR_FORMAT, "norm_quant: format must be FP8_E4M3, INT8_SYM or INT8_ASYM");
+  if (fmt != QG_FP8_E4M3 && fmt != QG_INT8_SYM && fmt != QG_INT8_ASYM && fmt != QG_MXFP4)
+    return fail(QG_ERR_FORMAT,
+                "norm_quant: format must be FP8_E4M3, INT8_SYM, INT8_ASYM or MXFP4");
   if (src_dtype != QG_BF16 && src_dtype != QG_F32)
     return fail(QG_ERR_FORMAT, "norm_quant: source dtype must be bf16 or f32");
   if (rows < 1 || rows > 0x7fffffffLL || K < 8 || K % 8 != 0)
     return fail(QG_ERR_GEOMETRY, "norm_quant: rows >= 1 and K a positive multiple of 8");
   if (!(eps >= 0.f) || !(eps <= 3.4e38f))
     return fail(QG_ERR_GEOMETRY, "norm_quant: eps must be finite and >= 0");
-  qg_status st = check_quant_operand(fmt, rows, K, K, codes, scales, zeros);
+  if (fmt == QG_MXFP4 && K % 32 != 0)
+    return fail(QG_ERR_GEOMETRY, "norm_quant: MXFP4 needs K a multiple of 32");
+  qg_status st = check_quant_operand(fmt, rows, K, fmt == QG_MXFP4 ? 32 : K, codes, scales, zeros);
   if (st != QG_OK) return st;
   if (!src || !gamma) return fail(QG_ERR_NULL, "norm_quant: src and gamma are required");
   if (norm == QG_NORM_LAYER && !beta) return fail(QG_ERR_NULL, "norm_quant: LayerNorm needs beta");

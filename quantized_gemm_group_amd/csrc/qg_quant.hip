@@ -30,7 +30,8 @@
 namespace qg {
 namespace {
 
-enum QKind { K_INT4_SYM = 0, K_INT4_ASYM = 1, K_INT8_SYM = 2, K_INT8_ASYM = 3, K_FP8 = 4 };
+enum QKind { K_INT4_SYM = 0, K_INT4_ASYM = 1, K_INT8_SYM = 2, K_INT8_ASYM = 3, K_FP8 = 4,
+             K_MX = 5 /* MXFP4 output of the fused normalization only */ };
 
 constexpr int kThreads = 256;
 
@@ -546,7 +547,10 @@ void launch_dequant_t(const void* codes, const void* scales, const void* zeros, 
 // x^2), mean and r = 1 / sqrt(var + eps) are rounded once to fp32, and the
 // normalized value is formed in fp32 with one rounding per operation and no
 // fused multiply-add: t = x - mean, u = t * r, y = u * gamma (+ beta).  The
-// codes are then those of the per-row quantizer above.
+// codes are then those of the per-row quantizer above, or (K_MX) those of
+// the MXFP4 quantizer: a 32-element block is 4 consecutive vecs, held by 4
+// consecutive threads, so its maximum is two xor-shuffles away and the row
+// needs no further reduction.
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
   __syncthreads();   // the previous use of red is over
@@ -640,11 +644,42 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __rest
       if constexpr (!RMS) y = y + (e < 4 ? b0[e] : b1[e - 4]);
       v[i][e] = y;
     }
-    const Stats s = stats_of(v[i]);
-    st.amax = __builtin_fmaxf(st.amax, s.amax);
-    st.lo = __builtin_fminf(st.lo, s.lo);
-    st.hi = __builtin_fmaxf(st.hi, s.hi);
+    if constexpr (K != K_MX) {
+      const Stats s = stats_of(v[i]);
+      st.amax = __builtin_fmaxf(st.amax, s.amax);
+      st.lo = __builtin_fminf(st.lo, s.lo);
+      st.hi = __builtin_fmaxf(st.hi, s.hi);
+    }
   }
+  if constexpr (K == K_MX) {
+    // K % 32 == 0, so the 4 threads of a block are all inside or all past
+    // the row; every thread takes part in the shuffles
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t vec = tid + (int64_t)kThreads * i;
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[i][e]));
+      m = __builtin_fmaxf(m, shfl_xor(m, 1));
+      m = __builtin_fmaxf(m, shfl_xor(m, 2));
+      if (vec < kvecs) {
+        const int ex = mx_shared_exponent(m);
+        // y / 2^e (exact) lies in [-6, 6]; the gfx950 conversion (scale 1)
+        // rounds to the nearest E2M1 value, ties to the even code, element
+        // 2 j into the low nibble of byte j
+        float t[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t[k] = __builtin_ldexpf(v[i][k], -ex);
+        uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[0], t[1], 1.0f, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, t[2], t[3], 1.0f, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, t[4], t[5], 1.0f, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, t[6], t[7], 1.0f, 3);
+        reinterpret_cast<uint32_t*>(codes)[v0 + vec] = word;
+        if ((vec & 3) == 0) reinterpret_cast<uint8_t*>(scales)[(v0 + vec) >> 2] = (uint8_t)(ex + 127);
+      }
+    }
+    return;
+  } else {
   for (int o = 1; o < 64; o <<= 1) {
     st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
     st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
@@ -670,6 +705,7 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __rest
     if (vec < kvecs) quantize_store<K>(v[i], p, codes, v0 + vec);
   }
   if (tid == 0) store_params<K>(p, scales, zeros, row);
+  }
 }
 
 template <int K, bool BF16, bool RMS>
@@ -701,6 +737,9 @@ void launch_norm_quant_fmt(qg_format fmt, const void* src, int64_t rows, int64_t
   else if (fmt == QG_INT8_ASYM)
     launch_norm_quant_t<K_INT8_ASYM, BF16, RMS>(src, rows, kvecs, gamma, beta, eps, codes,
                                                scales, zeros, stream);
+  else if (fmt == QG_MXFP4)
+    launch_norm_quant_t<K_MX, BF16, RMS>(src, rows, kvecs, gamma, beta, eps, codes, scales,
+                                        zeros, stream);
   else
     launch_norm_quant_t<K_FP8, BF16, RMS>(src, rows, kvecs, gamma, beta, eps, codes, scales,
                                          zeros, stream);

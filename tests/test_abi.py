@@ -121,6 +121,11 @@ def test_norm_quant_validation(lib):
     assert n(L, s8, A16, _lib.BF16, MIS, A16c, e, 4, 256, A16d, A16e, None, None) == _lib.ERR_ALIGN
     assert n(L, f8, A16, _lib.BF16, A16b, A16c, e, 4, 16392, A16d, A16e, None,
              None) == _lib.ERR_UNSUPPORTED
+    mx = _lib.MXFP4
+    assert n(L, mx, A16, _lib.BF16, A16b, A16c, e, 4, 264, A16d, A16e, None,
+             None) == _lib.ERR_GEOMETRY                       # K % 32
+    assert n(L, mx, A16, _lib.BF16, A16b, A16c, e, 4, 256, A16d, A16e, A16, None) == _lib.ERR_NULL
+    assert n(L, mx, A16, _lib.BF16, A16b, A16c, e, 4, 256, A16d, None, None, None) == _lib.ERR_NULL
 
 
 def test_qgemm_swiglu_validation(lib):
