@@ -238,6 +238,45 @@ def bench_projections(qg, torch, copies, stream, reps=40, tiled=True):
     return out
 
 
+def bench_swiglu_decode(qg, torch, copies, stream, reps=40):
+    """The fused SwiGLU GEMV on the gate+up projection (tiled codes) at
+    M = 1, 4, 16, against the unfused path (the GEMV writing [M][2I], then
+    torch's SiLU(g) * u): graphs of `reps` launches over the rotating copies,
+    median of 9 replays."""
+    idx = [i for i, p in enumerate(copies[0]) if p["name"] == "gate_up"][0]
+    p0 = copies[0][idx]
+    n2, k = p0["n"], p0["k"]
+    i = n2 // 2
+    dev = p0["x"].device
+    out = {}
+    for m in (1, 4, 16):
+        h = torch.empty((m, i), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((m, n2), dtype=torch.bfloat16, device=dev)
+
+        def fused():
+            for r in range(reps):
+                p = copies[r % len(copies)][idx]
+                qg.qgemv_swiglu(p["x"][:m], p["tiled"], p["s"], p["z"], "int4_asym", out=h)
+
+        def unfused():
+            for r in range(reps):
+                p = copies[r % len(copies)][idx]
+                qg.qgemv_tiled(p["x"][:m], p["tiled"], p["s"], p["z"], "int4_asym", out=y)
+                torch.mul(torch.nn.functional.silu(y[:, :i]), y[:, i:], out=h)
+        res = {}
+        for name, fn in (("fused", fused), ("unfused", unfused)):
+            g = graph_of(fn, stream)
+            time_graph(g, stream)
+            ts = sorted(time_graph(g, stream) / reps for _ in range(9))
+            res[name] = ts[4]
+            del g
+        b = p0["codes"].numel() * 4 + p0["s"].numel() * 4 + m * k * 2 + m * i * 2
+        out[f"m{m}"] = dict(us=round(res["fused"] * 1e6, 3), gbs=round(b / res["fused"] / 1e9, 1),
+                            frac=round(b / res["fused"] / 1e9 / HBM_PEAK_GBS, 4),
+                            unfused_us=round(res["unfused"] * 1e6, 3))
+    return out
+
+
 # ---------------------------------------------------- clocks and power
 
 def _card_dir(torch, dev):
@@ -921,6 +960,7 @@ def main():
         detail["decode_projections_m1"] = bench_projections(qg, torch, copies, stream)
         detail["decode_projections_m1_canonical"] = bench_projections(qg, torch, copies, stream,
                                                                       tiled=False)
+        detail["decode_swiglu_gate_up"] = bench_swiglu_decode(qg, torch, copies, stream)
         tc = bench_decode(qg, torch, copies, 1, args.steps, args.warmup, stream, tiled=False)
         detail["decode_layer_m1_canonical"] = dict(
             gbs=args.steps * per_layer / tc / 1e9,

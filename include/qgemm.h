@@ -189,6 +189,32 @@ qg_status qg_qgemv_tiled(qg_format wfmt, const void* x, int64_t M, const void* t
                          int64_t group, void* y, void* stream);
 
 /*
+ * qg_qgemv_swiglu -- fused SwiGLU projection of W4A16 decode:
+ * H = SiLU(X W_gate^T) * (X W_up^T) for 1 <= M <= 16 rows of X ([SRV]
+ * section 4.6: the gate and up projections as one product over the
+ * concatenation [W_gate; W_up], SiLU and the product formed in registers, H
+ * written once; SiLU(g) = g / (1 + e^-g)).  Each of g and u is the qg_qgemv
+ * sum in fp32; h = bf16(SiLU(g) * u), one rounding.
+ *   wfmt       QG_INT4_SYM (wzeros NULL) or QG_INT4_ASYM; group 128.
+ *   x          bf16 [M][K].
+ *   wcodes, wscales, wzeros   the quantized [N2][K] concatenation: rows
+ *              0 .. N2/2 - 1 are W_gate, rows N2/2 .. N2 - 1 are W_up;
+ *              codes canonical (tiled = 0, qg_quantize_pack) or in the tile
+ *              layout of qg_tile_gemv_weights over all N2 rows (tiled = 1);
+ *              scales and zeros fp16 [N2][K/group] either way.
+ *   N2         2 I, even.
+ *   h          bf16 [M][I].
+ * Limits: K a multiple of 512 and at most 32768 (M = 1), 16384 (M = 2..4)
+ * or 8192 (M = 5..16), QG_ERR_UNSUPPORTED otherwise.
+ * Errors: QG_ERR_GEOMETRY (M outside 1..16, N2 odd or < 2, group not
+ * dividing K, tiled not 0/1), QG_ERR_FORMAT, QG_ERR_UNSUPPORTED, QG_ERR_NULL,
+ * QG_ERR_ALIGN, QG_ERR_HIP.
+ */
+qg_status qg_qgemv_swiglu(qg_format wfmt, const void* x, int64_t M, const void* wcodes,
+                          const void* wscales, const void* wzeros, int64_t N2, int64_t K,
+                          int64_t group, int tiled, void* h, void* stream);
+
+/*
  * qg_qgemm -- quantized GEMM Y = dequant(A) * dequant(W)^T, fp32
  * accumulation, bf16 output (round to nearest even).  Format pairs:
  *   W INT4_SYM|INT4_ASYM, A BF16_ACT : W4A16 prefill ([SRV] 1.3; [L6] sec. 2);

@@ -279,6 +279,49 @@ def qgemv_tiled(x: torch.Tensor, codes: TiledCodes, scales: torch.Tensor, zeros,
     return y
 
 
+def qgemv_swiglu(x: torch.Tensor, codes, scales: torch.Tensor, zeros, fmt: str,
+                 group: int = 128, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused SwiGLU decode projection h = SiLU(x W_gate^T) * (x W_up^T) for
+    1 <= M <= 16 rows of bf16 x [M][K] and INT4 weights quantized as the
+    [2I][K] concatenation [W_gate; W_up]; codes canonical (int32 [2I][K/8])
+    or TiledCodes of that concatenation.  Returns h bf16 [M][I]."""
+    dev = x.device        # checked for the GPU below, after the shapes
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be bf16 [M][K]")
+    if not fmt.startswith("int4"):
+        raise ValueError("qgemv_swiglu: weights must be int4_sym or int4_asym")
+    m, k = x.shape
+    tiled = isinstance(codes, TiledCodes)
+    if tiled:
+        n2 = codes.n
+        if codes.k != k:
+            raise ValueError(f"tiled codes are for K={codes.k}, x has K={k}")
+        _expect(codes.data, ((n2 + 15) // 16 * 16 * k // 2,), torch.uint8, "tiled codes", dev)
+        data = codes.data
+    else:
+        n2 = codes.shape[0]
+        _expect(codes, (n2, k // 8), torch.int32, "weight codes", dev)
+        data = codes
+    if n2 % 2:
+        raise ValueError("invalid quantization geometry: [W_gate; W_up] needs an even row count")
+    if group <= 0 or k % group:
+        raise ValueError("invalid quantization geometry: group must divide K")
+    _expect(scales, (n2, k // group), torch.float16, "weight scales", dev)
+    if fmt in _ASYM:
+        _expect(zeros, (n2, k // group), torch.float16, "weight zeros", dev)
+    else:
+        _expect_none(zeros, "weight zeros")
+    if out is not None:
+        _expect(out, (m, n2 // 2), torch.bfloat16, "out", dev)
+    _dev(x)
+    lib = _lib.load()
+    h = torch.empty((m, n2 // 2), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_qgemv_swiglu(FORMATS[fmt], _ptr(x), m, _ptr(data), _ptr(scales),
+                                   _ptr(zeros), n2, k, group, 1 if tiled else 0, _ptr(h),
+                                   _stream(dev)))
+    return h
+
+
 def qgemm(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, w_zeros, wfmt: str,
           afmt: str, a_scales=None, a_zeros=None, k: int | None = None,
           group: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -269,6 +269,30 @@ qg_status qg_qgemv_tiled(qg_format wfmt, const void* x, int64_t M, const void* t
   return qgemv_common(true, wfmt, x, M, tiled_codes, wscales, wzeros, N, K, group, y, stream);
 }
 
+qg_status qg_qgemv_swiglu(qg_format wfmt, const void* x, int64_t M, const void* wcodes,
+                          const void* wscales, const void* wzeros, int64_t N2, int64_t K,
+                          int64_t group, int tiled, void* h, void* stream) {
+  if (!is_int4(wfmt))
+    return fail(QG_ERR_FORMAT, "qgemv_swiglu: weights must be INT4_SYM or INT4_ASYM");
+  if (M < 1 || M > 16) return fail(QG_ERR_GEOMETRY, "qgemv_swiglu: M must be in 1..16");
+  if (N2 < 2 || N2 % 2 != 0 || N2 > (int64_t)1 << 30)
+    return fail(QG_ERR_GEOMETRY, "qgemv_swiglu: N2 = 2 I must be even and positive");
+  if (tiled != 0 && tiled != 1) return fail(QG_ERR_GEOMETRY, "qgemv_swiglu: tiled must be 0 or 1");
+  qg_status st = check_quant_operand(wfmt, N2, K, group, wcodes, wscales, wzeros);
+  if (st != QG_OK) return st;
+  if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemv_swiglu: only group 128 is implemented");
+  if (!qg::qgemv_swiglu_supported(M, K))
+    return fail(QG_ERR_UNSUPPORTED, "qgemv_swiglu: K must be a multiple of 512, at most 32768 "
+                                    "(M = 1), 16384 (M = 2..4) or 8192 (M = 5..16)");
+  if (!fits_offsets(N2, K / 2) || !fits_offsets(M, K * 2))
+    return fail(QG_ERR_UNSUPPORTED, "qgemv_swiglu: operand larger than 2 GiB");
+  if (!x || !h) return fail(QG_ERR_NULL, "qgemv_swiglu: x and h are required");
+  if (!aligned16(x) || !aligned16(h))
+    return fail(QG_ERR_ALIGN, "qgemv_swiglu: x, h must be 16-byte aligned");
+  return from_hip(qg::launch_qgemv_swiglu(wfmt == QG_INT4_ASYM, tiled == 1, x, M, wcodes,
+                                          wscales, wzeros, N2, K, h, (hipStream_t)stream));
+}
+
 qg_status qg_tile_gemv_weights(const void* codes, int64_t N, int64_t K, void* tiled_codes,
                                void* stream) {
   if (N < 1 || N > (int64_t)1 << 30 || K < 128 || K % 128 != 0)

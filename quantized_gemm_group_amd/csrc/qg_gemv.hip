@@ -84,12 +84,16 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 template <bool TILED>
 struct WLayout {
   static constexpr int kGroupStride = TILED ? 1024 : 64;   // bytes between groups of a row
-  // lane's byte offset of group 0 of its row (li) in tile `tile`
-  __device__ static uint32_t lane_off(int tile, int li, int lg, int N, int K) {
-    const int n = tile * 16 + li;
+  // byte offset of the lane's 16 bytes (quarter lg) of group 0 of row n
+  __device__ static uint32_t row_off(int n, int lg, int N, int K) {
     if (n >= N) return 0x80000000u;                       // past the end: reads zero
-    return TILED ? (uint32_t)tile * (uint32_t)(K / 128) * 1024u + (uint32_t)(li * 64 + lg * 16)
+    return TILED ? (uint32_t)(n >> 4) * (uint32_t)(K / 128) * 1024u +
+                       (uint32_t)((n & 15) * 64 + lg * 16)
                  : (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(lg * 16);
+  }
+  // the same for row li of tile `tile`
+  __device__ static uint32_t lane_off(int tile, int li, int lg, int N, int K) {
+    return row_off(tile * 16 + li, lg, N, K);
   }
   __device__ static int64_t bytes(int N, int K) {
     return TILED ? (int64_t)((N + 15) / 16) * 16 * K / 2 : (int64_t)N * K / 2;
@@ -571,6 +575,180 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
   }
 }
 
+// SwiGLU decode GEMV for M <= MM (1 or 4) rows of x: h[m][i] = SiLU(g) * u
+// with g and u the GEMV outputs of rows i and I + i of the concatenation
+// [W_gate; W_up] (《推理优化与量化算子深度技术调研》 section 4.6: the gate and up
+// projections as one product over the concatenated weight, SiLU(g) * u
+// formed in registers and written once).  Workgroup = one 16-channel tile i
+// of h and KS waves over the K-slices, as in qgemv_wave_kernel, but every
+// wave streams two weight tiles -- the gate rows of the tile and the same
+// channels' up rows -- against one x slice (loaded, permuted and summed
+// once).  After the K-slice sum through LDS the first wave holds g and u of
+// each output in the same lane and writes bf16(SiLU(g) * u) (fp32, e^-g
+// from the hardware exponential).  The codes of either layout (canonical
+// or tiled) are addressed per row, so I needs no alignment.
+// LDS: [x slices: KS * MM * NG * 256 bytes][partials: KS * 2 KiB].
+template <bool ASYM, int NG, int MM, bool TILED>
+__global__ __launch_bounds__(1024) void qgemv_swiglu_kernel(const uint16_t* __restrict__ x, int M,
+                                                            const uint32_t* __restrict__ w,
+                                                            const uint16_t* __restrict__ s16,
+                                                            const uint16_t* __restrict__ z16,
+                                                            int I, int K, int KS,
+                                                            uint16_t* __restrict__ h,
+                                                            uint32_t mask, uint32_t cmag) {
+  extern __shared__ float4 lds4[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds4);
+  constexpr int kXBytes = MM * NG * 256;       // one wave's x slice
+  constexpr int kXLoads = NG / 4;              // 1 KiB loads per row of x
+  const int G = K / kGroup;
+  const int N2 = 2 * I;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int kw = wave;
+  const int i = blockIdx.x * 16 + li;          // output channel of this lane's rows
+  const int gb = kw * NG;
+  using WL = WLayout<TILED>;
+
+  // ---- 1. loads: x slice, the (s, z) of both rows, both tiles' codes
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x, (int64_t)M * K * 2);
+  u32x4 xr[MM * kXLoads];
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q)
+      xr[m * kXLoads + q] = bload(xres, m < M ? (uint32_t)(m * K + gb * 128 + q * 512 + 8 * lane) * 2
+                                              : 0x80000000u, 0);
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N2 * G * 2);
+  const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N2 * G * 2 : 0);
+  uint32_t sv[2][NG / 2], zv[2][NG / 2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = t * I + i;                   // gate row i, up row I + i
+    const uint32_t soff = i < I ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
+    if constexpr (NG == 4) {
+      const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
+      const uint2 z2 = ASYM ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0))
+                            : uint2{0u, 0u};
+      sv[t][0] = s2.x;
+      sv[t][1] = s2.y;
+      zv[t][0] = z2.x;
+      zv[t][1] = z2.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < NG / 8; ++c) {
+        const u32x4 s4 = bload(sres, soff, 16 * c);
+        const u32x4 z4 = ASYM ? bload(zres, soff, 16 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[t][4 * c + e] = s4[e];
+          zv[t][4 * c + e] = z4[e];
+        }
+      }
+    }
+  }
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N2, K));
+  u32x4 wr[2][NG];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t woff = WL::row_off(i < I ? t * I + i : N2, lg, N2, K);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) wr[t][j] = WL::load(wres, woff, (gb + j) * WL::kGroupStride);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before any use
+
+  // ---- 2. the x slice, pair-permuted, into this wave's LDS region
+  uint8_t* const xw = lds + wave * kXBytes;
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q)
+      reinterpret_cast<u32x4*>(xw)[m * NG * 16 + q * 64 + lane] =
+          pair_activations(xr[m * kXLoads + q]);
+  float gsum[MM == 1 ? kXLoads : 1];
+  if constexpr (MM == 1) {
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part += __uint_as_float(xr[q][e] << 16);
+        part += __uint_as_float(xr[q][e] & 0xffff0000u);
+      }
+      part += shfl_xor(part, 1);
+      part += shfl_xor(part, 2);
+      part += shfl_xor(part, 4);
+      part += shfl_xor(part, 8);
+      gsum[q] = part;
+    }
+  }
+
+  // ---- 3. groups: both tiles against the same x fragments and group sums
+  const int mrow = li < M ? li : 0;
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(xw) + mrow * NG * 16 + lg * 4;
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  float yacc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    bf16x8 bx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bx[q] = as_bf16x8(xrow[j * 16 + q]);
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[t][0] = acc[t][1] = sacc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[t][q & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            bx[q], as_bf16x8(unpack_word<ASYM>(wr[t][j][q], mask, cmag)), acc[t][q & 1], 0, 0, 0);
+      if constexpr (MM != 1)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bx[q], as_bf16x8(ones), sacc, 0, 0, 0);
+    }
+    if constexpr (MM == 1) {
+      const float sx = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gsum[j >> 2]), 16 * (j & 3)));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[r] = sx;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float sc = f16_bits_to_f32((sv[t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+      float cc = 136.f;
+      if constexpr (ASYM) cc = 128.f + f16_bits_to_f32((zv[t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        yacc[t][r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sacc[r], acc[t][0][r] + acc[t][1][r]),
+                                    yacc[t][r]);
+    }
+  }
+
+  // ---- 4. sum the K-slices: red[kw][t][r][lane]; lane (li, lg) of the
+  //      first wave writes h[m = 4 lg + r][i] for m < M
+  float* red = reinterpret_cast<float*>(lds + KS * kXBytes);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((kw * 2 + t) * 4 + r) * 64 + lane] = yacc[t][r];
+  __syncthreads();
+  if (wave == 0 && i < I) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r;
+      if (m < M) {
+        float g = 0.f, u = 0.f;
+        for (int k2 = 0; k2 < KS; ++k2) {
+          g += red[((k2 * 2 + 0) * 4 + r) * 64 + lane];
+          u += red[((k2 * 2 + 1) * 4 + r) * 64 + lane];
+        }
+        h[(int64_t)m * I + i] = (uint16_t)f32_to_bf16_bits(g / (1.f + __expf(-g)) * u);
+      }
+    }
+  }
+}
+
 // Codes of one word in natural order: dword d holds the bf16 pair
 // (128 + u_{2d}, 128 + u_{2d+1}), so activations read straight from memory
 // need no permute.  Byte d of w and of w >> 4 go to the two halves (one
@@ -615,7 +793,12 @@ __device__ __forceinline__ u32x4 transpose_rows(const u32x4& v) {
 // D[m = 4 lg + r][n = li] of each channel tile, and an MFMA against 1.0
 // gives the group sums of x in the same layout.
 // LDS: partial sums [KS][R][4][64] floats.
-template <bool ASYM, int NG, int R, bool TILED>
+// SWIGLU (R = 2): N is the row count 2I of [W_gate; W_up]; tile 0 of the
+// wave is the gate rows of output channels 16 b .. 16 b + 15 and tile 1 the
+// same channels' up rows (rows I + ...), and the first wave writes
+// h[m][i] = bf16(SiLU(g) * u) into y as [M][I] (《推理优化与量化算子深度技术调研》
+// section 4.6).
+template <bool ASYM, int NG, int R, bool TILED, bool SWIGLU = false>
 __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restrict__ x, int M,
                                                          const uint32_t* __restrict__ w,
                                                          const uint16_t* __restrict__ s16,
@@ -643,10 +826,13 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
   const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
   uint32_t woff[R];
   uint32_t sv[R][NG / 2], zv[R][NG / 2];
+  static_assert(!SWIGLU || R == 2, "SwiGLU pairs a gate and an up tile");
+  const int I = N / 2;
+  const int ich = blockIdx.x * 16 + li;          // SwiGLU: output channel of the lane
 #pragma unroll
   for (int t = 0; t < R; ++t) {
-    const int n = n0 + 16 * t + li;
-    woff[t] = WL::lane_off(blockIdx.x * R + t, li, lg, N, K);
+    const int n = SWIGLU ? (ich < I ? t * I + ich : N) : n0 + 16 * t + li;
+    woff[t] = SWIGLU ? WL::row_off(n, lg, N, K) : WL::lane_off(blockIdx.x * R + t, li, lg, N, K);
     if (woff[t] != 0x80000000u) woff[t] += (uint32_t)(gb * WL::kGroupStride);
     const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
     if constexpr (NG == 4) {
@@ -726,7 +912,22 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[((kw * R + t) * 4 + r) * 64 + lane] = yacc[t][r];
   __syncthreads();
-  if (kw == 0) {
+  if constexpr (SWIGLU) {
+    if (kw == 0 && ich < I) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * lg + r;
+        if (m < M) {
+          float g = 0.f, u = 0.f;
+          for (int k2 = 0; k2 < KS; ++k2) {
+            g += red[((k2 * 2 + 0) * 4 + r) * 64 + lane];
+            u += red[((k2 * 2 + 1) * 4 + r) * 64 + lane];
+          }
+          y[(int64_t)m * I + ich] = (uint16_t)f32_to_bf16_bits(g / (1.f + __expf(-g)) * u);
+        }
+      }
+    }
+  } else if (kw == 0) {
 #pragma unroll
     for (int t = 0; t < R; ++t) {
       const int n = n0 + 16 * t + li;
@@ -874,6 +1075,77 @@ int pick_wave_ng(int M, int N, int K) {
   return 0;
 }
 
+// Groups per wave of the SwiGLU wave kernel (0: not applicable): the
+// per-wave GEMV's choice with at most 16 K-slices and the LDS within 160
+// KiB; two weight tiles per wave, so 4 groups (8 for M = 1 when K needs
+// them; 16 only for M = 1).
+int swiglu_wave_ng(int M, int K) {
+  const int G = K / kGroup;
+  if (G % 4 != 0) return 0;
+  const int mm = M == 1 ? 1 : 4;
+  auto fits = [&](int ng) {
+    const int ks = G / ng;
+    return G % ng == 0 && ks <= 16 && (size_t)ks * (mm * ng * 256 + 2048) <= 160 * 1024;
+  };
+  if (fits(4)) return 4;
+  if (fits(8)) return 8;
+  if (M == 1 && fits(16)) return 16;
+  return 0;
+}
+
+// SwiGLU GEMV launch: M <= 4 on the per-wave kernel (gate and up tiles in
+// every wave, NG groups per wave so that K splits into at most 16 slices),
+// 5 <= M <= 16 on the 16-row kernel with the gate / up tile pair.  Returns
+// hipErrorInvalidValue for shapes neither covers (checked by the caller).
+template <bool TILED>
+hipError_t launch_swiglu_t(bool asym, const void* x, int M, const void* w, const void* s,
+                           const void* z, int N2, int K, void* h, hipStream_t stream) {
+  const int G = K / kGroup;
+  const int I = N2 / 2;
+  const int tiles = (I + 15) / 16;
+  const uint32_t mask = 0x000F000Fu, cmag = asym ? 0x43004300u : 0x43084308u;
+  if (M <= 4) {
+    const int ng = swiglu_wave_ng(M, K);
+    if (!ng) return hipErrorInvalidValue;
+    const int ks = G / ng;
+    const int mm = M == 1 ? 1 : 4;
+    const size_t lds = (size_t)ks * (mm * ng * 256 + 2048);
+#define QG_SWIGLU_WAVE(A, NGV, MMV)                                                              \
+  hipLaunchKernelGGL((qgemv_swiglu_kernel<A, NGV, MMV, TILED>), dim3(tiles), dim3(64 * ks), lds, \
+                     stream, (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,       \
+                     (const uint16_t*)z, I, K, ks, (uint16_t*)h, mask, cmag)
+    if (asym) {
+      if (mm == 1) {
+        if (ng == 4) QG_SWIGLU_WAVE(true, 4, 1); else if (ng == 8) QG_SWIGLU_WAVE(true, 8, 1);
+        else QG_SWIGLU_WAVE(true, 16, 1);
+      } else {
+        if (ng == 4) QG_SWIGLU_WAVE(true, 4, 4); else QG_SWIGLU_WAVE(true, 8, 4);
+      }
+    } else {
+      if (mm == 1) {
+        if (ng == 4) QG_SWIGLU_WAVE(false, 4, 1); else if (ng == 8) QG_SWIGLU_WAVE(false, 8, 1);
+        else QG_SWIGLU_WAVE(false, 16, 1);
+      } else {
+        if (ng == 4) QG_SWIGLU_WAVE(false, 4, 4); else QG_SWIGLU_WAVE(false, 8, 4);
+      }
+    }
+#undef QG_SWIGLU_WAVE
+    return hipGetLastError();
+  }
+  if (G % 4 != 0 || G / 4 > 16) return hipErrorInvalidValue;
+  const int ks = G / 4;
+  const size_t lds = (size_t)ks * 2 * 4 * 64 * sizeof(float);
+  if (asym)
+    hipLaunchKernelGGL((qgemv_m16_kernel<true, 4, 2, TILED, true>), dim3(tiles), dim3(64 * ks), lds,
+                       stream, (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
+                       (const uint16_t*)z, N2, K, ks, (uint16_t*)h, mask, cmag);
+  else
+    hipLaunchKernelGGL((qgemv_m16_kernel<false, 4, 2, TILED, true>), dim3(tiles), dim3(64 * ks),
+                       lds, stream, (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,
+                       (const uint16_t*)z, N2, K, ks, (uint16_t*)h, mask, cmag);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // LDS per workgroup: x (M*K*2 bytes when staged, <= 48 KiB) + (s, c) pairs
@@ -947,6 +1219,21 @@ hipError_t launch_qgemv(bool asym, bool tiled, const void* x, int64_t M, const v
                         hipStream_t stream) {
   return tiled ? launch_qgemv_t<true>(asym, x, M, wcodes, wscales, wzeros, N, K, y, stream)
                : launch_qgemv_t<false>(asym, x, M, wcodes, wscales, wzeros, N, K, y, stream);
+}
+
+bool qgemv_swiglu_supported(int64_t M, int64_t K) {
+  const int G = (int)(K / kGroup);
+  if (M <= 4) return swiglu_wave_ng((int)M, (int)K) != 0;
+  return G % 4 == 0 && G / 4 <= 16;
+}
+
+hipError_t launch_qgemv_swiglu(bool asym, bool tiled, const void* x, int64_t M,
+                               const void* wcodes, const void* wscales, const void* wzeros,
+                               int64_t N2, int64_t K, void* h, hipStream_t stream) {
+  return tiled ? launch_swiglu_t<true>(asym, x, (int)M, wcodes, wscales, wzeros, (int)N2, (int)K,
+                                       h, stream)
+               : launch_swiglu_t<false>(asym, x, (int)M, wcodes, wscales, wzeros, (int)N2, (int)K,
+                                        h, stream);
 }
 
 }  // namespace qg

@@ -48,6 +48,13 @@ hipError_t launch_qgemv(bool asym, bool tiled, const void* x, int64_t M, const v
                         const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
                         hipStream_t stream);
 
+// SwiGLU decode GEMV over [W_gate; W_up] (N2 = 2I rows) into h [M][I];
+// qgemv_swiglu_supported tells which (M, K) the kernels cover.
+bool qgemv_swiglu_supported(int64_t M, int64_t K);
+hipError_t launch_qgemv_swiglu(bool asym, bool tiled, const void* x, int64_t M,
+                               const void* wcodes, const void* wscales, const void* wzeros,
+                               int64_t N2, int64_t K, void* h, hipStream_t stream);
+
 hipError_t launch_tile_gemv_codes(const void* codes, int64_t N, int64_t K, void* tiled,
                                   hipStream_t stream);
 

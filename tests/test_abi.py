@@ -292,3 +292,18 @@ def test_tiled_gemv_validation(lib):
     assert g(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
     assert g(_lib.INT8_SYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_FORMAT
     assert g(_lib.INT4_ASYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_NULL
+
+
+def test_qgemv_swiglu_validation(lib):
+    f = lib.qg_qgemv_swiglu
+    i4 = _lib.INT4_SYM
+    ok = (A16, 1, A16b, A16c, None, 64, 4096, 128, 0, A16e, None)
+    assert f(_lib.INT8_SYM, *ok) == _lib.ERR_FORMAT
+    assert f(i4, A16, 17, *ok[2:]) == _lib.ERR_GEOMETRY
+    assert f(i4, *ok[:5], 63, *ok[6:]) == _lib.ERR_GEOMETRY             # odd N2
+    assert f(i4, *ok[:8], 2, *ok[9:]) == _lib.ERR_GEOMETRY              # tiled flag
+    assert f(i4, *ok[:6], 4096, 64, *ok[8:]) == _lib.ERR_UNSUPPORTED    # group
+    assert f(i4, *ok[:6], 640, *ok[7:]) == _lib.ERR_UNSUPPORTED         # K % 512
+    assert f(i4, A16, 8, *ok[2:6], 16384, *ok[7:]) == _lib.ERR_UNSUPPORTED   # M > 4, K > 8192
+    assert f(_lib.INT4_ASYM, *ok) == _lib.ERR_NULL
+    assert f(i4, *ok[:9], MIS, None) == _lib.ERR_ALIGN

@@ -80,3 +80,77 @@ def test_swiglu_equals_unfused():
     y = host(qg.qgemm(x, codes, scales, None, "int4_sym", "bf16")).astype(np.float64)
     g, u = y[:, :384], y[:, 384:]
     assert og.rel_fro(h, og.silu(g) * u) <= 4e-3
+
+
+# ------------------------------------------------------------ decode GEMV
+
+def _check_small(h, ref, what):
+    """rel. Frobenius <= 2e-3, or for fewer than 1024 outputs the
+    per-element bound of one bf16 step plus a small absolute floor."""
+    finite_checks(h)
+    if h.size < 1024:
+        floor = 1e-3 * np.sqrt(np.mean(ref ** 2))
+        bad = np.abs(h - ref) > 2.0 ** -8 * np.abs(ref) + floor
+        assert not bad.any(), f"{what}: {bad.sum()} outputs beyond one bf16 step"
+        return
+    check(h, ref, what)
+
+
+# M = 1 (one x row, group sums by shuffles), 2..4 (the 4-row layout), 5..16
+# (the 16-row kernel with the gate / up tile pair); K from one 512 slice to
+# 16 slices; I ragged (not a multiple of 16) and I = 14336 / 2 shapes
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("m,k,i", [(1, 512, 40), (1, 4096, 1000), (1, 16384, 24), (3, 1024, 33),
+                                   (4, 2048, 200), (2, 8192, 17), (5, 512, 48), (9, 4096, 300),
+                                   (16, 8192, 64), (16, 1536, 1)])
+def test_qgemv_swiglu_small(m, k, i, asym):
+    dev = device()
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"qgemv_swiglu m={m} k={k} I={i} {fmt}", flush=True)
+    c = small_case(m, k, 2 * i, seed=7 * m + i + k, w_outlier=(0.01, 20.0))
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
+    if asym:
+        q, s, z = oi.quantize_asym(c["w"], 128)
+    else:
+        (q, s), z = oi.quantize_sym(c["w"], 128), None
+    packed = oi.pack_int4(q)
+    assert (host(codes) == packed).all()
+    x = to_dev(c["x"], dev)
+    h = host(qg.qgemv_swiglu(x, codes, scales, zeros, fmt))
+    ht = host(qg.qgemv_swiglu(x, qg.tile_gemv_weights(codes), scales, zeros, fmt))
+    assert h.shape == (m, i)
+    # same arithmetic in the same order on either code layout
+    assert (ht.view(np.uint32) == h.view(np.uint32)).all(), "tiled differs from canonical"
+    _check_small(h, og.swiglu_reference(bf16_as_f32(c["x"]), packed, s, z, 128),
+                 f"qgemv_swiglu {fmt}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_qgemv_swiglu_llama3_8b_gate_up_sampled(m):
+    # the decode workload's gate+up projection (K = 4096, 28672 rows =
+    # gate and up of 14336 channels), asymmetric INT4 with outlier input
+    # channels; the oracle quantizes sampled channels' gate and up rows
+    dev = device()
+    c = workload_case("llama3_8b_decode", 2)
+    n2, k = c["n"], c["k"]
+    i = n2 // 2
+    print(f"qgemv_swiglu llama3_8b gate+up M={m} K={k} I={i}", flush=True)
+    codes, scales, zeros = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_asym", 128)
+    tiled = qg.tile_gemv_weights(codes)
+    h = host(qg.qgemv_swiglu(c["x"][:m].to(dev), tiled, scales, zeros, "int4_asym"))
+    ch = np.unique(np.concatenate([np.arange(16), np.arange(i - 16, i),
+                                   rng_for(88 + m).choice(i, 160, replace=False)]))
+    rows = np.concatenate([ch, ch + i])
+    q, s, z = oi.quantize_asym(c["w"][rows], 128)
+    assert (host(codes)[rows] == oi.pack_int4(q)).all()
+    packed_all = np.zeros((n2, k // 8), np.int32)
+    scales_all = np.ones((n2, k // 128), np.float16)
+    zeros_all = np.zeros((n2, k // 128), np.float16)
+    packed_all[rows], scales_all[rows], zeros_all[rows] = oi.pack_int4(q), s, z
+    ref = og.swiglu_reference(bf16_as_f32(c["x"][:m]), packed_all, scales_all, zeros_all, 128,
+                              channels=ch)
+    check(h[:, ch], ref, f"qgemv_swiglu llama3 M={m}")
+    # and against the unfused decode path: the GEMV, then SiLU(g) * u
+    y = host(qg.qgemv_tiled(c["x"][:m].to(dev), tiled, scales, zeros, "int4_asym"))
+    y = y.astype(np.float64)
+    assert og.rel_fro(h, og.silu(y[:, :i]) * y[:, i:]) <= 4e-3
