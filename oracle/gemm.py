@@ -115,3 +115,24 @@ def swiglu_reference(x, packed, scales, zeros, group: int, channels=None) -> np.
     gate = w4a16_reference(x, packed, scales, zeros, group, rows=ch)
     up = w4a16_reference(x, packed, scales, zeros, group, rows=ch + i)
     return silu(gate) * up
+
+
+def fp8_swiglu_reference(xq, sx, wq, sw, channels=None) -> np.ndarray:
+    """h [M][I] = SiLU(g) * u for FP8 W8A8 operands: per-token activation
+    codes xq [M][K] with scales sx, and the per-row quantized [2I][K]
+    concatenation [W_gate; W_up] (codes wq, scales sw), gate rows first.  g
+    and u are the fp64 products of the dequantized operands, i.e. the
+    rescaled code products of figure 6-2 of 《第 6 课：量化源码走读》, and the
+    activation follows 《推理优化与量化算子深度技术调研》 section 4.6 (the
+    W8A8 GEMM with dequantization and activation fused).  ``channels``
+    optionally selects intermediate channels (columns of h)."""
+    wq = np.asarray(wq)
+    sw = np.asarray(sw).reshape(-1)
+    n2 = wq.shape[0]
+    if n2 % 2:
+        raise ValueError("invalid quantization geometry")
+    i = n2 // 2
+    ch = np.arange(i) if channels is None else np.asarray(channels)
+    gate = fp8_reference(xq, sx, wq[ch], sw[ch])
+    up = fp8_reference(xq, sx, wq[ch + i], sw[ch + i])
+    return silu(gate) * up

@@ -2,6 +2,7 @@
 forms for constant operands, one-hot activations, and the error metric."""
 
 import numpy as np
+import pytest
 
 from oracle import fp8, gemm, intquant as IQ, mx
 
@@ -144,3 +145,41 @@ def test_parity_bound_rejects_a_missing_cross_term():
     assert gemm.rel_fro(rounded, ref) <= 2e-3
     assert gemm.rel_fro(no_cross, ref) > 100 * 2e-3
     assert gemm.rel_fro(off_by_one, ref) > 2e-3
+
+
+def test_fp8_swiglu_reference_brute_force():
+    # tiny case against a pure-Python evaluation of the definition: decode
+    # every E4M3 code from its bit fields, rescale by s_x s_w, sum, then
+    # SiLU(gate) * up with the gate rows first (a swapped split, or the
+    # scales left out, fails the comparison)
+    import math
+    from oracle import fp8 as F8
+    rng = np.random.default_rng(12)
+    m, k, i = 2, 64, 3
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    w = (rng.standard_normal((2 * i, k)) * 0.05).astype(np.float32)
+    xq, sx = F8.quantize_rows(x)
+    wq, sw = F8.quantize_rows(w)
+
+    def dec(c):
+        c = int(c)
+        e, f = (c >> 3) & 15, c & 7
+        mag = (8 + f) * 2.0 ** (e - 10) if e else f * 2.0 ** -9
+        return -mag if c & 0x80 else mag
+
+    sxv, swv = np.asarray(sx).reshape(-1), np.asarray(sw).reshape(-1)
+    y = [[sum(dec(xq[a, t]) * dec(wq[b, t]) for t in range(k)) * float(sxv[a]) * float(swv[b])
+          for b in range(2 * i)] for a in range(m)]
+    expect = np.array([[y[a][c] / (1.0 + math.exp(-y[a][c])) * y[a][c + i] for c in range(i)]
+                       for a in range(m)])
+    h = gemm.fp8_swiglu_reference(xq, sx, wq, sw)
+    assert np.allclose(h, expect, rtol=1e-12, atol=1e-14)
+    swapped = np.array([[y[a][c + i] / (1.0 + math.exp(-y[a][c + i])) * y[a][c] for c in range(i)]
+                        for a in range(m)])
+    assert not np.allclose(h, swapped, rtol=1e-3)
+    unscaled = gemm.fp8_swiglu_reference(xq, np.ones_like(sxv), wq, np.ones_like(swv))
+    assert not np.allclose(h, unscaled, rtol=1e-3)
+    assert np.allclose(gemm.fp8_swiglu_reference(xq, sx, wq, sw, channels=[1]), expect[:, [1]],
+                       rtol=1e-12, atol=1e-14)
+    with pytest.raises(ValueError):
+        gemm.fp8_swiglu_reference(xq, sx, wq[:5], sw[:5])
