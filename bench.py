@@ -418,6 +418,16 @@ def bench_gemms(qg, torch, dev, stream, cpu=None):
     out["fp8_gemm_8192"].update(act_quant_us=tq * 1e6,
                                 act_quant_gbs=(8192 * 8192 * 3 + 8192 * 4) / tq / 1e9,
                                 end_to_end_tflops=fl / (t + tq) / 1e12)
+    # the same operands read as [W_gate; W_up] of 4096 channels each: the
+    # SwiGLU epilogue writes SiLU(g) * u, [8192][4096], against the GEMM
+    # followed by torch's SiLU and product
+    h8 = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
+    th = timed(lambda: qg.qgemm_swiglu_fp8(xq, sx, wq, sw, out=h8), sample_s=0.05)
+    rh = rec(th, fl, "fp8", clocks_power=hw["last"])
+    tm = timed(lambda: torch.mul(torch.nn.functional.silu(y[:, :4096]), y[:, 4096:], out=h8))
+    rh["unfused_us"] = (t + tm) * 1e6
+    out["fp8_gemm_8192_swiglu"] = rh
+    del h8
     if cpu is not None:
         cpu["fp8_8192"] = cpu_fp8_sample(c, rows=1024)
     # fused RMSNorm / LayerNorm + per-token FP8 quantization of the same

@@ -258,6 +258,26 @@ qg_status qg_qgemm_swiglu(qg_format wfmt, qg_format afmt, const void* a, int64_t
                           int64_t N2, int64_t K, int64_t group, void* h, void* stream);
 
 /*
+ * qg_qgemm_swiglu_fp8 -- fused SwiGLU projection of FP8 W8A8 prefill:
+ * H = SiLU(G) * U with G, U the rescaled code products of qg_qgemm's FP8
+ * pair ([L6] figure 6-2: acc * s_x[m] * s_w[n]) over the gate and up rows of
+ * the concatenation [W_gate; W_up] ([SRV] section 4.6: the W8A8 GEMM with
+ * dequantization and activation fused, H written once).  Per output,
+ * g = acc_g * (s_x * s_g) and u = acc_u * (s_x * s_u) in fp32, then
+ * h = bf16(g / (1 + e^-g) * u), one rounding.
+ *   a, a_scales   FP8 E4M3 activation codes uint8 [M][K] and their per-token
+ *                 fp32 scales [M] (qg_quantize_pack, group == K).
+ *   wcodes, wscales   the per-row FP8 quantized [N2][K] concatenation: rows
+ *                 0 .. N2/2 - 1 gate, rows N2/2 .. N2 - 1 up; scales fp32 [N2].
+ *   h             bf16 [M][N2/2].
+ * Errors: QG_ERR_GEOMETRY (M, K < 1, K % 16, N2 odd or < 2), QG_ERR_NULL,
+ * QG_ERR_ALIGN, QG_ERR_UNSUPPORTED (an operand, padded by 256 rows, larger
+ * than 2 GiB - 4 KiB), QG_ERR_HIP.
+ */
+qg_status qg_qgemm_swiglu_fp8(const void* a, const void* a_scales, int64_t M, const void* wcodes,
+                              const void* wscales, int64_t N2, int64_t K, void* h, void* stream);
+
+/*
  * qg_channel_absmax -- per-channel statistics for calibration ([CH1]
  * section 4.3; [SRV] 1.5 per_channel_max): absmax[k] = max over rows of
  * |src[r][k]|, exact.

@@ -16,7 +16,8 @@ works without it, but every operation raises if it is missing.
 from .api import (dequant, mx_gemm, mx_quant, norm_quant, qgemm, qgemm_swiglu, qgemv,  # noqa: F401
                   quantize_pack, default_group, quantize_pack_smooth, channel_absmax,
                   smooth_scales, channel_scales, kv_cache_store, calib_stream_read, calib_mfma,
-                  CALIB_K, TiledCodes, tile_gemv_weights, qgemv_tiled, qgemv_swiglu)
+                  CALIB_K, TiledCodes, tile_gemv_weights, qgemv_tiled, qgemv_swiglu,
+                  qgemm_swiglu_fp8)
 from ._lib import LIB_PATH, QGError, load as load_library  # noqa: F401
 
 __all__ = ["quantize_pack", "dequant", "qgemv", "qgemm", "mx_quant", "mx_gemm", "norm_quant",

@@ -28,7 +28,7 @@ EXPORTS = [
     "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth", "qg_channel_absmax",
     "qg_smooth_scales", "qg_channel_scales", "qg_kv_cache_store", "qg_status_str",
     "qg_last_error", "qg_abi_version", "qg_calib_stream_read", "qg_calib_mfma",
-    "qg_tile_gemv_weights", "qg_qgemv_tiled", "qg_qgemv_swiglu",
+    "qg_tile_gemv_weights", "qg_qgemv_tiled", "qg_qgemv_swiglu", "qg_qgemm_swiglu_fp8",
 ]
 
 _lib = None
@@ -63,12 +63,14 @@ def load() -> ctypes.CDLL:
     lib.qg_tile_gemv_weights.argtypes = [vp, i64, i64, vp, vp]
     lib.qg_qgemv_tiled.argtypes = [i32, vp, i64, vp, vp, vp, i64, i64, i64, vp, vp]
     lib.qg_qgemv_swiglu.argtypes = [i32, vp, i64, vp, vp, vp, i64, i64, i64, i32, vp, vp]
+    lib.qg_qgemm_swiglu_fp8.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp]
     lib.qg_calib_mfma.argtypes = [i32, i64, i64, vp, vp]
     for name in ["qg_quantize_pack", "qg_dequant", "qg_qgemv", "qg_qgemm", "qg_mx_quant",
                  "qg_mx_gemm", "qg_norm_quant", "qg_qgemm_swiglu", "qg_quantize_pack_smooth",
                  "qg_channel_absmax", "qg_smooth_scales", "qg_channel_scales",
                  "qg_kv_cache_store", "qg_calib_stream_read", "qg_calib_mfma",
-                 "qg_tile_gemv_weights", "qg_qgemv_tiled", "qg_qgemv_swiglu"]:
+                 "qg_tile_gemv_weights", "qg_qgemv_tiled", "qg_qgemv_swiglu",
+                 "qg_qgemm_swiglu_fp8"]:
         getattr(lib, name).restype = i32
     lib.qg_status_str.argtypes = [i32]
     lib.qg_status_str.restype = ctypes.c_char_p

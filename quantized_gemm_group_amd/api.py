@@ -392,6 +392,33 @@ def qgemm_swiglu(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
     return h
 
 
+def qgemm_swiglu_fp8(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+                     w_scales: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fused SwiGLU projection of FP8 W8A8: h = SiLU(g) * u with g, u the
+    rescaled code products over the gate and up rows of the per-row FP8
+    quantized [2I][K] concatenation [W_gate; W_up]; a_codes uint8 [M][K]
+    with per-token scales.  Returns h bf16 [M][I]."""
+    dev = a_codes.device        # checked for the GPU below, after the shapes
+    if a_codes.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("codes must be [rows][K]")
+    m, k = a_codes.shape
+    n2 = w_codes.shape[0]
+    if n2 % 2:
+        raise ValueError("invalid quantization geometry: [W_gate; W_up] needs an even row count")
+    _expect(a_codes, (m, k), torch.uint8, "a_codes", dev)
+    _expect_rows(a_scales, m, "a_scales", dev)
+    _expect(w_codes, (n2, k), torch.uint8, "w_codes", dev)
+    _expect_rows(w_scales, n2, "w_scales", dev)
+    if out is not None:
+        _expect(out, (m, n2 // 2), torch.bfloat16, "out", dev)
+    _dev(a_codes)
+    lib = _lib.load()
+    h = torch.empty((m, n2 // 2), dtype=torch.bfloat16, device=dev) if out is None else out
+    _lib.check(lib.qg_qgemm_swiglu_fp8(_ptr(a_codes), _ptr(a_scales), m, _ptr(w_codes),
+                                       _ptr(w_scales), n2, k, _ptr(h), _stream(dev)))
+    return h
+
+
 def mx_quant(x: torch.Tensor):
     """OCP MXFP4 quantization of x [rows][K] along K.  Returns (codes uint8
     [rows][K/2], e8m0 uint8 [rows][K/32])."""

@@ -374,6 +374,25 @@ qg_status qg_qgemm_swiglu(qg_format wfmt, qg_format afmt, const void* a, int64_t
                                                N2, K, h, (hipStream_t)stream));
 }
 
+qg_status qg_qgemm_swiglu_fp8(const void* a, const void* a_scales, int64_t M, const void* wcodes,
+                              const void* wscales, int64_t N2, int64_t K, void* h, void* stream) {
+  if (M < 1 || N2 < 2 || K < 1 || N2 % 2 != 0)
+    return fail(QG_ERR_GEOMETRY, "qgemm_swiglu_fp8: M, K positive and N2 = 2 I even");
+  if (M > (int64_t)1 << 30 || N2 > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+    return fail(QG_ERR_GEOMETRY, "qgemm_swiglu_fp8: size out of range");
+  if (K % 16 != 0) return fail(QG_ERR_GEOMETRY, "qgemm_swiglu_fp8: K must be a multiple of 16");
+  qg_status st = check_quant_operand(QG_FP8_E4M3, N2, K, K, wcodes, wscales, nullptr);
+  if (st != QG_OK) return st;
+  st = check_quant_operand(QG_FP8_E4M3, M, K, K, a, a_scales, nullptr);
+  if (st != QG_OK) return st;
+  if (!h) return fail(QG_ERR_NULL, "qgemm_swiglu_fp8: h is required");
+  if (!aligned16(h)) return fail(QG_ERR_ALIGN, "qgemm_swiglu_fp8: h must be 16-byte aligned");
+  if (!fits_offsets(N2, K) || !fits_offsets(M, K))
+    return fail(QG_ERR_UNSUPPORTED, "qgemm_swiglu_fp8: operand larger than 2 GiB");
+  return from_hip(qg::launch_gemm_fp8_swiglu(a, a_scales, M, wcodes, wscales, N2, K, h,
+                                             (hipStream_t)stream));
+}
+
 qg_status qg_mx_quant(const void* src, qg_dtype src_dtype, int64_t rows, int64_t K, void* codes,
                       void* e8m0, void* stream) {
   if (src_dtype != QG_BF16 && src_dtype != QG_F32)

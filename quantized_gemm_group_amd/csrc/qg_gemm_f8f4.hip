@@ -96,7 +96,15 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // (K a multiple of 128); otherwise its 4 bytes are loaded one by one.
 // KFULL: K fills whole k-steps, so no load needs a K-tail check (loads past
 // the last k-step fill stages that are never read).
-template <bool MX, bool SALIGN, bool KFULL>
+// SWIGLU (FP8 only; 《推理优化与量化算子深度技术调研》 section 4.6, the W8A8 GEMM
+// with dequantization and activation fused): W is the [N][K] concatenation
+// [W_gate; W_up] (N = 2I) and a workgroup's 256 weight rows are 128 gate
+// channels and the same 128 up channels: wave w's 32 loaded rows are gate
+// (w even) or up (w odd) rows of channels c0 + 32 (w / 2) ..; so the W tiles
+// u = 0 and u = 1 of wave (wm, wn) hold gate and up of the same 32 channels
+// and each lane forms h = SiLU(s_x s_g g) * (s_x s_u u) of its own
+// accumulators.  Y is then h [M][I].
+template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false>
 __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
                                                              const void* __restrict__ a_aux, int M,
                                                              const uint8_t* __restrict__ W,
@@ -125,10 +133,14 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   const int wm = wave & 1, wn = wave >> 1;     // A rows 128 wm.., W rows 64 wn..
   const int l32 = lane & 31, lh = lane >> 5;
 
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  static_assert(!(SWIGLU && MX), "the SwiGLU epilogue is for the FP8 product");
+  const int I = N / 2;                          // SwiGLU: channels of h
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = SWIGLU ? (I + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   int tm, tn;
   xcd_tile(blockIdx.x, tiles_m, tiles_n, &tm, &tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const int c0 = tn * (BN / 2);                 // SwiGLU: first channel of the tile
 
   const int kbytes = MX ? K / 2 : K;           // bytes per operand row
   const int nk = (kbytes + BK - 1) / BK;
@@ -149,8 +161,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   for (int jp = 0; jp < 2; ++jp) {
     pchunk[jp] = (lane & 7) ^ (4 * jp + (lane >> 4));
     const int r = 32 * wave + (lane >> 3);
+    // SwiGLU: rows 32 w .. 32 w + 31 of the tile are the gate (w even) or
+    // up (w odd) rows of channels c0 + 32 (w / 2) + 0..31; gate rows past I
+    // read up rows and up rows past N read zero, both for channels that are
+    // never stored
+    const int wrow = SWIGLU ? (wave & 1) * I + c0 + 32 * (wave >> 1) + (lane >> 3) : n0 + r;
     voa[jp] = (uint32_t)(m0 + r) * kbytes + pchunk[jp] * 16;
-    vow[jp] = (uint32_t)(n0 + r) * kbytes + pchunk[jp] * 16;
+    vow[jp] = (uint32_t)wrow * kbytes + pchunk[jp] * 16;
   }
   // Exponent loads (MX): wave w brings the exponents of tile rows 64 w .. +63
   // (rows 0..255 of A, then 256..511 of W).  Grouped: lane l reads dword
@@ -396,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   if constexpr (!MX) {
     const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a_aux, (int64_t)M * 4);
     const __amdgpu_buffer_rsrc_t rsn = make_rsrc(w_aux, (int64_t)N * 4);
-    const bool edge_n = n0 + BN > N;
+    const bool edge_n = SWIGLU ? c0 + BN / 2 > I : n0 + BN > N;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       sxv[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -405,8 +422,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const uint32_t n = (uint32_t)(n0 + wn * 64 + u * 32 + 8 * b + 4 * lh);
-        if (!edge_n) {
+        const uint32_t n = SWIGLU ? (uint32_t)(u * I + c0 + wn * 32 + 8 * b + 4 * lh)
+                                  : (uint32_t)(n0 + wn * 64 + u * 32 + 8 * b + 4 * lh);
+        if (!edge_n && (!SWIGLU || (I & 3) == 0)) {
           swv[u][b] = __builtin_bit_cast(f32x4, buf_load16(rsn, n * 4, 0));
         } else {
 #pragma unroll
@@ -417,6 +435,48 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
       }
   }
   __syncthreads();   // every wave is done with the operand buffers
+  if constexpr (SWIGLU) {
+    // h = SiLU(g) * u per lane (fp32, e^-g from the hardware exponential),
+    // staged as the wave's 128 (m) x 32 (channel) bf16 piece with an 80-byte
+    // row pitch, then 16 rows per store instruction (4 lanes x 16 bytes)
+    constexpr int kHPitch = 80;
+    uint8_t* sh = smem + wave * (128 * kHPitch);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[0][t][4 * b + r] * (sxv[t] * swv[0][b][r]);
+          const float u = acc[1][t][4 * b + r] * (sxv[t] * swv[1][b][r]);
+          v[r] = g / (1.f + __expf(-g)) * u;
+        }
+        const int ml = t * 32 + l32, nl = 8 * b + 4 * lh;
+        *reinterpret_cast<uint2*>(sh + ml * kHPitch + nl * 2) =
+            make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
+      }
+    __syncthreads();
+    const int cbase = c0 + wn * 32 + (lane & 3) * 8;
+    const bool full_c = cbase + 7 < I && (I & 7) == 0;
+#pragma unroll 4
+    for (int i = 0; i < 8; ++i) {
+      const int ml = 16 * i + (lane >> 2);
+      const int m = m0 + wm * 128 + ml;
+      const u32x4 o = *reinterpret_cast<const u32x4*>(sh + ml * kHPitch + (lane & 3) * 16);
+      if (m < M) {
+        uint16_t* ph = Y + (int64_t)m * I + cbase;
+        if (full_c) {
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(ph));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (cbase + j < I) ph[j] = (uint16_t)(o[j >> 1] >> (16 * (j & 1)));
+        }
+      }
+    }
+    return;
+  }
   uint8_t* so = smem + wave * (128 * kEpiPitch);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -457,11 +517,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   }
 }
 
-template <bool MX, bool SALIGN, bool KFULL>
+template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false>
 hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, const void* w_aux,
                   int64_t N, int64_t K, void* y, hipStream_t stream) {
-  const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN, KFULL>), dim3(tiles), dim3(kThreads), 0, stream,
+  const int64_t tn = SWIGLU ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  const int tiles = (int)(((M + BM - 1) / BM) * tn);
+  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN, KFULL, SWIGLU>), dim3(tiles), dim3(kThreads), 0, stream,
                      (const uint8_t*)a, a_aux, (int)M, (const uint8_t*)w, w_aux, (int)N, (int)K,
                      (uint16_t*)y);
   return hipGetLastError();
@@ -474,6 +535,14 @@ hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const
                            hipStream_t stream) {
   if (K % BK == 0) return launch<false, true, true>(a, a_scales, M, w, w_scales, N, K, y, stream);
   return launch<false, true, false>(a, a_scales, M, w, w_scales, N, K, y, stream);
+}
+
+hipError_t launch_gemm_fp8_swiglu(const void* a, const void* a_scales, int64_t M, const void* w,
+                                  const void* w_scales, int64_t N2, int64_t K, void* h,
+                                  hipStream_t stream) {
+  if (K % BK == 0)
+    return launch<false, true, true, true>(a, a_scales, M, w, w_scales, N2, K, h, stream);
+  return launch<false, true, false, true>(a, a_scales, M, w, w_scales, N2, K, h, stream);
 }
 
 hipError_t launch_mx_gemm(const void* a_codes, const void* a_e8m0, int64_t M,

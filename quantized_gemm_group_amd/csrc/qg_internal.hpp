@@ -70,6 +70,12 @@ hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const
                            const void* w_scales, int64_t N, int64_t K, void* y,
                            hipStream_t stream);
 
+// FP8 W8A8 GEMM over [W_gate; W_up] (N2 = 2I rows) with the SwiGLU epilogue
+// into h [M][I].
+hipError_t launch_gemm_fp8_swiglu(const void* a, const void* a_scales, int64_t M, const void* w,
+                                  const void* w_scales, int64_t N2, int64_t K, void* h,
+                                  hipStream_t stream);
+
 hipError_t launch_gemm_int8(bool a_asym, bool w_asym, const void* a, const void* a_scales,
                             const void* a_zeros, int64_t M, const void* w, const void* w_scales,
                             const void* w_zeros, int64_t N, int64_t K, void* y,

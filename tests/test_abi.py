@@ -307,3 +307,15 @@ def test_qgemv_swiglu_validation(lib):
     assert f(i4, A16, 8, *ok[2:6], 16384, *ok[7:]) == _lib.ERR_UNSUPPORTED   # M > 4, K > 8192
     assert f(_lib.INT4_ASYM, *ok) == _lib.ERR_NULL
     assert f(i4, *ok[:9], MIS, None) == _lib.ERR_ALIGN
+
+
+def test_qgemm_swiglu_fp8_validation(lib):
+    f = lib.qg_qgemm_swiglu_fp8
+    ok = (A16, A16b, 8, A16c, A16d, 64, 256, A16e, None)
+    assert f(*ok[:5], 63, *ok[6:]) == _lib.ERR_GEOMETRY                 # odd N2
+    assert f(*ok[:6], 200, *ok[7:]) == _lib.ERR_GEOMETRY                # K % 16
+    assert f(A16, A16b, 0, *ok[3:]) == _lib.ERR_GEOMETRY
+    assert f(A16, None, *ok[2:]) == _lib.ERR_NULL
+    assert f(*ok[:7], None, None) == _lib.ERR_NULL
+    assert f(*ok[:7], MIS, None) == _lib.ERR_ALIGN
+    assert f(A16, A16b, 1 << 20, *ok[3:6], 8192, A16e, None) == _lib.ERR_UNSUPPORTED

@@ -154,3 +154,51 @@ def test_qgemv_swiglu_llama3_8b_gate_up_sampled(m):
     y = host(qg.qgemv_tiled(c["x"][:m].to(dev), tiled, scales, zeros, "int4_asym"))
     y = y.astype(np.float64)
     assert og.rel_fro(h, og.silu(y[:, :i]) * y[:, i:]) <= 4e-3
+
+
+# ------------------------------------------------------------ FP8 W8A8
+
+from oracle import fp8 as of8  # noqa: E402
+
+
+# ragged M, I (not a multiple of 4 or 8, a partial last 128-channel tile),
+# K with a partial last k-step (48, 176, 1040)
+@pytest.mark.parametrize("m,k,i", [(64, 256, 40), (130, 512, 200), (257, 1040, 129), (1, 128, 16),
+                                   (300, 2048, 384), (40, 48, 72), (100, 176, 97), (8, 64, 2)])
+def test_fp8_swiglu_small(m, k, i):
+    dev = device()
+    print(f"fp8 swiglu m={m} k={k} I={i}", flush=True)
+    c = small_case(m, k, 2 * i, seed=5 * m + i + k, x_outlier=(0.001, 100.0))
+    xq, sx, _ = qg.quantize_pack(to_dev(c["x"], dev), "fp8_e4m3")
+    wq, sw, _ = qg.quantize_pack(to_dev(c["w"], dev), "fp8_e4m3")
+    oxq, osx = of8.quantize_rows(bf16_as_f32(c["x"]))
+    owq, osw = of8.quantize_rows(c["w"])
+    assert (host(xq) == oxq).all() and (host(wq) == owq).all()
+    h = host(qg.qgemm_swiglu_fp8(xq, sx, wq, sw))
+    assert h.shape == (m, i)
+    _check_small(h, og.fp8_swiglu_reference(oxq, osx, owq, osw), "fp8 swiglu")
+
+
+def test_fp8_swiglu_8192_sampled():
+    # the FP8 workload's operands (M = K = 8192) read as [W_gate; W_up] of
+    # 4096 channels each; sampled channels against the oracle, and the whole
+    # output against the unfused path (the FP8 GEMM, then SiLU(g) * u)
+    dev = device()
+    c = workload_case("fp8_8192")
+    print("fp8 swiglu M=K=8192 I=4096", flush=True)
+    xq, sx, _ = qg.quantize_pack(to_dev(c["x"], dev), "fp8_e4m3")
+    wq, sw, _ = qg.quantize_pack(to_dev(c["w"], dev), "fp8_e4m3")
+    h = host(qg.qgemm_swiglu_fp8(xq, sx, wq, sw))
+    i = 4096
+    rm = np.unique(np.concatenate([np.arange(4), np.arange(8188, 8192),
+                                   rng_for(61).choice(8192, 40, replace=False)]))
+    ch = np.unique(np.concatenate([np.arange(8), np.arange(i - 8, i),
+                                   rng_for(62).choice(i, 56, replace=False)]))
+    rows = np.concatenate([ch, ch + i])
+    oxq, osx = of8.quantize_rows(bf16_as_f32(c["x"][rm]))
+    owq, osw = of8.quantize_rows(c["w"][rows])
+    assert (host(xq)[rm] == oxq).all() and (host(wq)[rows] == owq).all()
+    ref = og.fp8_swiglu_reference(oxq, osx, owq, osw)
+    check(h[np.ix_(rm, ch)], ref, "fp8 swiglu 8192")
+    y = host(qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx)).astype(np.float64)
+    assert og.rel_fro(h, og.silu(y[:, :i]) * y[:, i:]) <= 4e-3
