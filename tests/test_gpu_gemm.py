@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import quantized_gemm_group_amd as qg
-from oracle import fp8 as of8, gemm as og, intquant as oi, mx as omx
+from oracle import formats as of, fp8 as of8, gemm as og, intquant as oi, mx as omx
 from synthetic import (bf16_as_f32, rng_for, small_case, to_bf16, workload_case,
                        normal_activations, normal_weights, scale_input_channels,
                        scale_random_entries)
@@ -64,9 +64,14 @@ def test_fp8_gemm_small(m, k, n):
     check(y, og.fp8_reference(oxq, osx, owq, osw), "fp8")
 
 
-def _sample_rows(n, count, seed):
+def _sample_rows(n, count, seed, tile=256):
+    """Sampled output rows (or columns) of a full-size product: the first and
+    last 8, one at random inside every `tile`-wide block (so every 256 x 256
+    workgroup tile of the output, and with it every XCD and tile-order slot,
+    is looked at), and `count` more at random."""
     rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n),
+    per_tile = np.array([t + rng.integers(0, min(tile, n - t)) for t in range(0, n, tile)])
+    return np.unique(np.concatenate([np.arange(8), np.arange(n - 8, n), per_tile,
                                      rng.choice(n, count, replace=False)]))
 
 
@@ -77,7 +82,7 @@ def test_fp8_gemm_8192_sampled():
     xq, sx, _ = qg.quantize_pack(to_dev(c["x"], dev), "fp8_e4m3")
     wq, sw, _ = qg.quantize_pack(to_dev(c["w"], dev), "fp8_e4m3")
     y = host(qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx))
-    rm, rn = _sample_rows(8192, 80, 1), _sample_rows(8192, 80, 2)
+    rm, rn = _sample_rows(8192, 24, 1), _sample_rows(8192, 24, 2)
     oxq, osx = of8.quantize_rows(bf16_as_f32(c["x"][rm]))
     owq, osw = of8.quantize_rows(c["w"][rn])
     assert (host(xq)[rm] == oxq).all() and (host(sx)[rm, 0] == osx).all()
@@ -114,7 +119,7 @@ def test_mx_gemm_4096x8192_sampled():
     ac, ae = qg.mx_quant(to_dev(c["x"], dev))
     bc, be = qg.mx_quant(to_dev(c["w"], dev))
     y = host(qg.mx_gemm(ac, ae, bc, be))
-    rm, rn = _sample_rows(4096, 80, 3), _sample_rows(8192, 80, 4)
+    rm, rn = _sample_rows(4096, 24, 3), _sample_rows(8192, 24, 4)
     oac, oae = omx.quantize(bf16_as_f32(c["x"][rm]))
     obc, obe = omx.quantize(c["w"][rn])
     assert (host(ac)[rm] == oac).all() and (host(ae)[rm] == oae).all()
@@ -165,7 +170,7 @@ def test_int8_gemm_4096_sampled():
     aq, as_, az = qg.quantize_pack(to_dev(xb, dev), "int8_asym")
     wq, ws, _ = qg.quantize_pack(to_dev(w, dev), "int8_sym")
     y = host(qg.qgemm(aq, wq, ws, None, "int8_sym", "int8_asym", a_scales=as_, a_zeros=az))
-    rm, rn = _sample_rows(4096, 64, 5), _sample_rows(4096, 64, 6)
+    rm, rn = _sample_rows(4096, 24, 5), _sample_rows(4096, 24, 6)
     oaq, oas, oaz = _int8_oracle(bf16_as_f32(xb[rm]), "int8_asym")
     owq, ows, _ = _int8_oracle(w[rn], "int8_sym")
     assert (host(aq)[rm] == oaq).all() and (host(wq)[rn] == owq).all()
@@ -238,7 +243,7 @@ def test_w4a16_prefill_qwen72b_sampled(proj):
     print(f"w4a16 prefill {c['name']} M=2048 K={c['k']} N={c['n']}", flush=True)
     codes, scales, _ = qg.quantize_pack(to_dev(c["w"], dev), "int4_sym", 128)
     y = host(qg.qgemm(to_dev(c["x"], dev), codes, scales, None, "int4_sym", "bf16"))
-    rm, rn = _sample_rows(2048, 64, 7 + proj), _sample_rows(c["n"], 64, 9 + proj)
+    rm, rn = _sample_rows(2048, 24, 7 + proj), _sample_rows(c["n"], 24, 9 + proj)
     q, s = oi.quantize_sym(c["w"][rn], 128)
     packed = oi.pack_int4(q)
     assert (host(codes)[rn] == packed).all()
@@ -253,3 +258,122 @@ def test_qgemm_format_pair_errors():
     with pytest.raises(qg.QGError):
         qg.qgemm(a, a, torch.ones((4, 1), device=dev), None, "fp8_e4m3", "int8_sym",
                  a_scales=torch.ones((4, 1), device=dev))
+
+
+
+# ------------------------------------------------------- layout pins (one-hot)
+# Rows of A that are unit vectors e_k select one dequantized weight each:
+# y[m][n] = bf16(w_hat[n][k_m]) exactly (the products are exact and the sum
+# has one nonzero term), so any slip in the operand layout, the nibble or
+# byte order, the k mapping or the output placement shows up bit for bit.
+
+_ONE_HOT_K = 1024
+
+
+def _one_hot_positions(m, k, seed):
+    # group and block edges, every nibble position of a word, and random ones
+    fixed = [0, 1, 7, 8, 15, 16, 31, 32, 63, 64, 127, 128, 129, 255, 256, 511, 512, 1000, 1023]
+    rng = np.random.default_rng(seed)
+    return np.concatenate([fixed, rng.integers(0, k, m - len(fixed))]).astype(np.int64)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_w4a16_gemm_one_hot_is_bit_exact(asym):
+    dev = device()
+    m, k, n = 256, _ONE_HOT_K, 300
+    w = (rng_for(21).standard_normal((n, k), dtype=np.float32) * np.float32(0.02))
+    fmt = "int4_asym" if asym else "int4_sym"
+    codes, scales, zeros = qg.quantize_pack(to_dev(w, dev), fmt, 128)
+    if asym:
+        q, s, z = oi.quantize_asym(w, 128)
+    else:
+        (q, s), z = oi.quantize_sym(w, 128), None
+    ks = _one_hot_positions(m, k, 22)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), ks] = 1.0
+    y = host(qg.qgemm(to_dev(to_bf16(x), dev), codes, scales, zeros, fmt, "bf16"))
+    w_hat = oi.dequantize(oi.unpack_int4(oi.pack_int4(q), signed=not asym), s, z, 128, out="f32")
+    expect = of.round_to_bf16(w_hat[:, ks].T)
+    assert (y.view(np.uint32) == expect.view(np.uint32)).all()
+
+
+def test_fp8_gemm_one_hot_is_bit_exact():
+    # activation codes 0x38 (E4M3 1.0) at k_m with unit scales: the epilogue
+    # forms dec(w) * s_w in fp32 and rounds it once to bf16
+    dev = device()
+    m, k, n = 256, _ONE_HOT_K, 300
+    w = (rng_for(23).standard_normal((n, k), dtype=np.float32) * np.float32(0.02))
+    wq, sw = of8.quantize_rows(w)
+    ks = _one_hot_positions(m, k, 24)
+    xq = np.zeros((m, k), np.uint8)
+    xq[np.arange(m), ks] = 0x38
+    sx = np.ones(m, np.float32)
+    y = host(qg.qgemm(to_dev(xq, dev), to_dev(wq, dev), to_dev(np.asarray(sw, np.float32), dev),
+                      None, "fp8_e4m3", "fp8_e4m3", a_scales=to_dev(sx, dev)))
+    dec = of.decode(wq[:, ks].T, "e4m3").astype(np.float32)
+    expect = of.round_to_bf16(dec * np.asarray(sw, np.float32)[None, :])
+    # equal values (code 0x80 is -0; the matrix core's sum gives +0)
+    assert np.isfinite(y).all() and (y == expect).all()
+
+
+def test_mx_gemm_one_hot_is_bit_exact():
+    # A holds one E2M1 1.0 (code 2) at k_m with exponent byte 127 in every
+    # block: y[m][n] = bf16(e2m1(b[n][k_m]) * 2^(eb - 127)), exact
+    dev = device()
+    m, k, n = 256, _ONE_HOT_K, 300
+    w = rng_for(25).standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
+    w[:, 5] *= np.float32(50)
+    bc, be = omx.quantize(w)
+    ks = _one_hot_positions(m, k, 26)
+    nib = np.zeros((m, k), np.uint8)
+    nib[np.arange(m), ks] = 2
+    ac = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    ae = np.full((m, k // 32), 127, np.uint8)
+    y = host(qg.mx_gemm(to_dev(ac, dev), to_dev(ae, dev), to_dev(bc, dev), to_dev(be, dev)))
+    expect = of.round_to_bf16(omx.dequantize(bc, be)[:, ks].T.astype(np.float32))
+    # equal values: E2M1 code 8 is -0, and the matrix core's sum 0 + 1 * (-0)
+    # is +0; every nonzero output is compared bit for bit
+    assert np.isfinite(y).all() and (y == expect).all()
+
+
+def test_mx_gemm_on_edge_blocks():
+    # MX operands with zero, fp32-subnormal, 6 * 2^k-edge and tie blocks (the
+    # quantizer's edge matrix, with the huge block scaled to keep the
+    # products finite) through the GEMM; zero rows give exact zeros
+    from tests.test_gpu_quant import mx_edge_matrix
+    dev = device()
+    a = mx_edge_matrix(45, 2048, 5)
+    a[5, :32] = np.float32(3e30) * np.sign(a[5, :32] + 0.5)
+    w = mx_edge_matrix(70, 2048, 6)
+    w[5, :32] = np.float32(1e-20)
+    ac, ae = qg.mx_quant(to_dev(a, dev))
+    bc, be = qg.mx_quant(to_dev(w, dev))
+    oac, oae = omx.quantize(a)
+    obc, obe = omx.quantize(w)
+    assert (host(ac) == oac).all() and (host(ae) == oae).all()
+    assert (host(bc) == obc).all() and (host(be) == obe).all()
+    y = host(qg.mx_gemm(ac, ae, bc, be))
+    ref = og.mx_reference(oac, oae, obc, obe)
+    zero_rows = ~oac.any(axis=1)
+    assert (y[zero_rows] == 0).all()
+    check(y, ref, "mx edge blocks")
+
+
+def test_fp8_gemm_with_zero_rows():
+    # all-zero activation rows and weight rows take scale 1 (the zero-block
+    # rule) and all-zero codes; their outputs are exactly zero
+    dev = device()
+    w, x = fp8_case(130, 512, 200, seed=77)
+    x = bf16_as_f32(x)
+    x[[0, 17, 129]] = 0.0
+    w[[3, 199]] = 0.0
+    xq, sx, _ = qg.quantize_pack(to_dev(to_bf16(x), dev), "fp8_e4m3")
+    wq, sw, _ = qg.quantize_pack(to_dev(w, dev), "fp8_e4m3")
+    oxq, osx = of8.quantize_rows(x)
+    owq, osw = of8.quantize_rows(w)
+    assert (host(xq) == oxq).all() and (host(wq) == owq).all()
+    assert (host(sx).reshape(-1) == np.asarray(osx).reshape(-1)).all()
+    assert host(sx).reshape(-1)[0] == 1.0 and host(sw).reshape(-1)[3] == 1.0
+    y = host(qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx))
+    assert (y[[0, 17, 129]] == 0).all() and (y[:, [3, 199]] == 0).all()
+    check(y, og.fp8_reference(oxq, osx, owq, osw), "fp8 zero rows")

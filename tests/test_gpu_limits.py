@@ -103,6 +103,9 @@ def test_fp8_gemm_at_the_offset_limit():
     sw = torch.rand(n, device=dev, generator=g) * 0.01 + 0.001
     x = torch.from_numpy(rng_for(8).standard_normal((m, k), dtype=np.float32)).to(dev)
     xq, sx, _ = qg.quantize_pack(x, "fp8_e4m3")
+    from oracle import fp8 as of8
+    oxq, osx = of8.quantize_rows(host(x))
+    assert (host(xq) == oxq).all() and (host(sx).reshape(-1) == np.asarray(osx).reshape(-1)).all()
     y = host(qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx))
     assert y.shape == (m, n)
     finite_checks(y)
@@ -129,6 +132,9 @@ def test_mx_gemm_at_the_offset_limit():
     be = torch.randint(120, 131, (n, k // 32), dtype=torch.uint8, device=dev, generator=g)
     x = torch.from_numpy(rng_for(11).standard_normal((m, k), dtype=np.float32)).to(dev)
     ac, ae = qg.mx_quant(x)
+    from oracle import mx as omx
+    oac, oae = omx.quantize(host(x))
+    assert (host(ac) == oac).all() and (host(ae) == oae).all()
     y = host(qg.mx_gemm(ac, ae, bc, be))
     assert y.shape == (m, n)
     finite_checks(y)
