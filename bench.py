@@ -53,6 +53,12 @@ def parse():
     p.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                    help="print a markdown summary of a rocprofv3 kernel trace of a bench.py "
                         "run (per kernel and grid; the roofline kernel's timed replays) and exit")
+    p.add_argument("--gemm-counters", action="store_true",
+                   help="launch only the prefill GEMMs (FP8, MXFP4, W4A16 up/down) a few times, "
+                        "for rocprofv3 counter passes; prints one line")
+    p.add_argument("--counter-summary", nargs="+", metavar="COUNTER_CSV",
+                   help="print a markdown summary of rocprofv3 counter CSVs of --gemm-counters "
+                        "runs and exit")
     p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 counter-collection CSVs of --counters runs "
                         "(FETCH_SIZE, WRITE_SIZE) into profiles/hbm_traffic.json and exit")
@@ -833,6 +839,93 @@ def run_counters(reps=8):
                       "copy_bytes": COPY_BYTES}), flush=True)
 
 
+def run_gemm_counters(reps=3):
+    """Launches for rocprofv3 counter passes over the prefill GEMMs: FP8 W8A8
+    8192^3, MXFP4 4096x8192x8192 and the W4A16 Qwen2.5-72B FFN up and down
+    GEMMs, each `reps` times after one warm launch; prints one line."""
+    import torch
+    import quantized_gemm_group_amd as qg
+    from synthetic import workload_case
+    dev = torch.device("cuda:0")
+    c = workload_case("fp8_8192")
+    xq, sx, _ = qg.quantize_pack(c["x"].to(dev), "fp8_e4m3")
+    wq, sw, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "fp8_e4m3")
+    y = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+    for _ in range(reps + 1):
+        qg.qgemm(xq, wq, sw, None, "fp8_e4m3", "fp8_e4m3", a_scales=sx, out=y)
+    torch.cuda.synchronize()
+    del c, xq, sx, wq, sw, y
+    c = workload_case("mxfp4_4096x8192")
+    ac, ae = qg.mx_quant(c["x"].to(dev))
+    bc, be = qg.mx_quant(torch.from_numpy(c["w"]).to(dev))
+    y = torch.empty((4096, 8192), dtype=torch.bfloat16, device=dev)
+    for _ in range(reps + 1):
+        qg.mx_gemm(ac, ae, bc, be, out=y)
+    torch.cuda.synchronize()
+    del c, ac, ae, bc, be, y
+    for i in range(2):
+        c = workload_case("qwen72b_prefill", i)
+        x = c["x"].to(dev)
+        codes, s, _ = qg.quantize_pack(torch.from_numpy(c["w"]).to(dev), "int4_sym", 128)
+        y = torch.empty((2048, c["n"]), dtype=torch.bfloat16, device=dev)
+        for _ in range(reps + 1):
+            qg.qgemm(x, codes, s, None, "int4_sym", "bf16", out=y)
+        torch.cuda.synchronize()
+        del c, x, codes, s, y
+    print(json.dumps({"gemm_counters": ["fp8_8192", "mxfp4_4096x8192", "w4a16_qwen72b_up",
+                                        "w4a16_qwen72b_down"], "launches_each": reps + 1}),
+          flush=True)
+
+
+GEMM_COUNTER_KERNELS = [("gemm_f8f4_kernel<false", "FP8 W8A8 8192^3", 2 * 8192 ** 3),
+                        ("gemm_f8f4_kernel<true", "MXFP4 4096x8192x8192", 2 * 4096 * 8192 * 8192),
+                        ("gemm_w4a16_kernel", "W4A16 Qwen2.5-72B up / down", 2 * 2048 * 8192 * 29568)]
+
+
+def counter_summary(paths):
+    """Markdown summary of rocprofv3 counter CSVs of --gemm-counters runs: per
+    GEMM kernel (and launch grid) and counter, the mean per dispatch; with
+    SQ_BUSY_CU_CYCLES and SQ_VALU_MFMA_BUSY_CYCLES present, the effective
+    engine clock (busy CU cycles / 256 CUs / kernel duration) and the share
+    of cycles the matrix cores are busy (MFMA-busy cycles / 4 SIMDs / busy
+    CU cycles)."""
+    import statistics
+    groups = {}
+    for path in paths:
+        for r in _counter_rows(path):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            name = name.replace("void ", "")
+            key = (name, int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0))
+            d = groups.setdefault(key, {})
+            d.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+            if "Start_Timestamp" in r and r["Start_Timestamp"]:
+                d.setdefault("_dur_us", {})[r["Dispatch_Id"]] = (
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    lines = []
+    for (name, grid), d in sorted(groups.items()):
+        if not any(k in name for k, _, _ in GEMM_COUNTER_KERNELS):
+            continue
+        lines.append(f"### `{name}` (grid {grid})")
+        lines.append("")
+        lines.append("| counter | mean per dispatch | dispatches |")
+        lines.append("|---|---:|---:|")
+        for cn in sorted(k for k in d if not k.startswith("_")):
+            v = list(d[cn].values())
+            lines.append(f"| {cn} | {statistics.mean(v):.4g} | {len(v)} |")
+        busy = d.get("SQ_BUSY_CU_CYCLES")
+        mfma = d.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        dur = d.get("_dur_us")
+        if busy and mfma:
+            b = statistics.mean(busy.values())
+            lines.append(f"| MFMA busy share (MFMA-busy / 4 / busy CU cycles) | "
+                         f"{statistics.mean(mfma.values()) / 4 / b:.3f} | |")
+            if dur:
+                lines.append(f"| effective clock (busy CU cycles / 256 / duration), GHz | "
+                             f"{b / 256 / statistics.mean(dur.values()) / 1e3:.3f} | |")
+        lines.append("")
+    print("\n".join(lines))
+
+
 def _counter_rows(path):
     import csv
     with open(path) as f:
@@ -921,6 +1014,9 @@ def main():
     if args.trace_summary:
         trace_summary(args.trace_summary)
         return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.traffic:
         write_traffic(*args.traffic)
         return
@@ -936,6 +1032,9 @@ def main():
     qg.load_library()
     if args.counters:
         run_counters()
+        return
+    if args.gemm_counters:
+        run_gemm_counters()
         return
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(dev)
