@@ -147,11 +147,14 @@ qg_status qg_dequant(qg_format fmt, const void* codes, const void* scales, const
  *   wfmt       QG_INT4_SYM (wzeros NULL) or QG_INT4_ASYM.
  *   x          bf16 [M][K];  wcodes int32 [N][K/8];  wscales/wzeros fp16
  *              [N][K/group];  y bf16 [M][N].
- *   group      must be 128 (QG_ERR_UNSUPPORTED otherwise); K % 128 == 0.
+ *   group      128 (the tuned kernels), or 32, 64 or a multiple of 128
+ *              dividing K ([CH1] section 4.1: per-group granularity from 32
+ *              to 128) on a general kernel that flushes each group's
+ *              partial sum with its own scale; K % 128 == 0 in every case.
  * Errors: QG_ERR_GEOMETRY (M outside 1..16, N < 1, K not a multiple of
- * group), QG_ERR_UNSUPPORTED (group != 128, K > 65536, or codes / x padded
- * by 256 rows larger than 2 GiB - 4 KiB), QG_ERR_FORMAT, QG_ERR_NULL,
- * QG_ERR_ALIGN, QG_ERR_HIP.
+ * group), QG_ERR_UNSUPPORTED (another group size, K > 65536, or codes / x
+ * padded by 256 rows larger than 2 GiB - 4 KiB), QG_ERR_FORMAT,
+ * QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_HIP.
  */
 qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
                    const void* wcodes, const void* wscales, const void* wzeros,
@@ -218,7 +221,9 @@ qg_status qg_qgemv_swiglu(qg_format wfmt, const void* x, int64_t M, const void* 
  * qg_qgemm -- quantized GEMM Y = dequant(A) * dequant(W)^T, fp32
  * accumulation, bf16 output (round to nearest even).  Format pairs:
  *   W INT4_SYM|INT4_ASYM, A BF16_ACT : W4A16 prefill ([SRV] 1.3; [L6] sec. 2);
- *       a = bf16 [M][K], a_scales/a_zeros NULL, group must be 128.
+ *       a = bf16 [M][K], a_scales/a_zeros NULL; group 128 (the MFMA prefill
+ *       kernel), or 32, 64 or a multiple of 128 dividing K (the general
+ *       kernel of qg_qgemv, over blocks of 16 rows; M <= 1048560).
  *   W FP8_E4M3, A FP8_E4M3 : FP8 W8A8 ([L6] figure 6-2: the product of the
  *       codes is rescaled by s_x[m] * s_w[n]); per-row scales only
  *       (group == K): a_scales fp32 [M], wscales fp32 [N].

@@ -74,12 +74,17 @@ qg_status qgemv_common(bool tiled, qg_format wfmt, const void* x, int64_t M, con
   if (N < 1 || N > (int64_t)1 << 30) return fail(QG_ERR_GEOMETRY, "qgemv: N out of range");
   qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
   if (st != QG_OK) return st;
-  if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemv: only group 128 is implemented");
+  if (group != 128 && !qg::w4a16_group_supported(K, group))
+    return fail(QG_ERR_UNSUPPORTED, "qgemv: groups of 32, 64 or a multiple of 128 (K a "
+                                    "multiple of 128) are implemented");
   if (K > 65536) return fail(QG_ERR_UNSUPPORTED, "qgemv: K above 65536 is not implemented");
   if (!fits_offsets(N, K / 2) || !fits_offsets(M, K * 2))
     return fail(QG_ERR_UNSUPPORTED, "qgemv: operand larger than 2 GiB");
   if (!x || !y) return fail(QG_ERR_NULL, "qgemv: x and y are required");
   if (!aligned16(x) || !aligned16(y)) return fail(QG_ERR_ALIGN, "qgemv: x, y must be 16-byte aligned");
+  if (group != 128)
+    return from_hip(qg::launch_w4a16_groups(wfmt == QG_INT4_ASYM, tiled, x, M, wcodes, wscales,
+                                            wzeros, N, K, group, y, (hipStream_t)stream));
   return from_hip(qg::launch_qgemv(wfmt == QG_INT4_ASYM, tiled, x, M, wcodes, wscales, wzeros, N,
                                    K, y, (hipStream_t)stream));
 }
@@ -326,8 +331,15 @@ qg_status qg_qgemm(qg_format wfmt, qg_format afmt, const void* a, const void* a_
   if (is_int4(wfmt) && afmt == QG_BF16_ACT) {
     qg_status st = check_quant_operand(wfmt, N, K, group, wcodes, wscales, wzeros);
     if (st != QG_OK) return st;
-    if (group != 128) return fail(QG_ERR_UNSUPPORTED, "qgemm W4A16: only group 128 is implemented");
+    if (group != 128 && !qg::w4a16_group_supported(K, group))
+      return fail(QG_ERR_UNSUPPORTED, "qgemm W4A16: groups of 32, 64 or a multiple of 128 (K a "
+                                      "multiple of 128) are implemented");
     if (a_scales || a_zeros) return fail(QG_ERR_NULL, "qgemm W4A16: a_scales/a_zeros must be NULL");
+    if (group != 128 && M > 16 * 65535)
+      return fail(QG_ERR_UNSUPPORTED, "qgemm W4A16: M above 1048560 with a group other than 128");
+    if (group != 128)
+      return from_hip(qg::launch_w4a16_groups(wfmt == QG_INT4_ASYM, false, a, M, wcodes, wscales,
+                                              wzeros, N, K, group, y, s));
     return from_hip(qg::launch_gemm_w4a16(wfmt == QG_INT4_ASYM, a, M, wcodes, wscales, wzeros, N,
                                           K, y, s));
   }

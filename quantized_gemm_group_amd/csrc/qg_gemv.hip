@@ -1075,6 +1075,140 @@ int pick_wave_ng(int M, int N, int K) {
   return 0;
 }
 
+// W4A16 product for quantization groups other than 128 codes: g = 32, 64 or
+// a multiple of 128 dividing K (《第 1 章：推理加速全景》 section 4.1: per-group
+// granularity from 32 to 128 elements).  The codes are unpacked in natural k
+// order (the 4 x 4 transpose of the 16-row kernel), so MFMA i of a 128-code
+// block covers k = 32 i .. 32 i + 31: a group of 32 is one MFMA, a group of
+// 64 two, a group of 128 t the 4 t MFMAs of t blocks; each group is flushed
+// as y += s (acc - c sum_x) with its own scale and zero point.  Workgroup =
+// one 16-channel tile x one block of up to 16 rows of x (blockIdx.y), KS
+// waves over K-slices of NB blocks of 128 codes; the x pieces come straight
+// from the caches, the weights one block ahead.  Any M (the prefill GEMM's
+// fallback for these group sizes as well as the GEMV's).  Either code layout.
+template <bool ASYM, int GPB, bool TILED>   // groups per 128-code block: 4, 2 or 1
+__global__ __launch_bounds__(1024) void qgemv_groups_kernel(const uint16_t* __restrict__ x, int M,
+                                                            const uint32_t* __restrict__ w,
+                                                            const uint16_t* __restrict__ s16,
+                                                            const uint16_t* __restrict__ z16,
+                                                            int N, int K, int gsize, int KS,
+                                                            int NB, uint16_t* __restrict__ y,
+                                                            uint32_t mask, uint32_t cmag) {
+  extern __shared__ float4 lds4[];
+  float* red = reinterpret_cast<float*>(lds4);
+  const int lane = threadIdx.x & 63;
+  const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int n = blockIdx.x * 16 + li;
+  const int m0 = blockIdx.y * 16;
+  const int G128 = K / kGroup;
+  const int Gs = K / gsize;                      // scale groups per row
+  const int b0 = kw * NB;
+  const int b1 = b0 + NB < G128 ? b0 + NB : G128;
+  using WL = WLayout<TILED>;
+  // rows m0 + li >= M and channels n >= N read as zero (outside the ranges)
+  const int mrows = M - m0 < 16 ? M - m0 : 16;
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x + (int64_t)m0 * K, (int64_t)mrows * K * 2);
+  const uint32_t xoff = li < mrows ? (uint32_t)(li * K + 8 * lg) * 2 : 0x80000000u;
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N, K));
+  const uint32_t woff = WL::lane_off(blockIdx.x, li, lg, N, K);
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * Gs * 2);
+  const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * Gs * 2 : 0);
+  const uint32_t srow = n < N ? (uint32_t)n * (uint32_t)Gs * 2u : 0x80000000u;
+
+  struct Block {
+    u32x4 wv, xv[4];
+    uint32_t sv[GPB], zv[GPB];
+  };
+  auto load = [&](int b, Block& B) {
+    const bool ok = b < b1;
+    B.wv = WL::load(wres, ok ? woff : 0x80000000u, b * WL::kGroupStride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) B.xv[i] = bload(xres, ok ? xoff : 0x80000000u, b * 256 + i * 64);
+#pragma unroll
+    for (int h = 0; h < GPB; ++h) {
+      const int gi = GPB == 1 ? (int)((int64_t)b * kGroup / gsize) : b * GPB + h;
+      const uint32_t so = ok && srow != 0x80000000u ? srow + (uint32_t)gi * 2u : 0x80000000u;
+      B.sv[h] = __builtin_amdgcn_raw_buffer_load_b16(sres, so, 0, 0);
+      B.zv[h] = ASYM ? __builtin_amdgcn_raw_buffer_load_b16(zres, so, 0, 0) : 0u;
+    }
+  };
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+  Block cur, nxt;
+  load(b0, cur);
+  for (int b = b0; b < b1; ++b) {
+    load(b + 1, nxt);
+    const u32x4 wt = transpose_rows(cur.wv);
+    f32x4 acc[4], sacc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 a = as_bf16x8(cur.xv[i]);
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(unpack_word_nat(wt[i], mask, cmag)),
+                                                       z4, 0, 0, 0);
+      sacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(ones), z4, 0, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < GPB; ++h) {
+      const float sc = f16_bits_to_f32((uint16_t)cur.sv[h]);
+      const float cc = ASYM ? 128.f + f16_bits_to_f32((uint16_t)cur.zv[h]) : 136.f;
+      constexpr int kPer = 4 / GPB;              // MFMAs of one group inside the block
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = 0.f, sx = 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          a += acc[h * kPer + i][r];
+          sx += sacc[h * kPer + i][r];
+        }
+        yacc[r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sx, a), yacc[r]);
+      }
+    }
+    cur = nxt;
+  }
+
+  // sum the K-slices: red[kw][r][lane]; lane (li, lg) of the first wave
+  // writes y[m0 + 4 lg + r][n]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(kw * 4 + r) * 64 + lane] = yacc[r];
+  __syncthreads();
+  if (kw == 0 && n < N) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 4 * lg + r;
+      if (m < M) {
+        float v = 0.f;
+        for (int k2 = 0; k2 < KS; ++k2) v += red[(k2 * 4 + r) * 64 + lane];
+        y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+      }
+    }
+  }
+}
+
+template <bool TILED>
+hipError_t launch_groups_t(bool asym, const void* x, int M, const void* w, const void* s,
+                           const void* z, int N, int K, int gsize, void* y, hipStream_t stream) {
+  const int G128 = K / kGroup;
+  const int nb = (G128 + 7) / 8;                 // at most 8 K-slices
+  const int ks = (G128 + nb - 1) / nb;
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16));
+  const size_t lds = (size_t)ks * 4 * 64 * sizeof(float);
+  const int gpb = gsize == 32 ? 4 : (gsize == 64 ? 2 : 1);
+  const uint32_t mask = 0x000F000Fu, cmag = asym ? 0x43004300u : 0x43084308u;
+#define QG_GROUPS(A, GP)                                                                          \
+  hipLaunchKernelGGL((qgemv_groups_kernel<A, GP, TILED>), grid, dim3(64 * ks), lds, stream,         \
+                     (const uint16_t*)x, M, (const uint32_t*)w, (const uint16_t*)s,                  \
+                     (const uint16_t*)z, N, K, gsize, ks, nb, (uint16_t*)y, mask, cmag)
+  if (asym) {
+    if (gpb == 4) QG_GROUPS(true, 4); else if (gpb == 2) QG_GROUPS(true, 2); else QG_GROUPS(true, 1);
+  } else {
+    if (gpb == 4) QG_GROUPS(false, 4); else if (gpb == 2) QG_GROUPS(false, 2); else QG_GROUPS(false, 1);
+  }
+#undef QG_GROUPS
+  return hipGetLastError();
+}
+
 // Groups per wave of the SwiGLU wave kernel (0: not applicable): the
 // per-wave GEMV's choice with at most 16 K-slices and the LDS within 160
 // KiB; two weight tiles per wave, so 4 groups (8 for M = 1 when K needs
@@ -1219,6 +1353,20 @@ hipError_t launch_qgemv(bool asym, bool tiled, const void* x, int64_t M, const v
                         hipStream_t stream) {
   return tiled ? launch_qgemv_t<true>(asym, x, M, wcodes, wscales, wzeros, N, K, y, stream)
                : launch_qgemv_t<false>(asym, x, M, wcodes, wscales, wzeros, N, K, y, stream);
+}
+
+bool w4a16_group_supported(int64_t K, int64_t group) {
+  if (group <= 0 || K % group != 0 || K % kGroup != 0) return false;
+  return group == 32 || group == 64 || group % kGroup == 0;
+}
+
+hipError_t launch_w4a16_groups(bool asym, bool tiled, const void* x, int64_t M,
+                               const void* wcodes, const void* wscales, const void* wzeros,
+                               int64_t N, int64_t K, int64_t group, void* y, hipStream_t stream) {
+  return tiled ? launch_groups_t<true>(asym, x, (int)M, wcodes, wscales, wzeros, (int)N, (int)K,
+                                       (int)group, y, stream)
+               : launch_groups_t<false>(asym, x, (int)M, wcodes, wscales, wzeros, (int)N, (int)K,
+                                        (int)group, y, stream);
 }
 
 bool qgemv_swiglu_supported(int64_t M, int64_t K) {

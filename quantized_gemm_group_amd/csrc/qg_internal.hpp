@@ -48,6 +48,13 @@ hipError_t launch_qgemv(bool asym, bool tiled, const void* x, int64_t M, const v
                         const void* wscales, const void* wzeros, int64_t N, int64_t K, void* y,
                         hipStream_t stream);
 
+// W4A16 product for group sizes other than 128 (32, 64 or a multiple of 128
+// dividing K, K a multiple of 128), any M, canonical or tiled codes.
+bool w4a16_group_supported(int64_t K, int64_t group);
+hipError_t launch_w4a16_groups(bool asym, bool tiled, const void* x, int64_t M,
+                               const void* wcodes, const void* wscales, const void* wzeros,
+                               int64_t N, int64_t K, int64_t group, void* y, hipStream_t stream);
+
 // SwiGLU decode GEMV over [W_gate; W_up] (N2 = 2I rows) into h [M][I];
 // qgemv_swiglu_supported tells which (M, K) the kernels cover.
 bool qgemv_swiglu_supported(int64_t M, int64_t K);

@@ -71,7 +71,9 @@ def test_qgemv_validation(lib):
     assert g(_lib.INT4_SYM, A16, 17, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
     assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 0, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
     assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 200, 128, A16e, None) == _lib.ERR_GEOMETRY
-    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 256, 64, A16e, None) == _lib.ERR_UNSUPPORTED
+    # groups of 32, 64 and multiples of 128 are implemented; 96 is not
+    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 384, 96, A16e, None) == _lib.ERR_UNSUPPORTED
+    assert g(_lib.INT4_SYM, A16, 1, A16b, A16c, None, 16, 96, 32, A16e, None) == _lib.ERR_UNSUPPORTED
     assert g(_lib.INT8_SYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_FORMAT
     assert g(_lib.INT4_ASYM, A16, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_NULL
     assert g(_lib.INT4_SYM, MIS, 1, A16b, A16c, None, 16, 256, 128, A16e, None) == _lib.ERR_ALIGN
@@ -83,7 +85,7 @@ def test_qgemm_validation(lib):
     i4, bf, f8, i8 = _lib.INT4_SYM, _lib.BF16_ACT, _lib.FP8_E4M3, _lib.INT8_SYM
     assert g(i4, f8, A16, None, None, 8, A16b, A16c, None, 8, 256, 128, A16e, None) == _lib.ERR_FORMAT
     assert g(i4, bf, A16, None, None, 0, A16b, A16c, None, 8, 256, 128, A16e, None) == _lib.ERR_GEOMETRY
-    assert g(i4, bf, A16, None, None, 8, A16b, A16c, None, 8, 256, 64, A16e, None) == _lib.ERR_UNSUPPORTED
+    assert g(i4, bf, A16, None, None, 8, A16b, A16c, None, 8, 384, 96, A16e, None) == _lib.ERR_UNSUPPORTED
     assert g(f8, f8, A16, A16d, None, 8, A16b, A16c, None, 8, 256, 128, A16e, None) == _lib.ERR_UNSUPPORTED
     assert g(f8, f8, A16, None, None, 8, A16b, A16c, None, 8, 256, 256, A16e, None) == _lib.ERR_NULL
     assert g(i8, _lib.INT8_ASYM, A16, A16d, None, 8, A16b, A16c, None, 8, 256, 256, A16e,

@@ -236,6 +236,26 @@ def test_w4a16_gemm_small(m, k, n, asym):
     check(y, og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, 128), f"w4a16 {fmt}")
 
 
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("group", [32, 64, 256])
+@pytest.mark.parametrize("m,k,n", [(130, 1024, 200), (33, 2048, 72)])
+def test_w4a16_gemm_other_group_sizes(m, k, n, group, asym):
+    # groups other than 128 (《第 1 章：推理加速全景》 section 4.1 granularity)
+    dev = device()
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"w4a16 gemm group={group} m={m} k={k} n={n} {fmt}", flush=True)
+    c = small_case(m, k, n, seed=group + 3 * m + n, w_outlier=(0.01, 20.0))
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, group)
+    if asym:
+        q, s, z = oi.quantize_asym(c["w"], group)
+    else:
+        (q, s), z = oi.quantize_sym(c["w"], group), None
+    packed = oi.pack_int4(q)
+    assert (host(codes) == packed).all()
+    y = host(qg.qgemm(to_dev(c["x"], dev), codes, scales, zeros, fmt, "bf16", group=group))
+    check(y, og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, group), f"w4a16 g{group}")
+
+
 @pytest.mark.parametrize("proj", [0, 1])
 def test_w4a16_prefill_qwen72b_sampled(proj):
     dev = device()

@@ -149,3 +149,55 @@ def test_qgemv_llama3_8b_decode_sampled(proj):
         ref = og.w4a16_reference(xs[:m], packed, s, z, 128)
         err = og.rel_fro(y[:, rows], ref)
         assert err <= TOL, f"M={m} rel_fro {err}"
+
+
+
+# ------------------------------------------------ group sizes other than 128
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("group", [32, 64, 256, 1024])
+@pytest.mark.parametrize("m,k,n", [(1, 1024, 100), (4, 2048, 37), (16, 4096, 64), (7, 1024, 300)])
+def test_qgemv_other_group_sizes(m, k, n, group, asym):
+    # 《第 1 章：推理加速全景》 section 4.1: per-group granularity from 32 to 128
+    # (and coarser); the codes, scales and zero points of quantize_pack with
+    # the group, the GEMV on canonical and tiled codes against the oracle
+    dev = device()
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"qgemv group={group} m={m} k={k} n={n} {fmt}", flush=True)
+    c = small_case(m, k, n, seed=group + m + n, w_outlier=(0.01, 20.0))
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, group)
+    if asym:
+        q, s, z = oi.quantize_asym(c["w"], group, "int4_asym")
+    else:
+        (q, s), z = oi.quantize_sym(c["w"], group, "int4_sym"), None
+    packed = oi.pack_int4(q)
+    assert (host(codes) == packed).all()
+    assert (host(scales).view(np.uint16) == s.view(np.uint16)).all()
+    x = to_dev(c["x"], dev)
+    y = host(qg.qgemv(x, codes, scales, zeros, fmt, group=group))
+    yt = host(qg.qgemv_tiled(x, qg.tile_gemv_weights(codes), scales, zeros, fmt, group=group))
+    assert (yt.view(np.uint32) == y.view(np.uint32)).all()
+    ref = og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, group)
+    finite_checks(y)
+    if y.size < 1024:
+        floor = 1e-3 * np.sqrt(np.mean(ref ** 2))
+        assert (np.abs(y - ref) <= 2.0 ** -8 * np.abs(ref) + floor).all()
+    else:
+        assert og.rel_fro(y, ref) <= TOL
+
+
+def test_group_32_one_hot_is_bit_exact():
+    # the natural-order unpack of the other-group kernel: x rows e_k select
+    # one dequantized weight (groups of 32, asymmetric)
+    dev = device()
+    k, n = 512, 48
+    w = (rng_for(19).standard_normal((n, k), dtype=np.float32) * np.float32(0.02))
+    codes, scales, zeros = qg.quantize_pack(to_dev(w, dev), "int4_asym", 32)
+    q, s, z = oi.quantize_asym(w, 32, "int4_asym")
+    ks = [0, 1, 7, 8, 31, 32, 33, 63, 64, 100, 127, 128, 200, 300, 450, 511]
+    x = np.zeros((16, k), np.float32)
+    x[np.arange(16), ks] = 1.0
+    y = host(qg.qgemv(to_dev(to_bf16(x), dev), codes, scales, zeros, "int4_asym", group=32))
+    w_hat = oi.dequantize(oi.unpack_int4(oi.pack_int4(q), signed=False), s, z, 32, out="f32")
+    expect = of.round_to_bf16(w_hat[:, ks].T)
+    assert (y == expect).all()
