@@ -469,6 +469,27 @@ qg_status qg_calib_stream_read(const void* src, int64_t bytes, uint32_t* sink, v
 qg_status qg_calib_mfma(qg_calib_kind kind, int64_t waves, int64_t iters, float* sink,
                         void* stream);
 
+/*
+ * Debug outputs (a localisation aid, not part of the method): the debug
+ * library libqgemm_debug.so is the same source built with QG_DEBUG_FP32.  In
+ * it, every kernel that rounds an output to bf16 (the GEMV, GEMM and SwiGLU
+ * entry points) also stores the fp32 value it rounds, at the same index of
+ * an fp32 buffer shaped like that output ([M][N], or [M][I] for SwiGLU), so
+ * a parity failure can be told apart from the final rounding.
+ *
+ * qg_debug_fp32_output -- set (out != NULL) or clear (out == NULL) that
+ * buffer for every later launch, process-wide (library state; not for
+ * concurrent use).  The caller sizes the buffer for the next call's output.
+ *   out        fp32, 4-byte aligned, or NULL.
+ * Errors: QG_ERR_UNSUPPORTED in the product library, QG_ERR_ALIGN,
+ * QG_ERR_HIP.
+ *
+ * qg_debug_build -- 1 in the debug library, 0 in the product library.
+ */
+qg_status qg_debug_fp32_output(float* out, void* stream);
+
+int qg_debug_build(void);
+
 /* Human-readable name of a status code (static storage). */
 const char* qg_status_str(qg_status status);
 

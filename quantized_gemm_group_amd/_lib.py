@@ -29,21 +29,40 @@ EXPORTS = [
     "qg_smooth_scales", "qg_channel_scales", "qg_kv_cache_store", "qg_status_str",
     "qg_last_error", "qg_abi_version", "qg_calib_stream_read", "qg_calib_mfma",
     "qg_tile_gemv_weights", "qg_qgemv_tiled", "qg_qgemv_swiglu", "qg_qgemm_swiglu_fp8",
+    "qg_debug_fp32_output", "qg_debug_build",
 ]
 
 _lib = None
 
 
+LIB_DEBUG_PATH = os.path.join(HERE, "libqgemm_debug.so")
+_lib_debug = None
+
+
 def load() -> ctypes.CDLL:
     """Load libqgemm.so (once) and declare its prototypes."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def load_debug() -> ctypes.CDLL:
+    """Load the debug library libqgemm_debug.so (once): the same entry points,
+    plus fp32 output recording (qg_debug_fp32_output).  For tests and bug
+    hunts; the binding in api.py always uses the product library."""
+    global _lib_debug
+    if _lib_debug is None:
+        _lib_debug = _open(LIB_DEBUG_PATH)
+    return _lib_debug
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build it with `python -m quantized_gemm_group_amd.build` "
+            f"{path} is missing: build it with `python -m quantized_gemm_group_amd.build` "
             "(the HIP library is the only implementation)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.qg_quantize_pack.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp]
     lib.qg_dequant.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i32, vp]
@@ -78,7 +97,10 @@ def load() -> ctypes.CDLL:
     lib.qg_last_error.restype = ctypes.c_char_p
     lib.qg_abi_version.argtypes = []
     lib.qg_abi_version.restype = i32
-    _lib = lib
+    lib.qg_debug_fp32_output.argtypes = [vp, vp]
+    lib.qg_debug_fp32_output.restype = i32
+    lib.qg_debug_build.argtypes = []
+    lib.qg_debug_build.restype = i32
     return lib
 
 

@@ -1,8 +1,10 @@
 """Build the HIP library libqgemm.so in-tree for gfx950.
 
 Each translation unit under csrc/ is compiled with hipcc in parallel, then
-linked into quantized_gemm_group_amd/libqgemm.so.  Run as a script or call
-``build()``; it always recompiles.
+linked into quantized_gemm_group_amd/libqgemm.so; the same sources built
+with QG_DEBUG_FP32 give libqgemm_debug.so (fp32 outputs before the bf16
+rounding recorded on request).  Run as a script or call ``build()``; it
+always recompiles.
 """
 
 from __future__ import annotations
@@ -33,29 +35,44 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+LIB_DEBUG = os.path.join(HERE, "libqgemm_debug.so")
+
+
+def _compile(job) -> str:
+    src, debug = job
+    odir = OBJ + ("_debug" if debug else "")
+    obj = os.path.join(odir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(["-DQG_DEBUG_FP32"] if debug else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Build libqgemm.so (the product) and libqgemm_debug.so (the same
+    sources with QG_DEBUG_FP32: kernels also record their fp32 outputs
+    before the bf16 rounding)."""
+    os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(OBJ + "_debug", exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = [(s, False) for s in srcs] + [(s, True) for s in srcs]
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], LIB_DEBUG)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} and {LIB_DEBUG} from {len(srcs)} sources")
     return LIB
 
 

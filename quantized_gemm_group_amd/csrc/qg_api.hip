@@ -455,4 +455,28 @@ qg_status qg_calib_mfma(qg_calib_kind kind, int64_t waves, int64_t iters, float*
   return from_hip(qg::launch_calib_mfma((int)kind, waves, iters, sink, (hipStream_t)stream));
 }
 
+qg_status qg_debug_fp32_output(float* out, void* stream) {
+  (void)stream;
+#ifdef QG_DEBUG_FP32
+  if (out && !aligned_to(out, 4)) return fail(QG_ERR_ALIGN, "debug_fp32_output: 4-byte aligned");
+  hipError_t e = qg::debug_set_gemv(out);
+  if (e == hipSuccess) e = qg::debug_set_f8f4(out);
+  if (e == hipSuccess) e = qg::debug_set_int8(out);
+  if (e == hipSuccess) e = qg::debug_set_w4a16(out);
+  return from_hip(e);
+#else
+  (void)out;
+  return fail(QG_ERR_UNSUPPORTED, "debug_fp32_output: this library was built without "
+                                  "QG_DEBUG_FP32 (use libqgemm_debug.so)");
+#endif
+}
+
+int qg_debug_build(void) {
+#ifdef QG_DEBUG_FP32
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 }  // extern "C"

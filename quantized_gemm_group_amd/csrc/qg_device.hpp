@@ -86,6 +86,32 @@ __device__ __forceinline__ int mx_shared_exponent(float m) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// ------------------------------------------------------------ debug outputs
+
+// Built with QG_DEBUG_FP32 (the debug library libqgemm_debug.so): every
+// kernel that rounds a product to bf16 also stores the fp32 value it rounds,
+// at the same index of an fp32 buffer shaped like the output, when
+// qg_debug_fp32_output has set one (one pointer per translation unit, set
+// through the function that QG_DEBUG_TU_SETTER defines).  Without the macro
+// none of this is compiled.
+#ifdef QG_DEBUG_FP32
+static __device__ float* g_qg_debug_out = nullptr;
+#define QG_DEBUG_STORE(idx, v)              \
+  do {                                      \
+    float* qg_dbg_p_ = g_qg_debug_out;      \
+    if (qg_dbg_p_) qg_dbg_p_[idx] = (v);    \
+  } while (0)
+#define QG_DEBUG_TU_SETTER(name)                                          \
+  hipError_t name(float* p) {                                             \
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_qg_debug_out), &p, sizeof(p));   \
+  }
+#else
+#define QG_DEBUG_STORE(idx, v) \
+  do {                         \
+  } while (0)
+#define QG_DEBUG_TU_SETTER(name)
+#endif
+
 // ------------------------------------------------------------ wave utilities
 
 // xor-shuffle within a wave (ds_bpermute based).

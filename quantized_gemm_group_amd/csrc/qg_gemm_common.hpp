@@ -54,6 +54,10 @@ __device__ __forceinline__ void store_out4(uint16_t* __restrict__ y, int M, int 
                                            float v0, float v1, float v2, float v3) {
   if (m >= M) return;
   uint16_t* p = y + (int64_t)m * N + n;
+  if (n < N) QG_DEBUG_STORE((int64_t)m * N + n, v0);
+  if (n + 1 < N) QG_DEBUG_STORE((int64_t)m * N + n + 1, v1);
+  if (n + 2 < N) QG_DEBUG_STORE((int64_t)m * N + n + 2, v2);
+  if (n + 3 < N) QG_DEBUG_STORE((int64_t)m * N + n + 3, v3);
   if (n + 3 < N && (N & 3) == 0) {
     uint2 o;
     o.x = pack_bf16x2(v0, v1);

@@ -453,6 +453,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
           v[r] = g / (1.f + __expf(-g)) * u;
         }
         const int ml = t * 32 + l32, nl = 8 * b + 4 * lh;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * 128 + ml, c = c0 + wn * 32 + nl + r;
+          if (m < M && c < I) QG_DEBUG_STORE((int64_t)m * I + c, v[r]);
+        }
         *reinterpret_cast<uint2*>(sh + ml * kHPitch + nl * 2) =
             make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
@@ -491,6 +496,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
           if constexpr (!MX) v[r] *= sxv[t] * swv[u][b][r];
         }
         const int ml = t * 32 + l32, nl = u * 32 + 8 * b + 4 * lh;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * 128 + ml, n = n0 + wn * 64 + nl + r;
+          if (m < M && n < N) QG_DEBUG_STORE((int64_t)m * N + n, v[r]);
+        }
         *reinterpret_cast<uint2*>(so + ml * kEpiPitch + nl * 2) =
             make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
@@ -529,6 +539,8 @@ hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, co
 }
 
 }  // namespace
+
+QG_DEBUG_TU_SETTER(debug_set_f8f4)
 
 hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const void* w,
                            const void* w_scales, int64_t N, int64_t K, void* y,

@@ -206,6 +206,8 @@ void launch_t(const void* a, const void* sa, const void* za, int64_t M, const vo
 
 }  // namespace
 
+QG_DEBUG_TU_SETTER(debug_set_int8)
+
 hipError_t launch_gemm_int8(bool a_asym, bool w_asym, const void* a, const void* a_scales,
                             const void* a_zeros, int64_t M, const void* w, const void* w_scales,
                             const void* w_zeros, int64_t N, int64_t K, void* y,

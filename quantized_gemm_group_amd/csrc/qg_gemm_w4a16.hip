@@ -356,8 +356,11 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
         const int ml = mrow0 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
         const float g = yacc[mt][0][r];
         const float u = __shfl_xor(g, 16, 64);
-        if (l32 < 16)
-          so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(g / (1.f + __expf(-g)) * u, 0.f);
+        if (l32 < 16) {
+          const float hv = g / (1.f + __expf(-g)) * u;
+          if (m0 + ml < M && n0 + nl < NI) QG_DEBUG_STORE((int64_t)(m0 + ml) * NI + n0 + nl, hv);
+          so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(hv, 0.f);
+        }
       }
   } else {
 #pragma unroll
@@ -368,6 +371,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ml = mrow0 + mt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (m0 + ml < M && n0 + nl < NI)
+            QG_DEBUG_STORE((int64_t)(m0 + ml) * NI + n0 + nl, yacc[mt][nt][r]);
           so[ml * (kPitch / 2) + nl] = (uint16_t)cvt_bf16x2(yacc[mt][nt][r], 0.f);
         }
       }
@@ -406,6 +411,8 @@ void launch_t(const void* x, int64_t M, const void* wcodes, const void* wscales,
 }
 
 }  // namespace
+
+QG_DEBUG_TU_SETTER(debug_set_w4a16)
 
 hipError_t launch_gemm_w4a16(bool asym, const void* x, int64_t M, const void* wcodes,
                              const void* wscales, const void* wzeros, int64_t N, int64_t K,

@@ -395,6 +395,9 @@ __global__ __launch_bounds__(1024) void qgemv_kernel(const uint16_t* __restrict_
       v[r] = acc;
     }
     uint16_t* yp = y + (int64_t)m * N + nb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (nb + r < N) QG_DEBUG_STORE((int64_t)m * N + nb + r, v[r]);
     if (nb + 3 < N && (N & 3) == 0) {
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
@@ -569,6 +572,7 @@ __global__ __launch_bounds__(1024) void qgemv_wave_kernel(const uint16_t* __rest
       if (m < M) {
         float v = 0.f;
         for (int k2 = 0; k2 < KS; ++k2) v += red[(k2 * 4 + r) * 64 + lane];
+        QG_DEBUG_STORE((int64_t)m * N + n, v);
         y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
       }
     }
@@ -743,7 +747,9 @@ __global__ __launch_bounds__(1024) void qgemv_swiglu_kernel(const uint16_t* __re
           g += red[((k2 * 2 + 0) * 4 + r) * 64 + lane];
           u += red[((k2 * 2 + 1) * 4 + r) * 64 + lane];
         }
-        h[(int64_t)m * I + i] = (uint16_t)f32_to_bf16_bits(g / (1.f + __expf(-g)) * u);
+        const float hv = g / (1.f + __expf(-g)) * u;
+        QG_DEBUG_STORE((int64_t)m * I + i, hv);
+        h[(int64_t)m * I + i] = (uint16_t)f32_to_bf16_bits(hv);
       }
     }
   }
@@ -923,7 +929,9 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
             g += red[((k2 * 2 + 0) * 4 + r) * 64 + lane];
             u += red[((k2 * 2 + 1) * 4 + r) * 64 + lane];
           }
-          y[(int64_t)m * I + ich] = (uint16_t)f32_to_bf16_bits(g / (1.f + __expf(-g)) * u);
+          const float hv = g / (1.f + __expf(-g)) * u;
+          QG_DEBUG_STORE((int64_t)m * I + ich, hv);
+          y[(int64_t)m * I + ich] = (uint16_t)f32_to_bf16_bits(hv);
         }
       }
     }
@@ -937,7 +945,8 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
         if (m < M && n < N) {
           float v = 0.f;
           for (int k2 = 0; k2 < KS; ++k2) v += red[((k2 * R + t) * 4 + r) * 64 + lane];
-          y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+          QG_DEBUG_STORE((int64_t)m * N + n, v);
+        y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
         }
       }
     }
@@ -1180,6 +1189,7 @@ __global__ __launch_bounds__(1024) void qgemv_groups_kernel(const uint16_t* __re
       if (m < M) {
         float v = 0.f;
         for (int k2 = 0; k2 < KS; ++k2) v += red[(k2 * 4 + r) * 64 + lane];
+        QG_DEBUG_STORE((int64_t)m * N + n, v);
         y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
       }
     }
@@ -1339,6 +1349,8 @@ __global__ __launch_bounds__(256) void tile_codes_kernel(const u32x4* __restrict
 }
 
 }  // namespace
+
+QG_DEBUG_TU_SETTER(debug_set_gemv)
 
 hipError_t launch_tile_gemv_codes(const void* codes, int64_t N, int64_t K, void* tiled,
                                   hipStream_t stream) {

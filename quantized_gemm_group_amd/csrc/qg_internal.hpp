@@ -101,4 +101,12 @@ hipError_t launch_calib_stream_read(const void* src, int64_t bytes, uint32_t* si
 hipError_t launch_calib_mfma(int kind, int64_t waves, int64_t iters, float* sink,
                              hipStream_t stream);
 
+#ifdef QG_DEBUG_FP32
+// Debug library: point every translation unit's fp32 output recorder at p.
+hipError_t debug_set_gemv(float* p);
+hipError_t debug_set_f8f4(float* p);
+hipError_t debug_set_int8(float* p);
+hipError_t debug_set_w4a16(float* p);
+#endif
+
 }  // namespace qg

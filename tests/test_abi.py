@@ -321,3 +321,13 @@ def test_qgemm_swiglu_fp8_validation(lib):
     assert f(*ok[:7], None, None) == _lib.ERR_NULL
     assert f(*ok[:7], MIS, None) == _lib.ERR_ALIGN
     assert f(A16, A16b, 1 << 20, *ok[3:6], 8192, A16e, None) == _lib.ERR_UNSUPPORTED
+
+
+def test_debug_library_loads_and_product_library_refuses_recording(lib):
+    assert lib.qg_debug_build() == 0
+    assert lib.qg_debug_fp32_output(None, None) == _lib.ERR_UNSUPPORTED
+    dlib = _lib.load_debug()
+    assert dlib.qg_debug_build() == 1
+    for name in _lib.EXPORTS:
+        assert hasattr(dlib, name), name
+    assert dlib.qg_debug_fp32_output(vp(0x1002), None) == _lib.ERR_ALIGN
