@@ -167,8 +167,10 @@ qg_status qg_qgemv(qg_format wfmt, const void* x, int64_t M,
  * interleaved weight layout is the NVIDIA prior art).  Tiled layout: tile t
  * (rows 16t .. 16t+15), group g (128 codes = 64 bytes per row) is one
  * contiguous 1 KiB block at byte (t * K/128 + g) * 1024, holding the 16 rows'
- * 64-byte group segments in row order, each exactly as in the canonical
- * packing (same nibble order); rows past N in the last tile are zero.  The
+ * 64-byte group segments a quarter at a time: bytes 16q .. 16q+15 of the
+ * segment of row r (0..15) at block offset 256 q + 16 r, each exactly as in
+ * the canonical packing (same nibble order); rows past N in the last tile
+ * are zero.  The
  * nibbles only move, so INT4_SYM and INT4_ASYM tile alike, and the scales
  * and zero points keep their canonical [N][K/group] layout.
  *   codes        int32 [N][K/8], the canonical packing of qg_quantize_pack.

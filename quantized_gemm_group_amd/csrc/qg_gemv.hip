@@ -78,9 +78,12 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // int32): row n, group g at n * K/2 + 64 g; one wave-wide 16-byte load covers
 // 16 rows x 64 bytes, i.e. half of 16 cache lines.  Tiled layout (written
 // once by qg_tile_gemv_weights): tile t, group g is one contiguous 1 KiB block
-// [t][g][16 rows][64 bytes], so the same load covers 8 whole lines; those
-// loads carry the non-temporal hint (the codes are read once: they stream
-// past the caches instead of displacing the activations and scales there).
+// [t][g][4 quarters][16 rows][16 bytes], quarter q holding bytes 16 q .. +15
+// of each row's group, so the same load reads the block in lane order (lane
+// li + 16 lg at 16 (li + 16 lg)): every 4 lanes one 64-byte run, the wave 8
+// whole lines.  Those loads carry the non-temporal hint (the codes are read
+// once: they stream past the caches instead of displacing the activations and
+// scales there).
 template <bool TILED>
 struct WLayout {
   static constexpr int kGroupStride = TILED ? 1024 : 64;   // bytes between groups of a row
@@ -88,7 +91,7 @@ struct WLayout {
   __device__ static uint32_t row_off(int n, int lg, int N, int K) {
     if (n >= N) return 0x80000000u;                       // past the end: reads zero
     return TILED ? (uint32_t)(n >> 4) * (uint32_t)(K / 128) * 1024u +
-                       (uint32_t)((n & 15) * 64 + lg * 16)
+                       (uint32_t)(lg * 256 + (n & 15) * 16)
                  : (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(lg * 16);
   }
   // the same for row li of tile `tile`
@@ -789,11 +792,18 @@ __device__ __forceinline__ u32x4 transpose_rows(const u32x4& v) {
 // of the MFMA in use, every matrix instruction takes its activations straight
 // from memory (served by the caches: x is shared by every workgroup), no LDS
 // staging and no barrier until the K-slices are summed.  Within a group,
-// lane (li, lg) and MFMA i cover k = 32 i + 8 lg .. + 7 for both operands:
-// each activation load reads 64 contiguous bytes of every row (two loads
-// fill a cache line).  The lane's 16-byte code load holds words
-// 4 lg .. 4 lg + 3 of its channel; a transpose across the lane rows turns
-// them into words lg, 4 + lg, 8 + lg, 12 + lg, the ones its MFMAs need.
+// lane (li, lg) and MFMA i cover k = 32 i + 8 lg .. + 7 for both operands.
+// The lane's 16-byte code load holds words 4 lg .. 4 lg + 3 of its channel;
+// a transpose across the lane rows turns them into words lg, 4 + lg, 8 + lg,
+// 12 + lg, the ones its MFMAs need.
+// Activations are read in whole 128-byte lines: the lanes of a row pair
+// (li = 2p, 2p + 1) load, in load (h, e), all 8 chunks of line h of row
+// 2p + e (lane 2p + b takes chunk 4 (b ^ e) + lg of the line).  So each lane
+// holds, for line h, one chunk of its own row (k chunk 8 h + lg: MFMA 2 h)
+// and one of its partner row (k chunk 8 h + 4 + lg: MFMA 2 h + 1); a select
+// on the lane parity picks them.  MFMAs 1 and 3 thus see the rows of each
+// pair swapped, which swaps their output rows m, m ^ 1: they accumulate
+// apart and are read back with the register index flipped.
 // D groups are kept in flight in registers.
 // The matrix cores take x as the first operand: lane (li, lg) accumulates
 // D[m = 4 lg + r][n = li] of each channel tile, and an MFMA against 1.0
@@ -814,8 +824,8 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
                                                          uint32_t cmag) {
   extern __shared__ float4 lds4[];
   float* red = reinterpret_cast<float*>(lds4);
-  constexpr int D = NG == 16 ? 2 : (R == 1 ? 4 : 3);   // groups in flight
-  static_assert(NG % 4 == 0, "groups per wave: a multiple of 4");
+  constexpr int D = NG == 2 ? 2 : (NG == 16 ? 2 : (R == 1 ? 4 : 3));   // groups in flight
+  static_assert(NG == 2 || NG % 4 == 0, "groups per wave: 2 or a multiple of 4");
   const int G = K / kGroup;
   const int lane = threadIdx.x & 63;
   const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -825,12 +835,19 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
 
   // rows m >= M and channels n >= N read as zero (out of the buffer ranges)
   const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x, (int64_t)M * K * 2);
-  const uint32_t xoff = li < M ? (uint32_t)(li * K + gb * kGroup + 8 * lg) * 2 : 0x80000000u;
+  const int odd = li & 1;
+  uint32_t xoff[2];                              // load (h, e): row (li & ~1) + e
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int row = (li & ~1) + e;
+    xoff[e] = row < M ? (uint32_t)((row * K + gb * kGroup) * 2 + 64 * (odd ^ e) + 16 * lg)
+                      : 0x80000000u;
+  }
   using WL = WLayout<TILED>;
   const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N, K));
   const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * G * 2);
   const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
-  uint32_t woff[R];
+  uint32_t woff[R], soffs[R];
   uint32_t sv[R][NG / 2], zv[R][NG / 2];
   static_assert(!SWIGLU || R == 2, "SwiGLU pairs a gate and an up tile");
   const int I = N / 2;
@@ -840,8 +857,20 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
     const int n = SWIGLU ? (ich < I ? t * I + ich : N) : n0 + 16 * t + li;
     woff[t] = SWIGLU ? WL::row_off(n, lg, N, K) : WL::lane_off(blockIdx.x * R + t, li, lg, N, K);
     if (woff[t] != 0x80000000u) woff[t] += (uint32_t)(gb * WL::kGroupStride);
-    const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
-    if constexpr (NG == 4) {
+    soffs[t] = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
+  }
+  // Load order: every scale and zero point, then the ring group by group.
+  // Vector loads retire in issue order, so a scale load queued behind the
+  // ring would hold the first group's arithmetic until the whole ring lands;
+  // the scheduling barriers keep the compiler from moving loads across.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const uint32_t soff = soffs[t];
+    if constexpr (NG == 2) {
+      sv[t][0] = __builtin_amdgcn_raw_buffer_load_b32(sres, soff, 0, 0);
+      zv[t][0] = ASYM ? __builtin_amdgcn_raw_buffer_load_b32(zres, soff, 0, 0) : 0u;
+    } else if constexpr (NG == 4) {
       const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
       const uint2 z2 = ASYM ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0))
                             : uint2{0u, 0u};
@@ -863,15 +892,19 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
     }
   }
 
-  u32x4 xr[D][4], wr[D][R];
+  u32x4 xr[D][4], wr[D][R];                      // xr[slot][2 h + e]
   auto load = [&](int j, int slot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr[slot][i] = bload(xres, xoff, j * 256 + i * 64);
+    for (int i = 0; i < 4; ++i) xr[slot][i] = bload(xres, xoff[i & 1], j * 256 + (i >> 1) * 128);
 #pragma unroll
     for (int t = 0; t < R; ++t) wr[slot][t] = WL::load(wres, woff[t], j * WL::kGroupStride);
   };
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < D; ++j) load(j, j);
+  for (int j = 0; j < D; ++j) {
+    load(j, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   float yacc[R][4];
@@ -881,22 +914,32 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
     for (int r = 0; r < 4; ++r) yacc[t][r] = 0.f;
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
+    // one group at a time: nothing of a later group is hoisted into this one
+    // (its selects would wait for that group's loads)
+    __builtin_amdgcn_sched_barrier(0);
     const int slot = j % D;
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // [0]: MFMAs 0, 2 (own rows); [1]: MFMAs 1, 3 (rows of each pair swapped)
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     u32x4 wt[R];
 #pragma unroll
     for (int t = 0; t < R; ++t) wt[t] = transpose_rows(wr[slot][t]);
     f32x4 acc[R][2];
 #pragma unroll
-    for (int t = 0; t < R; ++t) acc[t][0] = acc[t][1] = sacc;
+    for (int t = 0; t < R; ++t) acc[t][0] = acc[t][1] = sacc[0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bf16x8 a = as_bf16x8(xr[slot][i]);
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(ones), sacc, 0, 0, 0);
+      // MFMA 2 h: own chunk of line h (load (h, odd)); 2 h + 1: the partner's
+      const int h = i >> 1, f = i & 1;
+      u32x4 xv;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        xv[d] = (odd ^ f) ? xr[slot][2 * h + 1][d] : xr[slot][2 * h][d];
+      const bf16x8 a = as_bf16x8(xv);
+      sacc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(ones), sacc[f], 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < R; ++t)
-        acc[t][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            a, as_bf16x8(unpack_word_nat(wt[t][i], mask, cmag)), acc[t][i & 1], 0, 0, 0);
+        acc[t][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            a, as_bf16x8(unpack_word_nat(wt[t][i], mask, cmag)), acc[t][f], 0, 0, 0);
     }
     if (j + D < NG) load(j + D, slot);
 #pragma unroll
@@ -906,8 +949,9 @@ __global__ __launch_bounds__(1024) void qgemv_m16_kernel(const uint16_t* __restr
       if constexpr (ASYM) cc = 128.f + f16_bits_to_f32((zv[t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        yacc[t][r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sacc[r], acc[t][0][r] + acc[t][1][r]),
-                                    yacc[t][r]);
+        yacc[t][r] = __builtin_fmaf(
+            sc, __builtin_fmaf(-cc, sacc[0][r] + sacc[1][r ^ 1], acc[t][0][r] + acc[t][1][r ^ 1]),
+            yacc[t][r]);
     }
   }
 
@@ -1329,7 +1373,7 @@ hipError_t launch_qgemv_t(bool asym, const void* x, int64_t M, const void* wcode
 namespace {
 
 // One lane per 16-byte piece of the tiled output: piece q of tile t, group g,
-// row r, quarter b is the 16 bytes at row t*16 + r, byte 64 g + 16 b of the
+// quarter b, row r is the 16 bytes at row t*16 + r, byte 64 g + 16 b of the
 // canonical codes (zero for rows past N).  64 consecutive lanes write one
 // contiguous 1 KiB block.
 __global__ __launch_bounds__(256) void tile_codes_kernel(const u32x4* __restrict__ src, int N,
@@ -1338,7 +1382,7 @@ __global__ __launch_bounds__(256) void tile_codes_kernel(const u32x4* __restrict
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= pieces) return;
   const int G = K / kGroup;
-  const int b = (int)(q & 3), r = (int)((q >> 2) & 15);
+  const int r = (int)(q & 15), b = (int)((q >> 4) & 3);
   const int64_t tg = q >> 6;
   const int g = (int)(tg % G);
   const int64_t t = tg / G;

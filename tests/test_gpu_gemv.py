@@ -92,7 +92,8 @@ def test_qgemv_one_hot_is_bit_exact(asym):
 @pytest.mark.parametrize("n,k", [(16, 128), (37, 384), (5, 1024), (1000, 4096)])
 def test_tile_gemv_weights_layout(n, k):
     # the tiled layout of the header, written out with numpy: block (t, g) of
-    # 1 KiB holds rows 16t .. 16t+15, bytes 64g .. 64g+63 of each, zero rows
+    # 1 KiB holds rows 16t .. 16t+15, bytes 64g .. 64g+63 of each, quarter by
+    # quarter (16 bytes of each of the 16 rows, then the next 16), zero rows
     # past N
     dev = device()
     codes = rng_for(n + k).integers(-2 ** 31, 2 ** 31, size=(n, k // 8), dtype=np.int64)
@@ -101,7 +102,7 @@ def test_tile_gemv_weights_layout(n, k):
     tiles, g = (n + 15) // 16, k // 128
     rows = np.zeros((tiles * 16, k // 2), np.uint8)
     rows[:n] = codes.view(np.uint8).reshape(n, k // 2)
-    want = rows.reshape(tiles, 16, g, 64).transpose(0, 2, 1, 3).reshape(-1)
+    want = rows.reshape(tiles, 16, g, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
     assert got.shape == want.shape and (got == want).all()
 
 
