@@ -30,6 +30,8 @@
 //    in LDS; the K-slices of a row tile are summed through LDS and rounded
 //    once to bf16 (RNE).  No scratch memory.
 
+#include <type_traits>
+
 #include "qg_device.hpp"
 #include "qg_internal.hpp"
 
@@ -1040,6 +1042,343 @@ hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, co
   return launch_m16_t<false, 8, 1, TILED>(x, M, w, s, z, N, K, y, stream);
 }
 
+// x-shared GEMV for 5 <= M <= 16 rows and K <= 4096 (all 16 rows of x fit in
+// LDS).  At 16 rows the activations, not the codes, dominate the reads: a
+// 16-channel tile's K-slice of codes is a quarter of the bytes of the same
+// slice of x, and every tile-wave re-reading x from L2 made those reads the
+// bound.  Here a workgroup of TL x KS waves (one per CU) stages x once -- 16
+// rows in 1 KiB direct-to-LDS loads, each covering 4 whole rows of a group,
+// chunk c of row r stored at 16-byte slot c ^ r so that the 16 rows of a
+// fragment read land on distinct banks -- forms the group sums of x once, and
+// then handles T consecutive 16-channel tiles: wave (tl, ks) takes K-slice ks
+// (NG groups) of tiles tl, tl + TL, ... (its units), streaming their codes
+// through a register ring that runs across unit boundaries, and reading its x
+// fragments from LDS.  Since x comes from LDS in any order, lane (li, lg) and
+// MFMA i cover chunk 4 lg + i: the lane's 16-byte code load holds exactly the
+// words its 4 MFMAs need.  After each unit the KS partial tiles are summed
+// through LDS (two barriers) and rounded once to bf16.
+// SWIGLU (R = 2): a unit is 16 channels of h, tile 0 their gate rows and
+// tile 1 their up rows of [W_gate; W_up] (N = 2I rows); h = bf16(SiLU(g) u)
+// (《推理优化与量化算子深度技术调研》 section 4.6).
+// LDS: [x: G x 16 x 256 B][sum_x: G x 16 floats][partials: TL KS R x 1 KiB].
+template <bool ASYM, int NG, int R, bool TILED, bool SWIGLU>
+__global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restrict__ x, int M,
+                                                        const uint32_t* __restrict__ w,
+                                                        const uint16_t* __restrict__ s16,
+                                                        const uint16_t* __restrict__ z16, int N,
+                                                        int K, int KS, int TL, int T, int U,
+                                                        uint16_t* __restrict__ y, uint32_t mask,
+                                                        uint32_t cmag) {
+  static_assert(SWIGLU ? R == 2 : R == 1, "one tile per unit, two (gate, up) for SwiGLU");
+  static_assert(NG == 2 || NG == 4 || NG % 8 == 0, "groups per unit: 2, 4 or a multiple of 8");
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  extern __shared__ float4 lds4[];
+  uint8_t* const xs = reinterpret_cast<uint8_t*>(lds4);
+  const int G = K / kGroup;
+  float* const sxs = reinterpret_cast<float*>(xs + G * 4096);
+  float* const red = sxs + G * 16;
+  constexpr int D = NG < 4 / R ? NG : 4 / R;         // ring depth (groups), divides NG
+  const int nw = TL * KS;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tl = wave / KS, ks = wave - tl * KS;
+  const int li = lane & 15, lg = lane >> 4;
+  const int gb = ks * NG;
+  const int I = N / 2;
+  const int tiles = SWIGLU ? (I + 15) / 16 : (N + 15) / 16;
+  using WL = WLayout<TILED>;
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc_g(x, (int64_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc_g(w, WL::bytes(N, K));
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc_g(s16, (int64_t)N * G * 2);
+  const __amdgpu_buffer_rsrc_t zres = make_rsrc_g(z16, ASYM ? (int64_t)N * G * 2 : 0);
+
+  // tile of unit u (-1: none) and the weight row of tile t of it for this lane
+  auto unit_tile = [&](int u) {
+    const int k = tl + u * TL;
+    const int tu = blockIdx.x * T + k;
+    return (k < T && tu < tiles) ? tu : -1;
+  };
+  auto unit_row = [&](int tu, int t) {
+    if (tu < 0) return N;
+    if constexpr (SWIGLU) {
+      const int ich = tu * 16 + li;
+      return ich < I ? t * I + ich : N;
+    }
+    return tu * 16 + li;
+  };
+  uint32_t woff_c[R], woff_n[R];                     // codes of the current / next unit
+  auto unit_woff = [&](int u, uint32_t (&wo)[R]) {
+    const int tu = u < U ? unit_tile(u) : -1;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const uint32_t o = WL::row_off(unit_row(tu, t), lg, N, K);
+      wo[t] = o == 0x80000000u ? o : o + (uint32_t)(gb * WL::kGroupStride);
+    }
+  };
+  uint32_t sv[2][R][NG / 2], zv[2][R][NG / 2];       // by unit parity
+  auto load_scales = [&](int u, auto pc) {
+    constexpr int P = decltype(pc)::value;
+    const int tu = u < U ? unit_tile(u) : -1;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int n = unit_row(tu, t);
+      const uint32_t soff = n < N ? (uint32_t)(n * G + gb) * 2 : 0x80000000u;
+      if constexpr (NG == 2) {
+        sv[P][t][0] = __builtin_amdgcn_raw_buffer_load_b32(sres, soff, 0, 0);
+        zv[P][t][0] = ASYM ? __builtin_amdgcn_raw_buffer_load_b32(zres, soff, 0, 0) : 0u;
+      } else if constexpr (NG == 4) {
+        const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 0, 0));
+        const uint2 z2 = ASYM ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(zres, soff, 0, 0))
+                              : uint2{0u, 0u};
+        sv[P][t][0] = s2.x;
+        sv[P][t][1] = s2.y;
+        zv[P][t][0] = z2.x;
+        zv[P][t][1] = z2.y;
+      } else {
+#pragma unroll
+        for (int c = 0; c < NG / 8; ++c) {
+          const u32x4 s4 = bload(sres, soff, 16 * c);
+          const u32x4 z4 = ASYM ? bload(zres, soff, 16 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[P][t][4 * c + e] = s4[e];
+            zv[P][t][4 * c + e] = z4[e];
+          }
+        }
+      }
+    }
+  };
+  constexpr int kScaleLoads = R * (NG <= 4 ? 1 : NG / 8) * (ASYM ? 2 : 1);
+
+  // ---- 1. x into LDS: load q covers group q / 4, rows 4 (q % 4) .. + 3;
+  //      lane l fetches chunk (l % 16) ^ r of row r = 4 (q % 4) + l / 16
+  //      (rows >= M read as zero)
+  for (int q = wave; q < 4 * G; q += nw) {
+    const int r = 4 * (q & 3) + (lane >> 4);
+    const int c = (lane & 15) ^ r;
+    const uint32_t vo = r < M ? (uint32_t)(r * K * 2 + c * 16) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)(xs + q * 1024), 16, vo,
+                                             (q >> 2) * 256, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- 2. scales of unit 0, then the first D groups of the code stream
+  load_scales(0, std::integral_constant<int, 0>{});
+  unit_woff(0, woff_c);
+  u32x4 wr[D][R];
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+#pragma unroll
+    for (int t = 0; t < R; ++t) wr[j][t] = WL::load(wres, woff_c[t], j * WL::kGroupStride);
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's x loads have landed (vector loads retire in order); then
+  // every wave's
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kScaleLoads + D * R) : "memory");
+
+  // ---- 3. group sums of x: lane l sums 32 values of row l / 4
+  {
+    const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    const int r = lane >> 2, part = lane & 3;
+    for (int g = wave; g < G; g += nw) {
+      float ps = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int c = 4 * part + h;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xs + g * 4096 + r * 256 + ((c ^ r) << 4));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t e = v[d];
+          ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e), ones2, ps, false);
+        }
+      }
+      ps += shfl_xor(ps, 1);
+      ps += shfl_xor(ps, 2);
+      if (part == 0) sxs[g * 16 + r] = ps;
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. units.  The lane's 4 fragment addresses in group gb (the group
+  //      of the slice then adds an immediate offset)
+  const uint8_t* xfa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xfa[i] = xs + gb * 4096 + li * 256 + (((4 * lg + i) ^ li) << 4);
+  const float* const sxa = sxs + gb * 16 + 4 * lg;
+  auto unit = [&](int u, auto pc) {
+    constexpr int P = decltype(pc)::value;
+    // (past the last unit these read nothing: the offsets are out of range)
+    load_scales(u + 1, std::integral_constant<int, 1 - P>{});
+    unit_woff(u + 1, woff_n);
+    float yacc[R][4];
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) yacc[t][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 xf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const u32x4*>(xfa[i] + j * 4096);
+      const float4 sx = *reinterpret_cast<const float4*>(sxa + j * 16);
+      f32x4 acc[R][2];
+#pragma unroll
+      for (int t = 0; t < R; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+          acc[t][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(xf[i]), as_bf16x8(unpack_word_nat(wr[j % D][t][i], mask, cmag)),
+              acc[t][i & 1], 0, 0, 0);
+      // the next item of the stream into this slot: group j + D of this unit
+      // or group j + D - NG of the next
+      if (j + D < NG) {
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+          wr[j % D][t] = WL::load(wres, woff_c[t], (j + D) * WL::kGroupStride);
+      } else {
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+          wr[j % D][t] = WL::load(wres, woff_n[t], (j + D - NG) * WL::kGroupStride);
+      }
+      const float sxr[4] = {sx.x, sx.y, sx.z, sx.w};
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const float sc = f16_bits_to_f32((sv[P][t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+        float cc = 136.f;
+        if constexpr (ASYM)
+          cc = 128.f + f16_bits_to_f32((zv[P][t][j >> 1] >> (16 * (j & 1))) & 0xffffu);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          yacc[t][r] = __builtin_fmaf(sc, __builtin_fmaf(-cc, sxr[r], acc[t][0][r] + acc[t][1][r]),
+                                      yacc[t][r]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- partial tiles: red[tl][ks][t][r][lane]; wave (tl, ks) then sums
+    //      registers r = ks, ks + KS, ... of its tile-lane's unit and writes
+    //      y[m = 4 lg + r][n = 16 tile + li] (m < M, n < N)
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(((tl * KS + ks) * R + t) * 4 + r) * 64 + lane] = yacc[t][r];
+    __syncthreads();
+    const int tu = unit_tile(u);
+    if (tu >= 0) {
+      for (int r = ks; r < 4; r += KS) {
+        const int m = 4 * lg + r;
+        float v[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          v[t] = 0.f;
+          for (int k2 = 0; k2 < KS; ++k2) v[t] += red[(((tl * KS + k2) * R + t) * 4 + r) * 64 + lane];
+        }
+        if constexpr (SWIGLU) {
+          const int ich = tu * 16 + li;
+          if (m < M && ich < I) {
+            const float hv = v[0] / (1.f + __expf(-v[0])) * v[1];
+            QG_DEBUG_STORE((int64_t)m * I + ich, hv);
+            y[(int64_t)m * I + ich] = (uint16_t)f32_to_bf16_bits(hv);
+          }
+        } else {
+          const int n = tu * 16 + li;
+          if (m < M && n < N) {
+            QG_DEBUG_STORE((int64_t)m * N + n, v[0]);
+            y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v[0]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < R; ++t) woff_c[t] = woff_n[t];
+  };
+  for (int u = 0; u < U; u += 2) {
+    unit(u, std::integral_constant<int, 0>{});
+    if (u + 1 < U) unit(u + 1, std::integral_constant<int, 1>{});
+  }
+}
+
+// Launch shape of the x-shared kernel (measured on MI355X for the Llama-3-8B
+// decode shapes): T = ceil(tiles / 256) tiles per workgroup (about one
+// workgroup per CU), TL = T tile-lanes up to 8 / R (beyond, the power of two
+// up to 4 / R with U = ceil(T / TL) units per wave) and KS K-slices, the
+// largest power of two with TL KS <= 16, halved until NG = G / KS is 2, 4, 8
+// or 16.  A 4-group ring (2 at R = 2): 8 groups measured slower.  0 when the
+// kernel does not apply: M outside 5..16, a single tile per workgroup (it
+// measured slower than the per-wave kernel there: nothing is shared), or x
+// and the partial sums beyond 160 KiB of LDS (K above about 4096).
+struct XsShape {
+  int T, TL, KS, U, NG;
+  size_t lds;
+};
+XsShape xs_shape(int M, int tiles, int K, int R) {
+  XsShape sh{0, 0, 0, 0, 0, 0};
+  const int G = K / kGroup;
+  if (M < 5 || M > 16 || K % kGroup != 0 || G < 2) return sh;
+  int T = (tiles + 255) / 256;
+  if (T < 2) return sh;                          // one tile a workgroup: nothing to share
+  int TL = 1;
+  if (T <= 8 / R) TL = T; else while (TL < T && TL < 4 / R) TL *= 2;
+  auto ng_ok = [](int ng) { return ng == 2 || ng == 4 || ng == 8 || ng == 16; };
+  int KS = 1;
+  while (KS * 2 * TL <= 16) KS *= 2;
+  while (KS > 1 && (G % KS != 0 || !ng_ok(G / KS))) KS /= 2;
+  const int NG = G / KS;
+  if (G % KS != 0 || !ng_ok(NG)) return sh;
+  const size_t lds = (size_t)G * 4096 + (size_t)G * 64 + (size_t)TL * KS * R * 1024;
+  if (lds > 160 * 1024) return sh;
+  sh.T = T;
+  sh.TL = TL;
+  sh.KS = KS;
+  sh.U = (T + TL - 1) / TL;
+  sh.NG = NG;
+  sh.lds = lds;
+  return sh;
+}
+
+template <bool ASYM, int NG, int R, bool TILED, bool SWIGLU>
+void launch_xs_t(const XsShape& sh, int blocks, const void* x, int M, const void* w, const void* s,
+                 const void* z, int N, int K, void* y, hipStream_t stream) {
+  hipLaunchKernelGGL((qgemv_xs_kernel<ASYM, NG, R, TILED, SWIGLU>), dim3(blocks),
+                     dim3(64 * sh.TL * sh.KS), sh.lds, stream, (const uint16_t*)x, M,
+                     (const uint32_t*)w, (const uint16_t*)s, (const uint16_t*)z, N, K, sh.KS, sh.TL,
+                     sh.T, sh.U, (uint16_t*)y, 0x000F000Fu, ASYM ? 0x43004300u : 0x43084308u);
+}
+
+// The x-shared GEMV (or SwiGLU GEMV over [W_gate; W_up], N = 2I rows) when
+// its shape applies; hipErrorNotSupported otherwise.
+template <bool TILED, bool SWIGLU>
+hipError_t launch_xs(bool asym, const void* x, int M, const void* w, const void* s, const void* z,
+                     int N, int K, void* y, hipStream_t stream) {
+  constexpr int R = SWIGLU ? 2 : 1;
+  const int tiles = SWIGLU ? (N / 2 + 15) / 16 : (N + 15) / 16;
+  const XsShape sh = xs_shape(M, tiles, K, R);
+  if (!sh.T) return hipErrorNotSupported;
+  const int blocks = (tiles + sh.T - 1) / sh.T;
+#define QG_XS(A, NGV) launch_xs_t<A, NGV, R, TILED, SWIGLU>(sh, blocks, x, M, w, s, z, N, K, y, stream)
+  if (asym) {
+    switch (sh.NG) {
+      case 2: QG_XS(true, 2); break;
+      case 4: QG_XS(true, 4); break;
+      case 8: QG_XS(true, 8); break;
+      case 16: QG_XS(true, 16); break;
+      default: return hipErrorNotSupported;
+    }
+  } else {
+    switch (sh.NG) {
+      case 2: QG_XS(false, 2); break;
+      case 4: QG_XS(false, 4); break;
+      case 8: QG_XS(false, 8); break;
+      case 16: QG_XS(false, 16); break;
+      default: return hipErrorNotSupported;
+    }
+  }
+#undef QG_XS
+  return hipGetLastError();
+}
+
 // Launch shape (measured on MI355X for the Llama-3-8B decode shapes): about
 // 1024 waves in the grid (4 per CU) with 8-16 groups per wave -- KS K-slices
 // per 16-row tile -- and 2 row tiles per workgroup once there are more than
@@ -1320,6 +1659,10 @@ hipError_t launch_swiglu_t(bool asym, const void* x, int M, const void* w, const
 #undef QG_SWIGLU_WAVE
     return hipGetLastError();
   }
+  {
+    const hipError_t e = launch_xs<TILED, true>(asym, x, M, w, s, z, N2, K, h, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (G % 4 != 0 || G / 4 > 16) return hipErrorInvalidValue;
   const int ks = G / 4;
   const size_t lds = (size_t)ks * 2 * 4 * 64 * sizeof(float);
@@ -1349,6 +1692,8 @@ hipError_t launch_qgemv_t(bool asym, const void* x, int64_t M, const void* wcode
   const int ng = pick_wave_ng(m, n, k);
   if (ng) return launch_wave<TILED>(asym, ng, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   if (m > 4) {
+    const hipError_t e = launch_xs<TILED, false>(asym, x, m, wcodes, wscales, wzeros, n, k, y, stream);
+    if (e != hipErrorNotSupported) return e;
     const int ng16 = pick_m16_ng(k);
     if (ng16) return launch_m16<TILED>(asym, ng16, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   }

@@ -57,7 +57,12 @@ def run_case(m, k, n, asym, seed, outliers=(0.01, 20.0)):
                                    (1, 18432, 40), (2, 14336, 70), (4, 512, 33), (1, 1536, 17),
                                    # 5..16 rows: 16 groups per wave (G = 144), two channel tiles
                                    # per wave with a ragged last tile, 4 groups per wave (G = 12)
-                                   (9, 18432, 50), (12, 1024, 16400), (5, 1536, 77)])
+                                   (9, 18432, 50), (12, 1024, 16400), (5, 1536, 77),
+                                   # 5..16 rows, x staged in LDS: 2 tiles per workgroup with a
+                                   # one-tile last workgroup, 3 tiles on 4 tile-lanes, one
+                                   # K-slice, 3 units per wave
+                                   (5, 4096, 4100), (13, 512, 8200), (8, 256, 40),
+                                   (6, 1024, 40000)])
 def test_qgemv_small(m, k, n, asym):
     run_case(m, k, n, asym, seed=m * 1000 + n)
 

@@ -102,7 +102,10 @@ def _check_small(h, ref, what):
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("m,k,i", [(1, 512, 40), (1, 4096, 1000), (1, 16384, 24), (3, 1024, 33),
                                    (4, 2048, 200), (2, 8192, 17), (5, 512, 48), (9, 4096, 300),
-                                   (16, 8192, 64), (16, 1536, 1)])
+                                   (16, 8192, 64), (16, 1536, 1),
+                                   # x staged in LDS: 2 channel tiles per workgroup with a ragged
+                                   # last tile; 2 units per wave with an empty last one
+                                   (16, 2048, 5000), (7, 1024, 9000)])
 def test_qgemv_swiglu_small(m, k, i, asym):
     dev = device()
     fmt = "int4_asym" if asym else "int4_sym"
