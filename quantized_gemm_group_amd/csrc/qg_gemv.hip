@@ -1049,7 +1049,8 @@ hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, co
 // bound.  Here a workgroup of TL x KS waves (one per CU) stages x once -- 16
 // rows in 1 KiB direct-to-LDS loads, each covering 4 whole rows of a group,
 // chunk c of row r stored at 16-byte slot c ^ r so that the 16 rows of a
-// fragment read land on distinct banks -- forms the group sums of x once, and
+// fragment read land on distinct banks -- forms the group sums of x once (for
+// SwiGLU per group, by an MFMA against 1.0: LDS holds two tiles' partials), and
 // then handles T consecutive 16-channel tiles: wave (tl, ks) takes K-slice ks
 // (NG groups) of tiles tl, tl + TL, ... (its units), streaming their codes
 // through a register ring that runs across unit boundaries, and reading its x
@@ -1060,7 +1061,8 @@ hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, co
 // SWIGLU (R = 2): a unit is 16 channels of h, tile 0 their gate rows and
 // tile 1 their up rows of [W_gate; W_up] (N = 2I rows); h = bf16(SiLU(g) u)
 // (《推理优化与量化算子深度技术调研》 section 4.6).
-// LDS: [x: G x 16 x 256 B][sum_x: G x 16 floats][partials: TL KS R x 1 KiB].
+// LDS: [x: G x 16 x 256 B][sum_x: G x 16 floats, not for SwiGLU][partials: TL KS R x
+// 1 KiB].
 template <bool ASYM, int NG, int R, bool TILED, bool SWIGLU>
 __global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restrict__ x, int M,
                                                         const uint32_t* __restrict__ w,
@@ -1076,8 +1078,11 @@ __global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restri
   extern __shared__ float4 lds4[];
   uint8_t* const xs = reinterpret_cast<uint8_t*>(lds4);
   const int G = K / kGroup;
+  // SwiGLU (two tiles a unit) forms the group sums of x with an MFMA against
+  // 1.0 instead, which leaves LDS room for both tiles' partial sums
+  constexpr bool kSxLds = !SWIGLU;
   float* const sxs = reinterpret_cast<float*>(xs + G * 4096);
-  float* const red = sxs + G * 16;
+  float* const red = sxs + (kSxLds ? G * 16 : 0);
   constexpr int D = NG < 4 / R ? NG : 4 / R;         // ring depth (groups), divides NG
   const int nw = TL * KS;
   const int lane = threadIdx.x & 63;
@@ -1176,7 +1181,7 @@ __global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restri
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kScaleLoads + D * R) : "memory");
 
   // ---- 3. group sums of x: lane l sums 32 values of row l / 4
-  {
+  if constexpr (kSxLds) {
     const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
     const int r = lane >> 2, part = lane & 3;
     for (int g = wave; g < G; g += nw) {
@@ -1196,7 +1201,7 @@ __global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restri
       if (part == 0) sxs[g * 16 + r] = ps;
     }
   }
-  __syncthreads();
+  if constexpr (kSxLds) __syncthreads();
 
   // ---- 4. units.  The lane's 4 fragment addresses in group gb (the group
   //      of the slice then adds an immediate offset)
@@ -1220,17 +1225,26 @@ __global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restri
       u32x4 xf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const u32x4*>(xfa[i] + j * 4096);
-      const float4 sx = *reinterpret_cast<const float4*>(sxa + j * 16);
+      float4 sx;
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kSxLds) sx = *reinterpret_cast<const float4*>(sxa + j * 16);
       f32x4 acc[R][2];
 #pragma unroll
       for (int t = 0; t < R; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (!kSxLds) {
+          const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xf[i]), as_bf16x8(ones), sacc,
+                                                         0, 0, 0);
+        }
 #pragma unroll
         for (int t = 0; t < R; ++t)
           acc[t][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               as_bf16x8(xf[i]), as_bf16x8(unpack_word_nat(wr[j % D][t][i], mask, cmag)),
               acc[t][i & 1], 0, 0, 0);
+      }
+      if constexpr (!kSxLds) sx = float4{sacc[0], sacc[1], sacc[2], sacc[3]};
       // the next item of the stream into this slot: group j + D of this unit
       // or group j + D - NG of the next
       if (j + D < NG) {
@@ -1327,7 +1341,7 @@ XsShape xs_shape(int M, int tiles, int K, int R) {
   while (KS > 1 && (G % KS != 0 || !ng_ok(G / KS))) KS /= 2;
   const int NG = G / KS;
   if (G % KS != 0 || !ng_ok(NG)) return sh;
-  const size_t lds = (size_t)G * 4096 + (size_t)G * 64 + (size_t)TL * KS * R * 1024;
+  const size_t lds = (size_t)G * 4096 + (R == 1 ? (size_t)G * 64 : 0) + (size_t)TL * KS * R * 1024;
   if (lds > 160 * 1024) return sh;
   sh.T = T;
   sh.TL = TL;
