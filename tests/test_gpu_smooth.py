@@ -84,6 +84,32 @@ def test_smooth_scales_bit_exact(alpha):
     assert len(bad) == 0, f"{len(bad)} factors differ, first {bad[:4]}: {s[bad[:4]]} {ref[bad[:4]]}"
 
 
+@pytest.mark.parametrize("alpha", [0.3, 0.5, 0.85])
+def test_smooth_scales_bulk_agreement(alpha):
+    # 2^20 factor pairs over twelve decades.  The GPU takes the fp64 power
+    # from its math library, the oracle from the host's; each is within an
+    # ulp of the exact fp64 value, so the fp32 factors may only differ where
+    # that value sits within a few fp64 units of the midpoint between two
+    # fp32 numbers.  Every other factor must match bit for bit, and any
+    # difference must be one fp32 step at such a midpoint.
+    dev = device()
+    rng = rng_for(int(alpha * 100) + 17)
+    n = 1 << 20
+    a = (10.0 ** rng.uniform(-6, 6, n)).astype(np.float32)
+    w = (10.0 ** rng.uniform(-6, 6, n)).astype(np.float32)
+    s = host(qg.smooth_scales(to_dev(a, dev), to_dev(w, dev), alpha))
+    ref = osm.smooth_scales(a, w, alpha)
+    diff = np.flatnonzero(bits32(s) != bits32(ref))
+    print(f"alpha={alpha}: {len(diff)} of {n} factors split at a midpoint", flush=True)
+    if len(diff):
+        gs, rs = s[diff], ref[diff]
+        assert (np.abs(bits32(gs).astype(np.int64) - bits32(rs).astype(np.int64)) == 1).all()
+        v = (np.power(a[diff].astype(np.float64), alpha)
+             / np.power(w[diff].astype(np.float64), 1.0 - alpha))
+        mid = (gs.astype(np.float64) + rs.astype(np.float64)) / 2
+        assert (np.abs(v - mid) <= 8 * np.spacing(v)).all(), "a split away from a midpoint"
+
+
 @pytest.mark.parametrize("divide", [False, True])
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 @pytest.mark.parametrize("fmt,group", [(f, 128) for f in FMTS] + [("int8_sym", 1024),
