@@ -1045,7 +1045,7 @@ hipError_t launch_m16(bool asym, int ng, const void* x, int M, const void* w, co
   return launch_m16_t<false, 8, 1, TILED>(x, M, w, s, z, N, K, y, stream);
 }
 
-// x-shared GEMV for 5 <= M <= 16 rows and K <= 4096 (all 16 rows of x fit in
+// x-shared GEMV for 3 <= M <= 16 rows and K <= 4096 (all 16 rows of x fit in
 // LDS).  At 16 rows the activations, not the codes, dominate the reads: a
 // 16-channel tile's K-slice of codes is a quarter of the bytes of the same
 // slice of x, and every tile-wave re-reading x from L2 made those reads the
@@ -1323,9 +1323,13 @@ __global__ __launch_bounds__(1024) void qgemv_xs_kernel(const uint16_t* __restri
 // up to 4 / R with U = ceil(T / TL) units per wave) and KS K-slices, the
 // largest power of two with TL KS <= 16, halved until NG = G / KS is 2, 4, 8
 // or 16.  A 4-group ring (2 at R = 2): 8 groups measured slower.  0 when the
-// kernel does not apply: M outside 5..16, a single tile per workgroup (it
-// measured slower than the per-wave kernel there: nothing is shared), or x
-// and the partial sums beyond 160 KiB of LDS (K above about 4096).
+// kernel does not apply: M outside 3..16, a single tile per workgroup (it
+// measured slower than the per-wave kernel there: nothing is shared), fewer
+// than 4 tiles per workgroup at M <= 4, or x and the partial sums beyond 160
+// KiB of LDS (K above about 4096).  At M = 4 the Llama-3-8B gate+up (7 tiles
+// per workgroup) measured 15.6-15.9 -> 14.8-14.9 us here and the SwiGLU
+// gate+up (4) 14.5 -> 14.2 us, while QKV (2 tiles) went 5.7 -> 7.6 us and
+// every projection at M = 2 was slower than on the per-wave kernel.
 struct XsShape {
   int T, TL, KS, U, NG;
   size_t lds;
@@ -1333,9 +1337,10 @@ struct XsShape {
 XsShape xs_shape(int M, int tiles, int K, int R) {
   XsShape sh{0, 0, 0, 0, 0, 0};
   const int G = K / kGroup;
-  if (M < 5 || M > 16 || K % kGroup != 0 || G < 2) return sh;
+  if (M < 3 || M > 16 || K % kGroup != 0 || G < 2) return sh;
   int T = (tiles + 255) / 256;
   if (T < 2) return sh;                          // one tile a workgroup: nothing to share
+  if (M <= 4 && T < 4) return sh;                // few rows: the per-wave kernel is faster
   int TL = 1;
   if (T <= 8 / R) TL = T; else while (TL < T && TL < 4 / R) TL *= 2;
   auto ng_ok = [](int ng) { return ng == 2 || ng == 4 || ng == 8 || ng == 16; };
@@ -1637,10 +1642,12 @@ int swiglu_wave_ng(int M, int K) {
   return 0;
 }
 
-// SwiGLU GEMV launch: M <= 4 on the per-wave kernel (gate and up tiles in
-// every wave, NG groups per wave so that K splits into at most 16 slices),
-// 5 <= M <= 16 on the 16-row kernel with the gate / up tile pair.  Returns
-// hipErrorInvalidValue for shapes neither covers (checked by the caller).
+// SwiGLU GEMV launch: the x-shared kernel with the gate / up tile pair where
+// its shape applies (3 <= M <= 16), else M <= 4 on the per-wave kernel (gate
+// and up tiles in every wave, NG groups per wave so that K splits into at
+// most 16 slices) and 5 <= M <= 16 on the 16-row kernel with the tile pair.
+// Returns hipErrorInvalidValue for shapes none covers (checked by the
+// caller).
 template <bool TILED>
 hipError_t launch_swiglu_t(bool asym, const void* x, int M, const void* w, const void* s,
                            const void* z, int N2, int K, void* h, hipStream_t stream) {
@@ -1648,6 +1655,10 @@ hipError_t launch_swiglu_t(bool asym, const void* x, int M, const void* w, const
   const int I = N2 / 2;
   const int tiles = (I + 15) / 16;
   const uint32_t mask = 0x000F000Fu, cmag = asym ? 0x43004300u : 0x43084308u;
+  if (M >= 3) {
+    const hipError_t e = launch_xs<TILED, true>(asym, x, M, w, s, z, N2, K, h, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (M <= 4) {
     const int ng = swiglu_wave_ng(M, K);
     if (!ng) return hipErrorInvalidValue;
@@ -1676,10 +1687,6 @@ hipError_t launch_swiglu_t(bool asym, const void* x, int M, const void* w, const
 #undef QG_SWIGLU_WAVE
     return hipGetLastError();
   }
-  {
-    const hipError_t e = launch_xs<TILED, true>(asym, x, M, w, s, z, N2, K, h, stream);
-    if (e != hipErrorNotSupported) return e;
-  }
   if (G % 4 != 0 || G / 4 > 16) return hipErrorInvalidValue;
   const int ks = G / 4;
   const size_t lds = (size_t)ks * 2 * 4 * 64 * sizeof(float);
@@ -1706,11 +1713,13 @@ hipError_t launch_qgemv_t(bool asym, const void* x, int64_t M, const void* wcode
                           hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   const int G = k / kGroup;
+  if (m >= 3) {
+    const hipError_t e = launch_xs<TILED, false>(asym, x, m, wcodes, wscales, wzeros, n, k, y, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   const int ng = pick_wave_ng(m, n, k);
   if (ng) return launch_wave<TILED>(asym, ng, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   if (m > 4) {
-    const hipError_t e = launch_xs<TILED, false>(asym, x, m, wcodes, wscales, wzeros, n, k, y, stream);
-    if (e != hipErrorNotSupported) return e;
     const int ng16 = pick_m16_ng(k);
     if (ng16) return launch_m16<TILED>(asym, ng16, x, m, wcodes, wscales, wzeros, n, k, y, stream);
   }

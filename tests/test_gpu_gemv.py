@@ -62,7 +62,11 @@ def run_case(m, k, n, asym, seed, outliers=(0.01, 20.0)):
                                    # one-tile last workgroup, 3 tiles on 4 tile-lanes, one
                                    # K-slice, 3 units per wave
                                    (5, 4096, 4100), (13, 512, 8200), (8, 256, 40),
-                                   (6, 1024, 40000)])
+                                   (6, 1024, 40000),
+                                   # 3 and 4 rows, x staged in LDS (4 or more tiles per
+                                   # workgroup, ragged last tile); 4 rows with 2 tiles per
+                                   # workgroup stay on the per-wave kernel
+                                   (4, 1024, 16400), (3, 512, 20008), (4, 2048, 6150)])
 def test_qgemv_small(m, k, n, asym):
     run_case(m, k, n, asym, seed=m * 1000 + n)
 

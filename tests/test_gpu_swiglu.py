@@ -104,8 +104,10 @@ def _check_small(h, ref, what):
                                    (4, 2048, 200), (2, 8192, 17), (5, 512, 48), (9, 4096, 300),
                                    (16, 8192, 64), (16, 1536, 1),
                                    # x staged in LDS: 2 channel tiles per workgroup with a ragged
-                                   # last tile; 2 units per wave with an empty last one
-                                   (16, 2048, 5000), (7, 1024, 9000)])
+                                   # last tile; 2 units per wave with an empty last one; 3 and 4
+                                   # rows with 4 tiles per workgroup (ragged last workgroup)
+                                   (16, 2048, 5000), (7, 1024, 9000), (3, 512, 12400),
+                                   (4, 1024, 12600)])
 def test_qgemv_swiglu_small(m, k, i, asym):
     dev = device()
     fmt = "int4_asym" if asym else "int4_sym"
