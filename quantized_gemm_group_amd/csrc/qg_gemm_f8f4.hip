@@ -13,11 +13,14 @@
 // scale, so 2^(ea + eb) is applied inside the matrix core and the epilogue
 // only rounds.
 //
-// Tiling: a 512-thread workgroup owns a 256x256 output tile and its 8 waves
-// a 128 (tokens) x 64 (channels) piece each (2x4 tiles of
+// Tiling: a workgroup owns a 256x256 output tile.  MXFP4 (and FP8 with a
+// K tail): 8 waves of 128 (tokens) x 64 (channels) each (2x4 tiles of
 // v_mfma_scale_f32_32x32x64_f8f6f4, 128 fp32 accumulators per lane), two
 // waves per SIMD so that one wave's fragment reads and barrier waits hide
-// behind the other's matrix work.
+// behind the other's matrix work.  FP8 with whole k-steps: 4 waves of 128 x
+// 128 (4x4 tiles, 256 accumulators per lane in AGPRs), one per SIMD: each
+// A fragment read from LDS feeds four matrix instructions instead of two,
+// which takes a third off the LDS reads per k-step.
 //
 // Operand pipeline: a k-step covers 64 bytes of every operand row (64 FP8 or
 // 128 FP4 codes).  Operand tiles go from HBM straight into LDS with buffer
@@ -50,8 +53,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BM = 256, BN = 256;   // workgroup tile
 constexpr int BK = 64;              // bytes of each operand row per k-step
 constexpr int kStages = 4;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+// Two wave layouts of the 256x256 tile: 8 waves of 128 (tokens) x 64
+// (channels), two per SIMD, or (W4) 4 waves of 128 x 128, one per SIMD,
+// with their 256 accumulators in AGPRs: each fragment read from LDS then
+// feeds twice the matrix instructions.
+template <bool W4> struct Layout {
+  static constexpr int kWaves = W4 ? 4 : 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRW = 256 / kWaves;        // tile rows each wave loads per operand
+  static constexpr int kNP = kRW / 8;             // 1 KiB operand pieces per wave and pair
+  static constexpr int NT = W4 ? 4 : 2;           // 32-channel W tiles per wave
+  static constexpr int kWN = 32 * NT;             // channels per wave
+  static constexpr int kEpiPitch = kWN * 2 + 16;  // bf16 staging row pitch (bytes)
+  static constexpr int kEpiBytes = kWaves * 128 * kEpiPitch;
+  static constexpr int kExpPieces = 512 / 16 / kWaves;   // 16-row exponent chunks per wave
+};
 constexpr int kOpBytes = BM * BK;   // one operand, one stage: 16 KiB
 constexpr int kStageBytes = 2 * kOpBytes;
 // The ring holds pairs of k-steps (even, odd) as double stages: each operand
@@ -60,10 +76,9 @@ constexpr int kStageBytes = 2 * kOpBytes;
 constexpr int kPRow = 2 * BK;             // 128 bytes per row and pair
 constexpr int kDOpBytes = BM * kPRow;     // one operand, one pair: 32 KiB
 constexpr int kDStageBytes = 2 * kDOpBytes;
-// epilogue: each wave's 128 (m) x 64 (n) bf16 piece with a 144-byte row pitch
-// (8-byte LDS writes of 32 rows spread over the banks, 16-byte aligned reads)
-constexpr int kEpiPitch = 144;
-constexpr int kEpiBytes = kWaves * 128 * kEpiPitch;
+// epilogue: each wave's 128 (m) x 64 (n) (W4: 128 x 128) bf16 piece with a
+// 144- (272-) byte row pitch (8-byte LDS writes of 32 rows spread over the
+// banks, 16-byte aligned reads)
 
 // Tile of workgroup `bid`: XCD-contiguous ranges (when the tile count divides
 // evenly over the XCDs), then column groups of 4 tile rows.
@@ -76,13 +91,13 @@ __device__ __forceinline__ void xcd_tile(int bid, int tiles_m, int tiles_n, int*
 }
 
 
-template <bool MX, bool SALIGN> struct Frags;
-template <bool SALIGN> struct Frags<false, SALIGN> {
-  i32x8 a[4], w[2];                       // [A tile], [W tile]: 32 codes each
+template <bool MX, int NT> struct Frags;
+template <int NT> struct Frags<false, NT> {
+  i32x8 a[4], w[NT];                      // [A tile], [W tile]: 32 codes each
 };
-template <bool SALIGN> struct Frags<true, SALIGN> {
-  i32x4 a[2][4], w[2][2];                 // [sub-step][tile]: 32 codes each
-  uint32_t as[4], ws[2];                  // exponent dword of each row, >> 8 lh
+template <int NT> struct Frags<true, NT> {
+  i32x4 a[2][4], w[2][NT];                // [sub-step][tile]: 32 codes each
+  uint32_t as[4], ws[NT];                 // exponent dword of each row, >> 8 lh
 };
 
 // Wait until at most N vector-memory loads of this wave are outstanding and
@@ -104,8 +119,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // u = 0 and u = 1 of wave (wm, wn) hold gate and up of the same 32 channels
 // and each lane forms h = SiLU(s_x s_g g) * (s_x s_u u) of its own
 // accumulators.  Y is then h [M][I].
-template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false>
-__global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
+template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false, bool W4 = false>
+__global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
                                                              const void* __restrict__ a_aux, int M,
                                                              const uint8_t* __restrict__ W,
                                                              const void* __restrict__ w_aux, int N,
@@ -114,6 +129,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // of all 512 tile rows in one of 3 slots, see issue_exp.  Otherwise per
   // row and k-step 4 bytes loaded one by one beside the operands, each
   // landing zero-extended in a dword of its own, in every ring stage.
+  using LY = Layout<W4>;
+  static_assert(LY::kThreads == (W4 ? 256 : 512), "launch bound of the layout");
+  constexpr int kWaves = LY::kWaves, kRW = LY::kRW, kNP = LY::kNP, NT = LY::NT, kWN = LY::kWN;
+  constexpr int kEpiPitch = LY::kEpiPitch, kEpiBytes = LY::kEpiBytes;
+  static_assert(!W4 || KFULL, "the 4-wave layout takes whole k-steps");
+  static_assert(!W4 || !MX || SALIGN, "the 4-wave layout takes grouped exponents");
   constexpr bool kGrouped = MX && SALIGN;
   constexpr int kSWords = (MX && !SALIGN) ? 4 : 0;
   constexpr int kScaleStage = (BM + BN) * 4 * kSWords;
@@ -125,9 +146,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   constexpr int kEpiScales = MX ? 0 : 2 * 1024;
   static_assert(MX || kRing + kEpiScales <= kEpiBytes, "epilogue scales within the staging area");
   constexpr int kLds = kRing + kEpiScales > kEpiBytes ? kRing + kEpiScales : kEpiBytes;
-  // loads per wave per k-step beside the grouped exponent loads: 4 operand
+  // loads per wave per k-step beside the grouped exponent loads: kNP operand
   // blocks of 1 KiB + per-k-step exponent loads
-  constexpr int kGroup = 4 + kSWords;
+  constexpr int kGroup = kNP + kSWords;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   uint8_t* const sscale = smem + kStages * kStageBytes;
 
@@ -159,20 +180,29 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // chunk (i & 7) ^ ((row >> 1) & 7) = (i & 7) ^ (4 (j & 1) + (i >> 4)),
   // which lands at LDS position i of the piece.  Piece j's row offset goes
   // into the scalar offset, so two voffsets per operand (by j & 1) suffice.
+  // W4: a wave's 64 rows are two runs of 32 (h = j / 4), each addressed from
+  // its own base (the SwiGLU row map is not linear across them).
+  // Local arrays are sized for the larger layout (the 8-wave one leaves the
+  // rest untouched): bounds that depend on the template arguments left the
+  // host compilation pass without the kernel's launch stub.
+  static_assert(kRW <= 64 && NT <= 4, "array bounds below");
   int pchunk[2];
-  uint32_t voa[2], vow[2];
+  uint32_t voa[4], vow[4];                        // [2 h + jp]
 #pragma unroll
-  for (int jp = 0; jp < 2; ++jp) {
-    pchunk[jp] = (lane & 7) ^ (4 * jp + (lane >> 4));
-    const int r = 32 * wave + (lane >> 3);
-    // SwiGLU: rows 32 w .. 32 w + 31 of the tile are the gate (w even) or
-    // up (w odd) rows of channels c0 + 32 (w / 2) + 0..31; gate rows past I
-    // read up rows and up rows past N read zero, both for channels that are
-    // never stored
-    const int wrow = SWIGLU ? (wave & 1) * I + c0 + 32 * (wave >> 1) + (lane >> 3) : n0 + r;
-    voa[jp] = (uint32_t)(m0 + r) * kbytes + pchunk[jp] * 16;
-    vow[jp] = (uint32_t)wrow * kbytes + pchunk[jp] * 16;
-  }
+  for (int h = 0; h < kRW / 32; ++h)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      pchunk[jp] = (lane & 7) ^ (4 * jp + (lane >> 4));
+      const int r = kRW * wave + 32 * h + (lane >> 3);
+      // SwiGLU: tile rows 32 q .. 32 q + 31 are the gate (q even) or up (q
+      // odd) rows of channels c0 + 32 (q / 2) + 0..31; gate rows past I read
+      // up rows and up rows past N read zero, both for channels that are
+      // never stored
+      const int q = r >> 5;
+      const int wrow = SWIGLU ? (q & 1) * I + c0 + 32 * (q >> 1) + (r & 31) : n0 + r;
+      voa[2 * h + jp] = (uint32_t)(m0 + r) * kbytes + pchunk[jp] * 16;
+      vow[2 * h + jp] = (uint32_t)wrow * kbytes + pchunk[jp] * 16;
+    }
   // Exponent loads (MX): wave w brings the exponents of tile rows 64 w .. +63
   // (rows 0..255 of A, then 256..511 of W).  Grouped: lane l reads dword
   // l / 16 (k-step) of row l % 16 of a 16-row chunk, so one load touches 16
@@ -181,9 +211,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   __amdgpu_buffer_rsrc_t rsx = make_rsrc(a_aux, 0);
   uint32_t vos = 0;
   if constexpr (MX) {
-    const bool wop = wave >= 4;
+    const bool wop = wave >= kWaves / 2;
     rsx = make_rsrc(wop ? w_aux : a_aux, (int64_t)(wop ? N : M) * kblocks);
-    const int grow = (wop ? n0 : m0) + 64 * (wave & 3) + (kGrouped ? (lane & 15) : lane);
+    const int grow = (wop ? n0 : m0) + 2 * kRW * (wave % (kWaves / 2)) +
+                     (kGrouped ? (lane & 15) : lane);
     vos = (uint32_t)grow * kblocks + (kGrouped ? 4 * (lane >> 4) : 0);
   }
 
@@ -192,23 +223,23 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // operand loads of the two k-steps cover both operands' 4 pieces; then the
   // per-k-step exponent loads (MX, K not a multiple of 128).
   auto issue_piece = [&](int k, int d) {
-    if (d < 4) {
+    if (d < kNP) {
       const int pk = k >> 1;
       uint8_t* sD = smem + (pk & 1) * kDStageBytes + (d & 1) * kDOpBytes;
       const int j = 2 * (d >> 1) + (k & 1);
-      const int jp = j & 1;
+      const int jp = j & 1, h = j >> 2;
       const bool kin = KFULL || pk * kPRow + pchunk[jp] * 16 < kbytes;   // K tail: whole chunks
-      const int soff = pk * kPRow + 8 * j * kbytes;
-      lds_void* dst = (lds_void*)(sD + (32 * wave + 8 * j) * kPRow);
+      const int soff = pk * kPRow + 8 * (j & 3) * kbytes;
+      lds_void* dst = (lds_void*)(sD + (kRW * wave + 8 * j) * kPRow);
       if (d & 1)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, kin ? vow[jp] : kOutOfRange, soff, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, kin ? vow[2 * h + jp] : kOutOfRange, soff,
+                                                 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, kin ? voa[jp] : kOutOfRange, soff, 0,
-                                                 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, kin ? voa[2 * h + jp] : kOutOfRange, soff,
+                                                 0, 0);
     } else if constexpr (MX && !SALIGN) {
       const int st = k & (kStages - 1);
-      const int j = d - 4;
+      const int j = d - kNP;
       uint8_t* ss = sscale + st * kScaleStage;
       lds_void* dst = (lds_void*)(ss + (j * 512 + 64 * wave) * 4);
       const uint32_t vo = k * 4 + j < kblocks ? vos + j : kOutOfRange;
@@ -227,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // latest, before the reads of k-step 4 g + 8.
   auto issue_exp = [&](int G, int p) {
     if constexpr (kGrouped) {
-      uint8_t* dst = sscale + (G % 3) * kExpSlot + (4 * wave + p) * kChunk;
+      uint8_t* dst = sscale + (G % 3) * kExpSlot + (LY::kExpPieces * wave + p) * kChunk;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_void*)dst, 4, vos,
                                                p * 16 * kblocks + G * 16, 0, 0);
     }
@@ -248,15 +279,16 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     for (int c = 0; c < 2; ++c) {
       const int ch = (4 * h + (MX ? 2 * c + lh : 2 * lh + c)) ^ ((l32 >> 1) & 7);
       offA[h][c] = (wm * 128 + l32) * kPRow + (ch << 4);
-      offW[h][c] = kDOpBytes + (wn * 64 + l32) * kPRow + (ch << 4);
+      offW[h][c] = kDOpBytes + (wn * kWN + l32) * kPRow + (ch << 4);
     }
 
-  typedef Frags<MX, SALIGN> frags_t;
+  typedef Frags<MX, NT> frags_t;
   // Fragment reads of k-step k, in the order the MFMAs consume them: entry
-  // e of kOrd is A tile e (e < 4) or W tile e - 4.
-  constexpr int kOrd[6] = {4, 0, 1, 2, 3, 5};
+  // e of kOrd is A tile e (e < 4) or W tile e - 4 (the first 4 + NT entries).
+  constexpr int kOrd[8] = {4, 0, 1, 2, 3, 5, 6, 7};
+  constexpr int kTiles = 4 + NT;                    // fragment tiles per k-step
   constexpr int kEWords = kGrouped ? 1 : kSWords;   // exponent reads per row and k-step
-  constexpr int kReads = MX ? 12 + 6 * kEWords : 12;
+  constexpr int kReads = MX ? 2 * kTiles + kTiles * kEWords : 2 * kTiles;
   auto read_piece = [&](int k, frags_t& f, int p, auto hpar) {
     constexpr int H = decltype(hpar)::value;   // k & 1
     const int st = k & (kStages - 1);
@@ -272,11 +304,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[4 * h + i] = (int)v[i];
     } else {
-      if (p < 6 * kEWords) {
-        // exponents first: row entry p / kEWords (A rows 0..3, W rows 4..5)
+      if (p < kTiles * kEWords) {
+        // exponents first: row entry p / kEWords (A rows 0..3, W rows 4..)
         const int e = p / kEWords, j = p % kEWords;
         const bool isw = e >= 4;
-        const int r0 = isw ? 256 + wn * 64 + (e - 4) * 32 : wm * 128 + e * 32;
+        const int r0 = isw ? 256 + wn * kWN + (e - 4) * 32 : wm * 128 + e * 32;
         uint32_t& dst = isw ? f.ws[e - 4] : f.as[e];
         uint32_t v;
         if constexpr (kGrouped) {
@@ -294,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
         if (j == kEWords - 1) dst >>= 8 * lh;
       } else {
         // sub-step s: the lane holds block 2 s + lh of the k-step (16 bytes)
-        const int q = p - 6 * kEWords;
-        const int sub = q / 6, e = kOrd[q % 6];
+        const int q = p - kTiles * kEWords;
+        const int sub = q / kTiles, e = kOrd[q % kTiles];
         const bool isw = e >= 4;
         const i32x4 v = *reinterpret_cast<const i32x4*>(
             sA + (isw ? offW[H][sub] + (e - 4) * 32 * kPRow : offA[H][sub] + e * 32 * kPRow));
@@ -307,20 +339,21 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     }
   };
 
-  // 2 x 4 tiles of 32x32 per wave (64 channels x 128 rows), D[n][m] in 16
-  // fp32 per lane
-  f32x16 acc[2][4];
+  // NT x 4 tiles of 32x32 per wave (32 NT channels x 128 rows), D[n][m] in
+  // 16 fp32 per lane
+  f32x16 acc[4][4];                               // [u < NT][t]
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // MFMA i of k-step k: tile (u, t) = ((i / 4) % 2, i % 4); MX sub-step i / 8
-  constexpr int kMfma = MX ? 16 : 8;
+  // MFMA i of k-step k: tile (u, t) = ((i / 4) % NT, i % 4); MX sub-step
+  // i / (4 NT)
+  constexpr int kMfma = (MX ? 2 : 1) * 4 * NT;
   auto mma_piece = [&](const frags_t& f, int k, int i) {
-    const int u = (i >> 2) & 1, t = i & 3;
+    const int u = (i >> 2) % NT, t = i & 3;
     if constexpr (!MX) {
       acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[u], f.a[t], acc[u][t], 0, 0,
                                                                   0, 127, 0, 127);
@@ -328,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
       // the scale operands are the exponent dwords with byte 2 s selected;
       // blocks past K (last k-step, K not a multiple of 128) have zero codes
       // and zero exponent bytes, so their products are zero
-      const int sub = i >> 3;
+      const int sub = i / (4 * NT);
       const i32x8 wf = i32x8{f.w[sub][u][0], f.w[sub][u][1], f.w[sub][u][2], f.w[sub][u][3], 0, 0, 0, 0};
       const i32x8 af = i32x8{f.a[sub][t][0], f.a[sub][t][1], f.a[sub][t][2], f.a[sub][t][3], 0, 0, 0, 0};
       if (sub == 0)
@@ -352,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // flight; at an odd step the pair holding k + 1 is waited for entirely.
   // Grouped exponents: every odd step also issues two exponent pieces after
   // its operand loads, so an even step lets those 10 loads stay in flight.
-  constexpr int kExpPer = kGrouped ? 2 : 0;
+  constexpr int kExpPer = kGrouped ? LY::kExpPieces / 2 : 0;
   constexpr int kReadsPer = (kReads + (3 * kMfma / 4) - 1) / (3 * kMfma / 4);
   constexpr int kLoadsPer = (2 * kGroup + kExpPer + kMfma - 1) / kMfma;
   auto step = [&](int k, frags_t& cur, frags_t& nxt, auto odd_t) {
@@ -372,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
           if (x < 2 * kGroup)
             issue_piece(k + 3 + (x & 1), x >> 1);
           else if (x < 2 * kGroup + kExpPer)   // group (k - 1) / 4 + 2, pieces 2 ((k >> 1) & 1) + 0, 1
-            issue_exp(((k - 1) >> 2) + 2, 2 * ((k >> 1) & 1) + (x - 2 * kGroup));
+            issue_exp(((k - 1) >> 2) + 2, kExpPer * ((k >> 1) & 1) + (x - 2 * kGroup));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -380,32 +413,38 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   };
 
   // FP8: the epilogue's scales go first (they retire before the operands
-  // the first wait is for).  Wave w brings 64 dwords: s_x of tile rows
-  // 64 w .. (w < 4), else s_w of tile channels 64 (w - 4) .. (SwiGLU: gate
-  // channels c0 .., then the same channels' up rows); out of range reads 0.
+  // the first wait is for).  The first half of the waves bring s_x of the
+  // 256 tile rows, the second half s_w of the 256 tile channels (SwiGLU:
+  // gate channels c0 .., then the same channels' up rows), 64 dwords per
+  // load; out of range reads 0.
   float* const sepi = reinterpret_cast<float*>(smem + kRing);
   if constexpr (!MX) {
-    const bool wsc = wave >= 4;
-    const int q = 64 * (wave & 3) + lane;
-    int row;
-    if (!wsc)
-      row = m0 + q;
-    else if constexpr (SWIGLU)
-      row = (q >> 7) * I + c0 + (q & 127);
-    else
-      row = n0 + q;
+    constexpr int kSL = 512 / 64 / kWaves;          // 64-dword loads per wave
+    const bool wsc = wave >= kWaves / 2;
     const __amdgpu_buffer_rsrc_t rsc =
         make_rsrc(wsc ? w_aux : a_aux, (int64_t)(wsc ? N : M) * 4);
-    const bool ok = SWIGLU && wsc ? c0 + (q & 127) < I : true;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_void*)(sepi + 256 * wsc + 64 * (wave & 3)), 4,
-                                             ok ? (uint32_t)row * 4 : kOutOfRange, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < kSL; ++h) {
+      const int q0 = 64 * (kSL * (wave % (kWaves / 2)) + h);
+      const int q = q0 + lane;
+      int row;
+      if (!wsc)
+        row = m0 + q;
+      else if constexpr (SWIGLU)
+        row = (q >> 7) * I + c0 + (q & 127);
+      else
+        row = n0 + q;
+      const bool ok = SWIGLU && wsc ? c0 + (q & 127) < I : true;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_void*)(sepi + 256 * wsc + q0), 4,
+                                               ok ? (uint32_t)row * 4 : kOutOfRange, 0, 0, 0);
+    }
   }
   // prologue: k-steps 0..3 in two interleaved pairs (grouped exponents:
   // group 0 before them, group 1 after); stage 0 (all of the first pair)
   // must land before its fragments are read
   if constexpr (kGrouped) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) issue_exp(0, p);
+    for (int p = 0; p < LY::kExpPieces; ++p) issue_exp(0, p);
   }
 #pragma unroll
   for (int k0 = 0; k0 < 4; k0 += 2)
@@ -413,9 +452,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
     for (int x = 0; x < 2 * kGroup; ++x) issue_piece(k0 + (x & 1), x >> 1);
   if constexpr (kGrouped) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) issue_exp(1, p);
+    for (int p = 0; p < LY::kExpPieces; ++p) issue_exp(1, p);
   }
-  wait_vm_barrier<2 * kGroup + (kGrouped ? 4 : 0)>();
+  wait_vm_barrier<2 * kGroup + (kGrouped ? LY::kExpPieces : 0)>();
   frags_t f0, f1;
 #pragma unroll
   for (int p = 0; p < kReads; ++p) read_piece(0, f0, p, std::integral_constant<int, 0>{});
@@ -435,54 +474,62 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   // 16-byte pieces that fill whole cache lines (stores straight from the
   // accumulators, 32 bytes of 32 rows per instruction, measured 15 % slower
   // for the FP8 and 37 % for the MXFP4 product).
-  f32x4 swv[2][4];
+  f32x4 swv[4][4];                                // [u < NT][b]
   float sxv[4];
   if constexpr (!MX) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) sxv[t] = sepi[wm * 128 + t * 32 + l32];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int q = SWIGLU ? u * 128 + wn * 32 + 8 * b + 4 * lh : wn * 64 + u * 32 + 8 * b + 4 * lh;
+        // SwiGLU: W tile u holds the gate (u even) or up (u odd) rows of
+        // channels wn kWN / 2 + 32 (u / 2) .. of the tile
+        const int q = SWIGLU ? (u & 1) * 128 + wn * (kWN / 2) + 32 * (u >> 1) + 8 * b + 4 * lh
+                             : wn * kWN + u * 32 + 8 * b + 4 * lh;
         swv[u][b] = *reinterpret_cast<const f32x4*>(sepi + 256 + q);
       }
   }
   __syncthreads();   // every wave is done with the operand buffers
   if constexpr (SWIGLU) {
     // h = SiLU(g) * u per lane (fp32, e^-g from the hardware exponential),
-    // staged as the wave's 128 (m) x 32 (channel) bf16 piece with an 80-byte
-    // row pitch, then 16 rows per store instruction (4 lanes x 16 bytes)
-    constexpr int kHPitch = 80;
+    // staged as the wave's 128 (m) x kWN / 2 (channel) bf16 piece with a
+    // 16-byte pad per row, then whole rows per store instruction (kLR lanes
+    // x 16 bytes a row)
+    constexpr int kHC = kWN / 2;                    // channels of h per wave
+    constexpr int kHPitch = kHC * 2 + 16;
+    constexpr int kLR = kHC / 8;                    // lanes per staged row
     uint8_t* sh = smem + wave * (128 * kHPitch);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int pp = 0; pp < NT / 2; ++pp)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float v[4];
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float g = acc[0][t][4 * b + r] * (sxv[t] * swv[0][b][r]);
-          const float u = acc[1][t][4 * b + r] * (sxv[t] * swv[1][b][r]);
-          v[r] = g / (1.f + __expf(-g)) * u;
+        for (int b = 0; b < 4; ++b) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float g = acc[2 * pp][t][4 * b + r] * (sxv[t] * swv[2 * pp][b][r]);
+            const float u = acc[2 * pp + 1][t][4 * b + r] * (sxv[t] * swv[2 * pp + 1][b][r]);
+            v[r] = g / (1.f + __expf(-g)) * u;
+          }
+          const int ml = t * 32 + l32, nl = 32 * pp + 8 * b + 4 * lh;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + wm * 128 + ml, c = c0 + wn * kHC + nl + r;
+            if (m < M && c < I) QG_DEBUG_STORE((int64_t)m * I + c, v[r]);
+          }
+          *reinterpret_cast<uint2*>(sh + ml * kHPitch + nl * 2) =
+              make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
         }
-        const int ml = t * 32 + l32, nl = 8 * b + 4 * lh;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * 128 + ml, c = c0 + wn * 32 + nl + r;
-          if (m < M && c < I) QG_DEBUG_STORE((int64_t)m * I + c, v[r]);
-        }
-        *reinterpret_cast<uint2*>(sh + ml * kHPitch + nl * 2) =
-            make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
-      }
     __syncthreads();
-    const int cbase = c0 + wn * 32 + (lane & 3) * 8;
+    const int cbase = c0 + wn * kHC + (lane % kLR) * 8;
     const bool full_c = cbase + 7 < I && (I & 7) == 0;
 #pragma unroll 4
-    for (int i = 0; i < 8; ++i) {
-      const int ml = 16 * i + (lane >> 2);
+    for (int i = 0; i < 128 * kLR / 64; ++i) {
+      const int ml = (64 / kLR) * i + lane / kLR;
       const int m = m0 + wm * 128 + ml;
-      const u32x4 o = *reinterpret_cast<const u32x4*>(sh + ml * kHPitch + (lane & 3) * 16);
+      const u32x4 o = *reinterpret_cast<const u32x4*>(sh + ml * kHPitch + (lane % kLR) * 16);
       if (m < M) {
         uint16_t* ph = Y + (int64_t)m * I + cbase;
         if (full_c) {
@@ -500,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         float v[4];
@@ -512,21 +559,22 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
         const int ml = t * 32 + l32, nl = u * 32 + 8 * b + 4 * lh;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * 128 + ml, n = n0 + wn * 64 + nl + r;
+          const int m = m0 + wm * 128 + ml, n = n0 + wn * kWN + nl + r;
           if (m < M && n < N) QG_DEBUG_STORE((int64_t)m * N + n, v[r]);
         }
         *reinterpret_cast<uint2*>(so + ml * kEpiPitch + nl * 2) =
             make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
   __syncthreads();
-  // 8 rows per instruction, 8 lanes x 8 outputs per row
-  const int nbase = n0 + wn * 64 + (lane & 7) * 8;
+  // kLR lanes x 8 outputs per row (8 or 16), 64 / kLR rows per instruction
+  constexpr int kLR = kWN / 8;
+  const int nbase = n0 + wn * kWN + (lane % kLR) * 8;
   const bool full_n = nbase + 7 < N && (N & 7) == 0;
 #pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int ml = 8 * i + (lane >> 3);
+  for (int i = 0; i < 128 * kLR / 64; ++i) {
+    const int ml = (64 / kLR) * i + lane / kLR;
     const int m = m0 + wm * 128 + ml;
-    const u32x4 o = *reinterpret_cast<const u32x4*>(so + ml * kEpiPitch + (lane & 7) * 16);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(so + ml * kEpiPitch + (lane % kLR) * 16);
     if (m < M) {
       uint16_t* py = Y + (int64_t)m * N + nbase;
       if (full_n) {
@@ -541,12 +589,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f8f4_kernel(const uint8_t* __re
   }
 }
 
-template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false>
+template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false, bool W4 = false>
 hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, const void* w_aux,
                   int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int64_t tn = SWIGLU ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const int tiles = (int)(((M + BM - 1) / BM) * tn);
-  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN, KFULL, SWIGLU>), dim3(tiles), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((gemm_f8f4_kernel<MX, SALIGN, KFULL, SWIGLU, W4>), dim3(tiles),
+                     dim3(Layout<W4>::kThreads), 0, stream,
                      (const uint8_t*)a, a_aux, (int)M, (const uint8_t*)w, w_aux, (int)N, (int)K,
                      (uint16_t*)y);
   return hipGetLastError();
@@ -556,10 +605,14 @@ hipError_t launch(const void* a, const void* a_aux, int64_t M, const void* w, co
 
 QG_DEBUG_TU_SETTER(debug_set_f8f4)
 
+// FP8 with whole k-steps runs the 4-wave layout (8192^3 on MI355X: 375 ->
+// 369 us and 387 -> 381 us in A/Bs on two boxes); MXFP4 keeps 8 waves (the
+// 4-wave layout measured 131 -> 132.5 us).
 hipError_t launch_gemm_fp8(const void* a, const void* a_scales, int64_t M, const void* w,
                            const void* w_scales, int64_t N, int64_t K, void* y,
                            hipStream_t stream) {
-  if (K % BK == 0) return launch<false, true, true>(a, a_scales, M, w, w_scales, N, K, y, stream);
+  if (K % BK == 0)
+    return launch<false, true, true, false, true>(a, a_scales, M, w, w_scales, N, K, y, stream);
   return launch<false, true, false>(a, a_scales, M, w, w_scales, N, K, y, stream);
 }
 
@@ -567,7 +620,7 @@ hipError_t launch_gemm_fp8_swiglu(const void* a, const void* a_scales, int64_t M
                                   const void* w_scales, int64_t N2, int64_t K, void* h,
                                   hipStream_t stream) {
   if (K % BK == 0)
-    return launch<false, true, true, true>(a, a_scales, M, w, w_scales, N2, K, h, stream);
+    return launch<false, true, true, true, true>(a, a_scales, M, w, w_scales, N2, K, h, stream);
   return launch<false, true, false, true>(a, a_scales, M, w, w_scales, N2, K, h, stream);
 }
 
