@@ -114,10 +114,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // SWIGLU (FP8 only; 《推理优化与量化算子深度技术调研》 section 4.6, the W8A8 GEMM
 // with dequantization and activation fused): W is the [N][K] concatenation
 // [W_gate; W_up] (N = 2I) and a workgroup's 256 weight rows are 128 gate
-// channels and the same 128 up channels: wave w's 32 loaded rows are gate
-// (w even) or up (w odd) rows of channels c0 + 32 (w / 2) ..; so the W tiles
-// u = 0 and u = 1 of wave (wm, wn) hold gate and up of the same 32 channels
-// and each lane forms h = SiLU(s_x s_g g) * (s_x s_u u) of its own
+// channels and the same 128 up channels: tile rows 32 q .. 32 q + 31 are the
+// gate (q even) or up (q odd) rows of channels c0 + 32 (q / 2) ..; so the W
+// tiles u = 2 p and u = 2 p + 1 of a wave hold gate and up of the same 32
+// channels and each lane forms h = SiLU(s_x s_g g) * (s_x s_u u) of its own
 // accumulators.  Y is then h [M][I].
 template <bool MX, bool SALIGN, bool KFULL, bool SWIGLU = false, bool W4 = false>
 __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t* __restrict__ A,
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;     // A rows 128 wm.., W rows 64 wn..
+  const int wm = wave & 1, wn = wave >> 1;     // A rows 128 wm.., W rows kWN wn..
   const int l32 = lane & 31, lh = lane >> 5;
 
   static_assert(!(SWIGLU && MX), "the SwiGLU epilogue is for the FP8 product");
@@ -174,9 +174,10 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (int64_t)M * kbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (int64_t)N * kbytes);
 
-  // Operand loads, one pair of k-steps at a time: wave w brings rows 32 w ..
-  // 32 w + 31 of both operand tiles in 4 loads each (piece j: rows 32 w + 8 j
-  // .. + 7, whole 128-byte lines); lane i brings row 32 w + 8 j + i / 8,
+  // Operand loads, one pair of k-steps at a time: wave w brings rows kRW w
+  // .. kRW w + kRW - 1 (kRW = 32, or 64 in the 4-wave layout) of both operand
+  // tiles in kNP loads each (piece j: rows kRW w + 8 j .. + 7, whole 128-byte
+  // lines); lane i brings row kRW w + 8 j + i / 8,
   // chunk (i & 7) ^ ((row >> 1) & 7) = (i & 7) ^ (4 (j & 1) + (i >> 4)),
   // which lands at LDS position i of the piece.  Piece j's row offset goes
   // into the scalar offset, so two voffsets per operand (by j & 1) suffice.
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
       voa[2 * h + jp] = (uint32_t)(m0 + r) * kbytes + pchunk[jp] * 16;
       vow[2 * h + jp] = (uint32_t)wrow * kbytes + pchunk[jp] * 16;
     }
-  // Exponent loads (MX): wave w brings the exponents of tile rows 64 w .. +63
+  // Exponent loads (MX): wave w brings the exponents of tile rows 2 kRW w ..
   // (rows 0..255 of A, then 256..511 of W).  Grouped: lane l reads dword
   // l / 16 (k-step) of row l % 16 of a 16-row chunk, so one load touches 16
   // rows' cache lines instead of 64; otherwise one load per k-step and byte
@@ -251,8 +252,9 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
   // of 16 rows, chunk q at q * kChunk: dword 16 j + r' of a chunk holds k-step
   // j of row 16 q + r', so one k-step of 32 consecutive rows spans 32 banks
   // (the 64-byte skew per chunk shifts the second 16 rows by 16 banks).
-  // Piece p (0..3) of a group is chunk 4 w + p of wave w.  The pieces of
-  // group g + 2 go out two per odd step at steps 4 g + 1 and 4 g + 3; its slot
+  // Piece p (0 .. kExpPieces - 1) of a group is chunk kExpPieces w + p of
+  // wave w.  The pieces of group g + 2 go out half per odd step at steps
+  // 4 g + 1 and 4 g + 3; its slot
   // last held group g - 1, whose reads ended before the barrier of step
   // 4 g - 1.  They are waited for by the barrier of step 4 g + 5 at the
   // latest, before the reads of k-step 4 g + 8.
