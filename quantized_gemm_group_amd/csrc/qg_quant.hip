@@ -84,15 +84,46 @@ struct Stats {
   float amax, lo, hi;
 };
 
+// Only the statistics a format uses are formed and reduced: the range (lo,
+// hi) for the asymmetric kinds, the absolute maximum for the others; the
+// unused ones keep their identity values.
+template <int K>
+constexpr bool kRange = K == K_INT4_ASYM || K == K_INT8_ASYM;
+
+template <int K>
 __device__ __forceinline__ Stats stats_of(const float (&v)[8]) {
   Stats s{0.f, __builtin_inff(), -__builtin_inff()};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    s.amax = __builtin_fmaxf(s.amax, __builtin_fabsf(v[i]));
-    s.lo = __builtin_fminf(s.lo, v[i]);
-    s.hi = __builtin_fmaxf(s.hi, v[i]);
+    if constexpr (kRange<K>) {
+      s.lo = __builtin_fminf(s.lo, v[i]);
+      s.hi = __builtin_fmaxf(s.hi, v[i]);
+    } else {
+      s.amax = __builtin_fmaxf(s.amax, __builtin_fabsf(v[i]));
+    }
   }
   return s;
+}
+
+template <int K>
+__device__ __forceinline__ void merge(Stats& a, const Stats& b) {
+  if constexpr (kRange<K>) {
+    a.lo = __builtin_fminf(a.lo, b.lo);
+    a.hi = __builtin_fmaxf(a.hi, b.hi);
+  } else {
+    a.amax = __builtin_fmaxf(a.amax, b.amax);
+  }
+}
+
+// merge with the statistics of lane (lane ^ o)
+template <int K>
+__device__ __forceinline__ void merge_xor(Stats& a, int o) {
+  if constexpr (kRange<K>) {
+    a.lo = __builtin_fminf(a.lo, shfl_xor(a.lo, o));
+    a.hi = __builtin_fmaxf(a.hi, shfl_xor(a.hi, o));
+  } else {
+    a.amax = __builtin_fmaxf(a.amax, shfl_xor(a.amax, o));
+  }
 }
 
 struct Params {
@@ -243,12 +274,10 @@ __global__ __launch_bounds__(kThreads) void quant_wave_kernel(const void* __rest
 #pragma unroll
   for (int i = 0; i < kVpl; ++i) {
     const int64_t vec = base + 64 * i + lane;
-    Stats st = stats_of(v[i]);
+    Stats st = stats_of<K>(v[i]);
     // segments never straddle valid and invalid lanes (total_vecs % seg == 0)
     for (int o = 1; o < seg; o <<= 1) {
-      st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
-      st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
-      st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+      merge_xor<K>(st, o);
     }
     if (vec < total_vecs) {
       const Params p = make_params<K>(st);
@@ -284,15 +313,11 @@ __global__ __launch_bounds__(kThreads) void quant_rowwave_kernel(const void* __r
   Stats st{0.f, __builtin_inff(), -__builtin_inff()};
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const Stats s = stats_of(v[i]);
-    st.amax = __builtin_fmaxf(st.amax, s.amax);
-    st.lo = __builtin_fminf(st.lo, s.lo);
-    st.hi = __builtin_fmaxf(st.hi, s.hi);
+    const Stats s = stats_of<K>(v[i]);
+    merge<K>(st, s);
   }
   for (int o = 1; o < 64; o <<= 1) {
-    st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
-    st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
-    st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+    merge_xor<K>(st, o);
   }
   const Params p = make_params<K>(st);
 #pragma unroll
@@ -316,15 +341,11 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const void* __res
     float v[8];
     load_vec<BF16>(src, v0 + i, v);
     if (sm.s) apply_smooth(v, sm, c0 + (uint32_t)i);
-    const Stats s = stats_of(v);
-    st.amax = __builtin_fmaxf(st.amax, s.amax);
-    st.lo = __builtin_fminf(st.lo, s.lo);
-    st.hi = __builtin_fmaxf(st.hi, s.hi);
+    const Stats s = stats_of<K>(v);
+    merge<K>(st, s);
   }
   for (int o = 1; o < 64; o <<= 1) {
-    st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
-    st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
-    st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+    merge_xor<K>(st, o);
   }
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
@@ -335,9 +356,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const void* __res
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kThreads / 64; ++i) {
-    st.amax = __builtin_fmaxf(st.amax, red[0][i]);
-    st.lo = __builtin_fminf(st.lo, red[1][i]);
-    st.hi = __builtin_fmaxf(st.hi, red[2][i]);
+    merge<K>(st, Stats{red[0][i], red[1][i], red[2][i]});
   }
   const Params p = make_params<K>(st);
   for (int64_t i = threadIdx.x; i < t_vecs; i += kThreads) {
@@ -645,10 +664,8 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __rest
       v[i][e] = y;
     }
     if constexpr (K != K_MX) {
-      const Stats s = stats_of(v[i]);
-      st.amax = __builtin_fmaxf(st.amax, s.amax);
-      st.lo = __builtin_fminf(st.lo, s.lo);
-      st.hi = __builtin_fmaxf(st.hi, s.hi);
+      const Stats s = stats_of<K>(v[i]);
+      merge<K>(st, s);
     }
   }
   if constexpr (K == K_MX) {
@@ -681,9 +698,7 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __rest
     return;
   } else {
   for (int o = 1; o < 64; o <<= 1) {
-    st.amax = __builtin_fmaxf(st.amax, shfl_xor(st.amax, o));
-    st.lo = __builtin_fminf(st.lo, shfl_xor(st.lo, o));
-    st.hi = __builtin_fmaxf(st.hi, shfl_xor(st.hi, o));
+    merge_xor<K>(st, o);
   }
   const int w = tid >> 6;
   if ((tid & 63) == 0) {
@@ -694,9 +709,7 @@ __global__ __launch_bounds__(kThreads) void norm_quant_kernel(const void* __rest
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kThreads / 64; ++i) {
-    st.amax = __builtin_fmaxf(st.amax, red[0][i]);
-    st.lo = __builtin_fminf(st.lo, red[1][i]);
-    st.hi = __builtin_fmaxf(st.hi, red[2][i]);
+    merge<K>(st, Stats{red[0][i], red[1][i], red[2][i]});
   }
   const Params p = make_params<K>(st);
 #pragma unroll
