@@ -107,6 +107,15 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// The epilogue's staging pieces are private to their wave (each wave reads
+// back only rows it wrote), so between its LDS writes and reads a wave only
+// waits for its own LDS operations, which complete in order; no barrier.
+// (Against a workgroup barrier there: MXFP4 129.9 -> 128.9 us, FP8 unchanged,
+// outputs bit-identical.)
+__device__ __forceinline__ void wait_own_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // SALIGN (MX only): every row's exponents of a k-step are one aligned dword
 // (K a multiple of 128); otherwise its 4 bytes are loaded one by one.
 // KFULL: K fills whole k-steps, so no load needs a K-tail check (loads past
@@ -524,7 +533,7 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
           *reinterpret_cast<uint2*>(sh + ml * kHPitch + nl * 2) =
               make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
         }
-    __syncthreads();
+    wait_own_lds();
     const int cbase = c0 + wn * kHC + (lane % kLR) * 8;
     const bool full_c = cbase + 7 < I && (I & 7) == 0;
 #pragma unroll 4
@@ -567,7 +576,7 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
         *reinterpret_cast<uint2*>(so + ml * kEpiPitch + nl * 2) =
             make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
       }
-  __syncthreads();
+  wait_own_lds();
   // kLR lanes x 8 outputs per row (8 or 16), 64 / kLR rows per instruction
   constexpr int kLR = kWN / 8;
   const int nbase = n0 + wn * kWN + (lane % kLR) * 8;
