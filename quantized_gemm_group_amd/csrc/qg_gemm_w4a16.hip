@@ -66,7 +66,6 @@ constexpr int kStageBytes = kXBytes + kWBytes + 2 * kSBytes;
 constexpr int kSumBytes = BM * 16;        // four partial sums per X row
 constexpr int kSumBufs = 3;
 constexpr int kLdsBytes = kStages * kStageBytes + kSumBufs * kSumBytes;
-constexpr int kGroupLoads = 4 + 2 + 1;    // loads per wave per k-step
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 // Codes of one 32-bit word (elements 8 w .. 8 w + 7, element i in bits
@@ -107,11 +106,19 @@ struct Parity {
   static constexpr int value = V;
 };
 
-template <bool ASYM, bool SWIGLU>
+// SUB = 4: each workgroup covers one 32-token quarter of a 128 x 256 tile
+// (the tiles of a last, partly filled wave of workgroups, spread over every
+// CU); the four quarters of a tile run on one XCD so its codes come from
+// that XCD's L2.  lin0: linear index of the launch's first tile.
+template <bool ASYM, bool SWIGLU, int SUB = 1>
 __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ Wc,
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ Z, int N, int K,
-    uint16_t* __restrict__ Y, uint32_t mask, uint32_t cmag) {
+    uint16_t* __restrict__ Y, uint32_t mask, uint32_t cmag, int lin0) {
+  static_assert(SUB == 1 || SUB == 4, "whole tiles or quarters");
+  constexpr int BMS = BM / SUB;                    // token rows of the workgroup
+  constexpr int kXL = BMS / 32;                    // X loads (4 rows each) per wave and k-step
+  constexpr int kGroupLoads = kXL + 2 + 1;         // loads per wave per k-step
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
   uint8_t* const sums = smem + kStages * kStageBytes;
 
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   // Wave tile: 128 tokens x 32 weight rows (4 x 1 tiles of 32x32), so every
   // wave unpacks codes no other wave unpacks and uses each unpacked code for
   // four MFMAs.  SWIGLU: the 32 rows are 16 gate and the same 16 up channels.
-  constexpr int MT = 4, NT = 1;
+  constexpr int MT = BMS / 32, NT = 1;
   const int mrow0 = 0;                             // first X row of the wave tile
   const int nrow0 = 32 * wave;                     // first LDS code row
 
@@ -130,9 +137,18 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   const int NI = SWIGLU ? N / 2 : N;                 // output columns
   const int TN = SWIGLU ? BN / 2 : BN;               // output columns per tile
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (NI + TN - 1) / TN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, 8, &tm, &tn);
-  const int m0 = tm * BM, n0 = tn * TN;
+  int tm, tn, lin = lin0 + (int)blockIdx.x, quarter = 0;
+  if constexpr (SUB > 1) {
+    // unit u = SUB * (tile - lin0) + quarter; XCD x (blocks x, x + 8, ...)
+    // takes a contiguous range of units when the count divides by 8
+    const int units = (int)gridDim.x;
+    const int u = units % 8 == 0 ? ((int)blockIdx.x % 8) * (units / 8) + (int)blockIdx.x / 8
+                                 : (int)blockIdx.x;
+    lin = lin0 + u / SUB;
+    quarter = u % SUB;
+  }
+  tile_coords(lin, tiles_m, tiles_n, 8, &tm, &tn);
+  const int m0 = tm * BM + quarter * BMS, n0 = tn * TN;
   // weight row of LDS tile row r (0..255); SWIGLU: rows 32 w .. 32 w + 15
   // are gate channels n0 + 16 w .., rows 32 w + 16 .. their up channels
   auto wrow = [&](int r) {
@@ -155,8 +171,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   // which keeps the counts equal).
   uint32_t vx[4], vw[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 16 * wave + 4 * q + (lane >> 4);
+  for (int q = 0; q < kXL; ++q) {
+    const int r = 4 * kXL * wave + 4 * q + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
     vx[q] = (uint32_t)(m0 + r) * (uint32_t)(K * 2) + c * 16;
   }
@@ -177,9 +193,9 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     uint8_t* st = smem + stage * kStageBytes;
     const int gl = g < G ? g : G - 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + (16 * wave + 4 * q) * XROW), 16,
-                                               vx[q], gl * XROW, 0, 0);
+    for (int q = 0; q < kXL; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(st + (4 * kXL * wave + 4 * q) * XROW),
+                                               16, vx[q], gl * XROW, 0, 0);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -193,7 +209,10 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
 
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                          0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  f32x16 yacc[MT][NT];
+  // (bounds fixed at the largest MT: bounds that depend on the template
+  // arguments left the host compilation pass without the launch stub)
+  static_assert(MT <= 4 && NT == 1, "array bounds below");
+  f32x16 yacc[4][1];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -211,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   // channel as the second); without `pair` group g0 + 1 does not exist.
   auto cross = [&](int g0, bool pair) {
     const uint8_t* sb = sums + ((g0 + lh) % kSumBufs) * kSumBytes;
-    float sx[MT];
+    float sx[4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const u32x4 p = *reinterpret_cast<const u32x4*>(sb + (mrow0 + 32 * mt + l32) * 16);
@@ -243,8 +262,9 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     if (P == 0 && g >= 2) cross(g - 2, true);
 
     // this wave's share of the row sums of group g: rows 16 w .. 16 w + 15,
-    // four lanes a row, each one of four partial sums of 32 k
-    {
+    // four lanes a row, each one of four partial sums of 32 k (a quarter
+    // tile: the first two waves)
+    if (SUB == 1 || wave < BMS / 16) {
       const int r = 16 * wave + (lane >> 2);
       const int part = lane & 3;
       const int c0 = 4 * part;
@@ -280,10 +300,10 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
       scp[P][nt] = sv[nt] * c;
     }
 
-    f32x16 gacc[MT][NT];
+    f32x16 gacc[4][1];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      bf16x8 a[MT];
+      bf16x8 a[4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = mrow0 + mt * 32 + l32;
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   constexpr int kChunks = (SWIGLU ? BN / 2 : BN) / 8;   // 16-byte pieces per row
   const bool vec_ok = (NI & 7) == 0;
 #pragma unroll 4
-  for (int c = tid; c < BM * kChunks; c += kThreads) {
+  for (int c = tid; c < BMS * kChunks; c += kThreads) {
     const int ml = c / kChunks, cn = c - ml * kChunks;
     const int m = m0 + ml, n = n0 + cn * 8;
     if (m >= M || n >= NI) continue;
@@ -399,15 +419,44 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   }
 }
 
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+// One workgroup per CU at a time (the LDS holds one), so the tiles run in
+// waves of `cus`.  When the last wave would fill at most a quarter of the
+// CUs, its tiles go to a second launch in 32-token quarters, four per tile
+// (each quarter unpacks the tile's codes again for a quarter of the matrix
+// work, but all CUs take part).  Qwen2.5-72B up projection (1856 tiles, 7.25
+// waves): 1055 -> 1034 us, the SwiGLU gate+up 1086 -> 1056 us (medians of
+// three A/B pairs on one box); outputs bit-identical.
 template <bool ASYM, bool SWIGLU>
 void launch_t(const void* x, int64_t M, const void* wcodes, const void* wscales,
               const void* wzeros, int64_t N, int64_t K, void* y, hipStream_t stream) {
   const int64_t tn = SWIGLU ? (N / 2 + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   const int tiles = (int)(((M + BM - 1) / BM) * tn);
-  hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU>), dim3(tiles), dim3(kThreads), 0, stream,
+  const int cus = device_cus();
+  const int rest = cus > 0 ? tiles % cus : 0;
+  const int full = (rest > 0 && tiles > cus && 4 * rest <= cus) ? tiles - rest : tiles;
+  const uint32_t cmag = ASYM ? 0x43004300u : 0x43084308u;
+  hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU>), dim3(full), dim3(kThreads), 0, stream,
                      (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
                      (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
-                     (uint16_t*)y, 0x000F000Fu, ASYM ? 0x43004300u : 0x43084308u);
+                     (uint16_t*)y, 0x000F000Fu, cmag, 0);
+  if (full < tiles)
+    hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU, 4>), dim3(4 * (tiles - full)),
+                       dim3(kThreads), 0, stream, (const uint16_t*)x, (int)M,
+                       (const uint32_t*)wcodes, (const uint16_t*)wscales,
+                       (const uint16_t*)wzeros, (int)N, (int)K, (uint16_t*)y, 0x000F000Fu, cmag,
+                       full);
 }
 
 }  // namespace

@@ -237,6 +237,32 @@ def test_w4a16_gemm_small(m, k, n, asym):
 
 
 @pytest.mark.parametrize("asym", [False, True])
+def test_w4a16_gemm_last_wave_quarters(asym):
+    # 3 x 90 = 270 tiles of 128 x 256: on a 256-CU GPU 256 whole tiles run
+    # first and the last 14 as 32-token quarters (the last row tile is ragged,
+    # 44 rows: one full and one partial quarter, two empty).  Against the
+    # oracle, and bit for bit against each 128-row slice computed alone (one
+    # partly filled wave, whole tiles): every output is the same arithmetic.
+    dev = device()
+    m, k, n = 300, 512, 23040
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"w4a16 gemm last-wave quarters m={m} k={k} n={n} {fmt}", flush=True)
+    c = small_case(m, k, n, seed=5 + asym, w_outlier=(0.01, 20.0))
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
+    if asym:
+        q, s, z = oi.quantize_asym(c["w"], 128)
+    else:
+        (q, s), z = oi.quantize_sym(c["w"], 128), None
+    packed = oi.pack_int4(q)
+    x = to_dev(c["x"], dev)
+    y = qg.qgemm(x, codes, scales, zeros, fmt, "bf16")
+    check(host(y), og.w4a16_reference(bf16_as_f32(c["x"]), packed, s, z, 128), f"w4a16 {fmt}")
+    for r0 in (0, 128, 256):
+        part = qg.qgemm(x[r0:r0 + 128].contiguous(), codes, scales, zeros, fmt, "bf16")
+        assert torch.equal(part.view(torch.int16), y[r0:r0 + 128].view(torch.int16)), r0
+
+
+@pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("group", [32, 64, 256])
 @pytest.mark.parametrize("m,k,n", [(130, 1024, 200), (33, 2048, 72)])
 def test_w4a16_gemm_other_group_sizes(m, k, n, group, asym):

@@ -47,6 +47,30 @@ def test_swiglu_small(m, k, i, asym):
     check(h, og.swiglu_reference(bf16_as_f32(c["x"]), packed, s, z, 128), f"swiglu {fmt}")
 
 
+@pytest.mark.parametrize("asym", [False, True])
+def test_swiglu_last_wave_quarters(asym):
+    # 3 x 90 = 270 tiles of 128 tokens x 128 channels of h: the last 14 run as
+    # 32-token quarters on a 256-CU GPU; against the oracle, and bit for bit
+    # against each 128-row slice computed alone
+    dev = device()
+    m, k, i = 300, 512, 11520
+    fmt = "int4_asym" if asym else "int4_sym"
+    print(f"swiglu last-wave quarters m={m} k={k} I={i} {fmt}", flush=True)
+    c = small_case(m, k, 2 * i, seed=17 + asym, w_outlier=(0.01, 20.0))
+    codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
+    if asym:
+        q, s, z = oi.quantize_asym(c["w"], 128)
+    else:
+        (q, s), z = oi.quantize_sym(c["w"], 128), None
+    x = to_dev(c["x"], dev)
+    h = qg.qgemm_swiglu(x, codes, scales, zeros, fmt)
+    check(host(h), og.swiglu_reference(bf16_as_f32(c["x"]), oi.pack_int4(q), s, z, 128),
+          f"swiglu {fmt}")
+    for r0 in (0, 128, 256):
+        part = qg.qgemm_swiglu(x[r0:r0 + 128].contiguous(), codes, scales, zeros, fmt)
+        assert torch.equal(part.view(torch.int16), h[r0:r0 + 128].view(torch.int16)), r0
+
+
 def test_swiglu_qwen72b_gate_up_sampled():
     dev = device()
     c = workload_case("qwen72b_prefill", 0)          # K = 8192, 29568 rows = 2 x 14784
