@@ -1,9 +1,10 @@
 """HIP-graph capture of the library's launches (the benchmark times graph
 replays): every output of a captured sequence -- the decode GEMV at 1, 4 and
 16 rows on tiled and canonical codes (per-wave, x-shared and 16-row
-kernels), the SwiGLU GEMV, the W4A16 / SwiGLU / FP8 / FP8-SwiGLU / INT8 /
-MXFP4 GEMMs, the per-token quantizers, the fused norm + quantization and the
-FP8 KV-cache store -- is bit-identical to the eager launch's on every one of
+kernels), the SwiGLU GEMV, the W4A16 (also with its last wave of tiles in
+quarters) / SwiGLU / FP8 / FP8-SwiGLU / INT8 / MXFP4 GEMMs, the per-token
+quantizers, the fused norm + quantization and the FP8 KV-cache store -- is
+bit-identical to the eager launch's on every one of
 several replays.  Between replays the outputs are overwritten eagerly and
 other eager library work runs, with synchronizations in between."""
 
@@ -34,6 +35,7 @@ def _inputs(dev):
     p = small_case(300, 1024, 1000, seed=73)
     f = small_case(300, 512, 520, seed=74)
     m = small_case(256, 512, 384, seed=75)
+    t = small_case(300, 512, 23040, seed=77)
     inp = {}
     inp["x"] = to_dev(c["x"], dev)
     inp["w"] = qg.quantize_pack(to_dev(c["w"], dev), "int4_asym", 128)
@@ -46,6 +48,8 @@ def _inputs(dev):
     inp["xf"] = to_dev(f["x"], dev)
     inp["wf"] = qg.quantize_pack(to_dev(f["w"], dev), "fp8_e4m3")
     inp["wi"] = qg.quantize_pack(to_dev(f["w"], dev), "int8_sym")
+    inp["xt"] = to_dev(t["x"], dev)
+    inp["wt4"] = qg.quantize_pack(to_dev(t["w"], dev), "int4_sym", 128)
     inp["xm"] = to_dev(m["x"], dev)
     inp["wm"] = qg.mx_quant(to_dev(m["w"], dev))
     k = inp["xp"].shape[1]
@@ -74,6 +78,8 @@ def _launches(inp):
     pc, ps, _ = inp["wp"]
     out["w4a16"] = qg.qgemm(inp["xp"], pc, ps, None, "int4_sym", "bf16")
     out["w4a16_swiglu"] = qg.qgemm_swiglu(inp["xp"], pc, ps, None, "int4_sym")
+    tc, ts, _ = inp["wt4"]     # 270 tiles: whole tiles, then a launch of quarter tiles
+    out["w4a16_last_wave"] = qg.qgemm(inp["xt"], tc, ts, None, "int4_sym", "bf16")
     xq, sx, _ = qg.quantize_pack(inp["xf"], "fp8_e4m3")
     out["fp8_codes"], out["fp8_scales"] = xq, sx
     wq, sw, _ = inp["wf"]
