@@ -45,6 +45,8 @@
 // l32 + 16 hold gate[n] and up[n] of the same channel and token rows, and one
 // lane exchange per value pairs them in the epilogue.
 
+#include <atomic>
+
 #include "qg_gemm_common.hpp"
 #include "qg_internal.hpp"
 
@@ -419,15 +421,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
   }
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; host threads
+// may race to fill an entry, all with the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
