@@ -112,7 +112,11 @@ struct Parity {
 // (the tiles of a last, partly filled wave of workgroups, spread over every
 // CU); the four quarters of a tile run on one XCD so its codes come from
 // that XCD's L2.  lin0: linear index of the launch's first tile.
-template <bool ASYM, bool SWIGLU, int SUB = 1>
+// PAIRS (an even number of groups G): the scales (and zero points) of two
+// groups, one dword per row, come in one load at every even k-step, into
+// slot (g / 2) % 3 of the three stages' scale areas, instead of one 2-byte
+// load per group: half the scale loads and half their cache-line requests.
+template <bool ASYM, bool SWIGLU, int SUB = 1, bool PAIRS = false>
 __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     const uint16_t* __restrict__ X, int M, const uint32_t* __restrict__ Wc,
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ Z, int N, int K,
@@ -202,11 +206,25 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     for (int q = 0; q < 2; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rwc, (lds_void*)(st + kXBytes + (32 * wave + 16 * q) * WROW), 16, vw[q], gl * WROW, 0, 0);
-    lds_void* sd = (lds_void*)(st + kXBytes + kWBytes + (zwave ? kSBytes : 0) + 256 * (wave & 3));
-    if (zwave)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, sd, 2, vs, gl * 2, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, sd, 2, vs, gl * 2, 0, 0);
+    if constexpr (PAIRS) {
+      // groups g, g + 1 (g even; past the end the last pair again, into a
+      // slot nobody reads) into slot (g / 2) % 3; odd g: no scale load
+      if ((g & 1) == 0) {
+        const int gp = g < G ? g : G - 2;
+        uint8_t* slot = smem + ((g >> 1) % 3) * kStageBytes + kXBytes + kWBytes;
+        lds_void* sd = (lds_void*)(slot + (zwave ? kSBytes : 0) + 256 * (wave & 3));
+        if (zwave)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, sd, 4, vs, gp * 2, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, sd, 4, vs, gp * 2, 0, 0);
+      }
+    } else {
+      lds_void* sd = (lds_void*)(st + kXBytes + kWBytes + (zwave ? kSBytes : 0) + 256 * (wave & 3));
+      if (zwave)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, sd, 2, vs, gl * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, sd, 2, vs, gl * 2, 0, 0);
+    }
   };
 
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
@@ -258,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
     const int sg = SC >= 0 ? SC : g % kStages;        // stage of g (also its row-sum buffer)
     // group g has landed for every wave; stage (g - 1) % 3 is free and the
     // row sums of the groups before g are in LDS
-    wait_vm_barrier<kGroupLoads>();
+    // PAIRS: step g - 1 issued its scale load iff it was even, i.e. iff P = 1
+    wait_vm_barrier<PAIRS ? kXL + 2 + P : kGroupLoads>();
     issue(g + 2, SC >= 0 ? (SC + 2) % kStages : (g + 2) % kStages);
     const uint8_t* st = smem + sg * kStageBytes;
     if (P == 0 && g >= 2) cross(g - 2, true);
@@ -293,12 +312,19 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(
       cw[nt][1] = *reinterpret_cast<const u32x4*>(st + w_off(r, 2 * lh + 1));
     }
     float sv[NT];
-    const uint32_t* sl = reinterpret_cast<const uint32_t*>(st + kXBytes + kWBytes);
+    // PAIRS: slot (g / 2) % 3, known at compile time inside the unrolled
+    // loop (position i of the six steps: i % 2 = P, i % 3 = SC); the dword
+    // holds group g - P in its low half and group g - P + 1 in its high half
+    constexpr int kSlot = SC >= 0 ? ((3 * P + 4 * SC) % 6) / 2 : -1;
+    const int slot = kSlot >= 0 ? kSlot : (g >> 1) % 3;
+    const uint32_t* sl = reinterpret_cast<const uint32_t*>(
+        (PAIRS ? smem + slot * kStageBytes : st) + kXBytes + kWBytes);
+    constexpr int kHalf = PAIRS ? 16 * P : 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int r = nrow0 + nt * 32 + l32;
-      sv[nt] = f16_bits_to_f32((uint16_t)sl[r]);
-      const float c = ASYM ? 128.f + f16_bits_to_f32((uint16_t)sl[BN + r]) : 136.f;
+      sv[nt] = f16_bits_to_f32((uint16_t)(sl[r] >> kHalf));
+      const float c = ASYM ? 128.f + f16_bits_to_f32((uint16_t)(sl[BN + r] >> kHalf)) : 136.f;
       scp[P][nt] = sv[nt] * c;
     }
 
@@ -437,6 +463,23 @@ int device_cus() {
   return n;
 }
 
+// Whole tiles [0, full), then tiles [full, tiles) as quarters.
+template <bool ASYM, bool SWIGLU, bool PAIRS>
+void launch_tiles(const void* x, int64_t M, const void* wcodes, const void* wscales,
+                  const void* wzeros, int64_t N, int64_t K, void* y, int full, int tiles,
+                  uint32_t cmag, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU, 1, PAIRS>), dim3(full), dim3(kThreads), 0,
+                     stream, (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
+                     (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
+                     (uint16_t*)y, 0x000F000Fu, cmag, 0);
+  if (full < tiles)
+    hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU, 4, PAIRS>), dim3(4 * (tiles - full)),
+                       dim3(kThreads), 0, stream, (const uint16_t*)x, (int)M,
+                       (const uint32_t*)wcodes, (const uint16_t*)wscales,
+                       (const uint16_t*)wzeros, (int)N, (int)K, (uint16_t*)y, 0x000F000Fu, cmag,
+                       full);
+}
+
 // One workgroup per CU at a time (the LDS holds one), so the tiles run in
 // waves of `cus`.  When the last wave would fill at most a quarter of the
 // CUs, its tiles go to a second launch in 32-token quarters, four per tile
@@ -453,16 +496,12 @@ void launch_t(const void* x, int64_t M, const void* wcodes, const void* wscales,
   const int rest = cus > 0 ? tiles % cus : 0;
   const int full = (rest > 0 && tiles > cus && 4 * rest <= cus) ? tiles - rest : tiles;
   const uint32_t cmag = ASYM ? 0x43004300u : 0x43084308u;
-  hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU>), dim3(full), dim3(kThreads), 0, stream,
-                     (const uint16_t*)x, (int)M, (const uint32_t*)wcodes,
-                     (const uint16_t*)wscales, (const uint16_t*)wzeros, (int)N, (int)K,
-                     (uint16_t*)y, 0x000F000Fu, cmag, 0);
-  if (full < tiles)
-    hipLaunchKernelGGL((gemm_w4a16_kernel<ASYM, SWIGLU, 4>), dim3(4 * (tiles - full)),
-                       dim3(kThreads), 0, stream, (const uint16_t*)x, (int)M,
-                       (const uint32_t*)wcodes, (const uint16_t*)wscales,
-                       (const uint16_t*)wzeros, (int)N, (int)K, (uint16_t*)y, 0x000F000Fu, cmag,
-                       full);
+  if ((K / BK) % 2 == 0)
+    launch_tiles<ASYM, SWIGLU, true>(x, M, wcodes, wscales, wzeros, N, K, y, full, tiles, cmag,
+                                     stream);
+  else
+    launch_tiles<ASYM, SWIGLU, false>(x, M, wcodes, wscales, wzeros, N, K, y, full, tiles, cmag,
+                                      stream);
 }
 
 }  // namespace
