@@ -1056,8 +1056,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "qgemv_wave_kernel<asym, 8 groups/wave, M<=1, tiled codes> (gate+up "
-                          "4096->28672, M=1; grid 1792 x 256)",
+                "kernel": "qgemv_wave_kernel<asym, 4 groups/wave, M<=1, tiled codes> (gate+up "
+                          "4096->28672, M=1; grid 1792 x 512)",
                 "us_per_launch": round(dom_t * 1e6, 3),
                 "us_per_launch_min_max": [round(dom_min * 1e6, 3), round(dom_max * 1e6, 3)],
                 "timing": f"median of {ROOFLINE_TRIALS} graph replays of {ROOFLINE_REPS} launches",

@@ -1469,11 +1469,11 @@ hipError_t launch_wave(bool asym, int ng, const void* x, int M, const void* w, c
 
 // Groups per wave for the per-wave kernel (0: not applicable).  Measured on
 // MI355X for the Llama-3-8B decode layer (four projections back to back in
-// a graph): 4 groups per wave for projections of at most 8192 channels (more
-// waves in flight when there are few 16-channel tiles: at M = 4 the layer
-// 2.81 -> 2.90 TB/s; at M = 1 the 4096 x 4096 GEMV 4.12 -> 3.91 us and QKV
-// 0.1 - 0.2 us faster, the layer unchanged or 0.1 us faster), else 8; 16
-// (M = 1 only: 128 VGPRs) when K is too long for 16 slices of 8.
+// a graph): 4 groups per wave wherever K fits 16 slices of 4 (more waves in
+// flight: at M = 4 the layer 2.81 -> 2.90 TB/s; at M = 1 the 4096 x 4096
+// GEMV 4.12 -> 3.91 us, QKV 0.1 - 0.2 us faster, and with the gate+up
+// projection on it too the layer 0.2 - 0.3 us faster in six A/B pairs), else
+// 8; 16 (M = 1 only: 128 VGPRs) when K is too long for 16 slices of 8.
 int pick_wave_ng(int M, int N, int K) {
   const int G = K / kGroup;
   if (M > 4 || G % 4 != 0) return 0;
@@ -1482,7 +1482,7 @@ int pick_wave_ng(int M, int N, int K) {
     const int ks = G / ng;
     return G % ng == 0 && ks <= 16 && (size_t)ks * (mm * ng * 256 + 1024) <= 160 * 1024;
   };
-  if (N <= 8192 && fits(4)) return 4;
+  if (fits(4)) return 4;
   if (fits(8)) return 8;
   if (fits(4)) return 4;
   if (M == 1 && fits(16)) return 16;
