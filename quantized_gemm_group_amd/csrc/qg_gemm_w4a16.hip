@@ -26,15 +26,18 @@
 // and scaling overlaps the other's matrix instructions), 128 (tokens) x 256
 // (channels) output tile; one k-step = one group.  Each of the 8 waves owns
 // 128 x 32 (4 x 1 tiles of 32x32): a wave unpacks only its own 32 weight
-// rows' codes and uses each unpacked code for four MFMAs.  The operands travel HBM -> LDS with buffer loads that
-// write LDS directly, into a ring of 3 stages: X (128 rows x 256 bytes,
-// 16-byte chunks XOR-swizzled by row bits 0..3), the codes (256 rows x 64
-// bytes, swizzled by row bits 2..3) and the group's fp16 scales and zero
-// points (one 2-byte load per row).  The loads of k-step k + 2 go out after
-// the barrier of k-step k; the compiler does not track loads that write LDS,
-// so the waits are explicit.  Within a group, lane half h and MFMA j cover
-// k = 64 h + 8 j .. + 7 in natural order, so a lane's codes of the group are
-// 32 contiguous bytes and its X pieces 128.
+// rows' codes and uses each unpacked code for four MFMAs.  The operands
+// travel HBM -> LDS with buffer loads that write LDS directly, into a ring of
+// 3 stages: X (128 rows x 256 bytes, 16-byte chunks XOR-swizzled by row bits
+// 0..3), the codes (256 rows x 64 bytes, swizzled by row bits 2..3) and the
+// fp16 scales and zero points (one 2-byte load per row and group, or, for an
+// even group count, one dword load per row for two groups).  The loads of
+// k-step k + 2 go out after the barrier of k-step k; the compiler does not
+// track loads that write LDS, so the waits are explicit.  Within a group,
+// lane half h and MFMA j cover k = 64 h + 8 j .. + 7 in natural order, so a
+// lane's codes of the group are 32 contiguous bytes and its X pieces 128.
+// Tiles are ordered XCD by XCD (contiguous ranges in column groups of 4 tile
+// rows), and a last, mostly empty wave of tiles runs in 32-token quarters.
 //
 // SwiGLU variant (《推理优化与量化算子深度技术调研》 section 4.6: the gate and
 // up projections as one GEMM over [W_gate; W_up], SiLU(gate) * up formed in
