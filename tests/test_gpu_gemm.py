@@ -237,17 +237,18 @@ def test_w4a16_gemm_small(m, k, n, asym):
 
 
 @pytest.mark.parametrize("asym", [False, True])
-def test_w4a16_gemm_last_wave_quarters(asym):
+@pytest.mark.parametrize("k", [512, 640])      # 4 groups (paired scale loads), 5 groups (single)
+def test_w4a16_gemm_last_wave_quarters(asym, k):
     # 3 x 90 = 270 tiles of 128 x 256: on a 256-CU GPU 256 whole tiles run
     # first and the last 14 as 32-token quarters (the last row tile is ragged,
     # 44 rows: one full and one partial quarter, two empty).  Against the
     # oracle, and bit for bit against each 128-row slice computed alone (one
     # partly filled wave, whole tiles): every output is the same arithmetic.
     dev = device()
-    m, k, n = 300, 512, 23040
+    m, n = 300, 23040
     fmt = "int4_asym" if asym else "int4_sym"
     print(f"w4a16 gemm last-wave quarters m={m} k={k} n={n} {fmt}", flush=True)
-    c = small_case(m, k, n, seed=5 + asym, w_outlier=(0.01, 20.0))
+    c = small_case(m, k, n, seed=5 + asym + k, w_outlier=(0.01, 20.0))
     codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
     if asym:
         q, s, z = oi.quantize_asym(c["w"], 128)

@@ -48,15 +48,16 @@ def test_swiglu_small(m, k, i, asym):
 
 
 @pytest.mark.parametrize("asym", [False, True])
-def test_swiglu_last_wave_quarters(asym):
+@pytest.mark.parametrize("k", [512, 640])      # paired / single scale loads
+def test_swiglu_last_wave_quarters(asym, k):
     # 3 x 90 = 270 tiles of 128 tokens x 128 channels of h: the last 14 run as
     # 32-token quarters on a 256-CU GPU; against the oracle, and bit for bit
     # against each 128-row slice computed alone
     dev = device()
-    m, k, i = 300, 512, 11520
+    m, i = 300, 11520
     fmt = "int4_asym" if asym else "int4_sym"
     print(f"swiglu last-wave quarters m={m} k={k} I={i} {fmt}", flush=True)
-    c = small_case(m, k, 2 * i, seed=17 + asym, w_outlier=(0.01, 20.0))
+    c = small_case(m, k, 2 * i, seed=17 + asym + k, w_outlier=(0.01, 20.0))
     codes, scales, zeros = qg.quantize_pack(to_dev(c["w"], dev), fmt, 128)
     if asym:
         q, s, z = oi.quantize_asym(c["w"], 128)
