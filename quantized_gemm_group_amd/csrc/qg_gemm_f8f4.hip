@@ -4,8 +4,9 @@
 // FP8 (《第 6 课：量化源码走读》 section 2 and figure 6-2): the matrix cores
 // multiply the E4M3 codes exactly and accumulate in fp32; the epilogue
 // rescales by s_x[m] * s_w[n] (per-token activation scale, per-channel weight
-// scale) and rounds once to bf16.  The MFMA's own block scales are set to
-// 2^0 (E8M0 byte 127).
+// scale) and rounds once to bf16.  The MFMA's own block scales are off: the
+// unscaled form of the instruction, which multiplies as block scales of 2^0
+// would.
 //
 // MXFP4 (《大模型量化推理引擎全景大复盘》 section 2 eq. 3; 《第 6 课：量化源码走读》
 // section 2): each lane of the MFMA holds 32 E2M1 codes of one row that form
@@ -366,8 +367,11 @@ __global__ __launch_bounds__(W4 ? 256 : 512) void gemm_f8f4_kernel(const uint8_t
   auto mma_piece = [&](const frags_t& f, int k, int i) {
     const int u = (i >> 2) % NT, t = i & 3;
     if constexpr (!MX) {
+      // constant zero scale operands: the compiler selects the unscaled
+      // v_mfma_f32_32x32x64_f8f6f4 (8-byte encoding, no scale prefix), whose
+      // products equal those of scale bytes 127 (2^0) bit for bit
       acc[u][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[u], f.a[t], acc[u][t], 0, 0,
-                                                                  0, 127, 0, 127);
+                                                                  0, 0, 0, 0);
     } else {
       // the scale operands are the exponent dwords with byte 2 s selected;
       // blocks past K (last k-step, K not a multiple of 128) have zero codes
