@@ -47,10 +47,12 @@ def fp8_case(m, k, n, seed):
     return c["w"], c["x"]
 
 
-# K a multiple of 64 (whole k-steps) and K = 48, 176, 1040 (a last k-step of
-# 3, 3 and 1 of its four 16-byte chunks)
+# K a multiple of 64 (whole k-steps; 1, 3 and 5 of them leave the last pair
+# of k-steps half empty) and K = 48, 176, 1040 (a last k-step of 3, 3 and 1
+# of its four 16-byte chunks)
 @pytest.mark.parametrize("m,k,n", [(64, 256, 80), (130, 512, 200), (257, 1040, 129), (1, 128, 16),
-                                   (300, 2048, 384), (40, 48, 72), (100, 176, 96)])
+                                   (300, 2048, 384), (40, 48, 72), (100, 176, 96), (5, 64, 24),
+                                   (70, 192, 136), (300, 320, 264)])
 def test_fp8_gemm_small(m, k, n):
     dev = device()
     w, x = fp8_case(m, k, n, seed=m + n + k)

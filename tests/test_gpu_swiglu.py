@@ -192,9 +192,11 @@ from oracle import fp8 as of8  # noqa: E402
 
 
 # ragged M, I (not a multiple of 4 or 8, a partial last 128-channel tile),
-# K with a partial last k-step (48, 176, 1040)
+# K with a partial last k-step (48, 176, 1040) or an odd number of whole
+# k-steps (64, 192)
 @pytest.mark.parametrize("m,k,i", [(64, 256, 40), (130, 512, 200), (257, 1040, 129), (1, 128, 16),
-                                   (300, 2048, 384), (40, 48, 72), (100, 176, 97), (8, 64, 2)])
+                                   (300, 2048, 384), (40, 48, 72), (100, 176, 97), (8, 64, 2),
+                                   (70, 192, 136)])
 def test_fp8_swiglu_small(m, k, i):
     dev = device()
     print(f"fp8 swiglu m={m} k={k} I={i}", flush=True)
